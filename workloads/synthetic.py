@@ -1,0 +1,183 @@
+"""Seeded synthetic workloads for the static per-tensor FP8 linear layer.
+
+The pages measure on Cosmos3 checkpoints and prompts that are not available
+here; these generators stand in for them with the shapes, scales and value
+distributions of the layer ([DF-15170] "Logs": a 4096 -> 4096 projection,
+bias=False, input amax 0.5430 and weight amax 0.5039 under a max calibrator).
+
+Recipe: every tensor is drawn on the CPU with torch.Generator().manual_seed
+(seed) as float32 N(0, 1) times its standard deviation, then cast to bf16
+with torch's round-to-nearest-even cast. Static scales are "calibrated" the
+way a max calibrator does it: amax / 448 in float32 over a separately seeded
+calibration batch (activations) or over the tensor itself (weights).
+
+Nothing here performs the layer's own arithmetic (no quantization, no FP8
+GEMM); that is done separately by the HIP library and by the oracle.
+"""
+
+from dataclasses import dataclass, field
+from typing import List
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0  # largest finite E4M3 magnitude: the calibrator's target
+
+__all__ = [
+    "E4M3_MAX",
+    "normal_bf16",
+    "max_calibrated_scale",
+    "random_e4m3_codes",
+    "all_bf16_patterns",
+    "LinearCase",
+    "GroupCase",
+    "MlpCase",
+    "linear_case",
+    "config1",
+    "config2",
+    "config3",
+    "config4",
+    "QKV_RATIOS",
+]
+
+QKV_RATIOS = (1.0, 0.7, 0.45)
+
+
+def normal_bf16(shape, std, seed, device="cpu"):
+    """bf16 tensor of N(0, std^2) draws, reproducible from `seed`."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=gen, dtype=torch.float32) * float(std)
+    return t.to(torch.bfloat16).to(device)
+
+
+def max_calibrated_scale(t):
+    """float32(amax(|t|)) / float32(448): the max-calibrator scale of `t`."""
+    amax = np.float32(t.detach().abs().max().float().cpu().item())
+    return float(amax / np.float32(E4M3_MAX))
+
+
+def random_e4m3_codes(shape, seed):
+    """uint8 tensor of uniformly drawn finite E4M3 codes (NaN codes excluded)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    r = torch.randint(0, 254, tuple(shape), generator=gen, dtype=torch.int32)
+    r = torch.where(r >= 0x7F, r + 1, r)  # skip 0x7F; 253 -> 0xFE
+    return r.to(torch.uint8)
+
+
+def all_bf16_patterns():
+    """All 65,536 bf16 bit patterns in order, as a bf16 tensor [65536]."""
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    return bits.view(torch.bfloat16)
+
+
+@dataclass
+class LinearCase:
+    """One projection: activation x [M, K], unquantized weight w [N, K]."""
+
+    x: torch.Tensor
+    w: torch.Tensor
+    input_scale: float
+    weight_scale: float
+
+
+@dataclass
+class GroupCase:
+    """Projections sharing one activation and one input scale (Q/K/V)."""
+
+    x: torch.Tensor
+    ws: List[torch.Tensor]
+    input_scale: float
+    weight_scales: List[float]
+    ratios: tuple = field(default=())
+
+
+@dataclass
+class MlpCase:
+    """Split gated MLP: gate/up on a shared input, SwiGLU, then down."""
+
+    x: torch.Tensor
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    input_scale: float
+    s_gate: float
+    s_up: float
+    s_down: float
+    s_h: float
+
+
+def linear_case(m, n, k, x_std, w_std, seed_x, seed_w, seed_cal, cal_rows):
+    x = normal_bf16((m, k), x_std, seed_x)
+    w = normal_bf16((n, k), w_std, seed_w)
+    cal = normal_bf16((cal_rows, k), x_std, seed_cal)
+    return LinearCase(x, w, max_calibrated_scale(cal), max_calibrated_scale(w))
+
+
+def config1():
+    """x [128, 512] ~ N(0, 0.5), W [512, 512] ~ N(0, 0.02).
+
+    The input scale comes from a 64-element calibration draw, so about 1% of
+    x exceeds 448 * s_in and saturates.
+    """
+    x = normal_bf16((128, 512), 0.5, 123)
+    w = normal_bf16((512, 512), 0.02, 124)
+    cal = normal_bf16((64,), 0.5, 125)
+    return LinearCase(x, w, max_calibrated_scale(cal), max_calibrated_scale(w))
+
+
+def config2(m=8192):
+    """4096 -> 4096 projection, x [m, 4096] ~ N(0, 0.35) (m in {1024, 8192})."""
+    x = normal_bf16((8192, 4096), 0.35, 223)[:m].contiguous()
+    w = normal_bf16((4096, 4096), 0.02, 224)
+    cal = normal_bf16((1024, 4096), 0.35, 225)
+    return LinearCase(x, w, max_calibrated_scale(cal), max_calibrated_scale(w))
+
+
+def config3(m=16384, k=4096, n=4096):
+    """Shared QKV: x [m, k] ~ N(0, 0.35); W_q, W_k, W_v ~ N(0, (0.02 r_i)^2).
+
+    Weight scales keep the exact ratios r = (1, 0.7, 0.45):
+    s_i = float32(r_i * s0) with s0 = max_i(amax(W_i) / r_i) / 448, so the
+    three scales genuinely differ and no weight saturates.
+    """
+    x = normal_bf16((m, k), 0.35, 323)
+    ws = [normal_bf16((n, k), 0.02 * r, 324 + i) for i, r in enumerate(QKV_RATIOS)]
+    amax = [float(w.abs().max().float()) for w in ws]
+    s0 = np.float32(max(a / r for a, r in zip(amax, QKV_RATIOS))) / np.float32(E4M3_MAX)
+    scales = [float(np.float32(r) * s0) for r in QKV_RATIOS]
+    cal = normal_bf16((1024, k), 0.35, 327)
+    return GroupCase(x, ws, max_calibrated_scale(cal), scales, QKV_RATIOS)
+
+
+def config4(m=8192, hidden=4096, inter=16384, cal_rows=1024, device="cpu"):
+    """Split gated MLP on x [m, hidden] ~ N(0, 0.35).
+
+    W_gate, W_up [inter, hidden] and W_down [hidden, inter] ~ N(0, 0.02).
+    s_h, the down projection's input scale, is calibrated on an unquantized
+    float32 forward of `cal_rows` calibration rows (what an offline max
+    calibrator observes at the SwiGLU output); `device` only selects where
+    that float32 calibration forward runs.
+    """
+    x = normal_bf16((m, hidden), 0.35, 423)
+    w_gate = normal_bf16((inter, hidden), 0.02, 424)
+    w_up = normal_bf16((inter, hidden), 0.02, 425)
+    w_down = normal_bf16((hidden, inter), 0.02, 426)
+    cal = normal_bf16((cal_rows, hidden), 0.35, 427)
+    with torch.no_grad():
+        c = cal.to(device).float()
+        g = c @ w_gate.to(device).float().t()
+        u = c @ w_up.to(device).float().t()
+        h = torch.nn.functional.silu(g) * u
+        s_h = max_calibrated_scale(h)
+        del c, g, u, h
+    return MlpCase(
+        x,
+        w_gate,
+        w_up,
+        w_down,
+        max_calibrated_scale(cal),
+        max_calibrated_scale(w_gate),
+        max_calibrated_scale(w_up),
+        max_calibrated_scale(w_down),
+        s_h,
+    )
