@@ -1,0 +1,241 @@
+/*
+ * fp8lin -- static per-tensor FP8 linear layers for AMD MI355X (gfx950).
+ *
+ * C ABI of the library libfp8lin.so. Every entry point is extern "C", takes
+ * plain pointers and sizes, and returns an int32_t status (FP8LIN_OK = 0,
+ * negative on error). No C++ exception crosses the ABI.
+ *
+ * The method (web pages, cited by title and section):
+ *   [CF-157]    NVIDIA/cosmos-framework PR #157, "feat: load ModelOpt
+ *               static-FP8 checkpoints via TorchAO".
+ *   [DF-14664]  huggingface/diffusers PR #14664, "[Cosmos3] Mixed W8A8/W8A16
+ *               denoising for ModelOpt FP8 checkpoints".
+ *   [TRT-17476] NVIDIA/TensorRT-LLM PR #17476, "Load static FP8 Cosmos3
+ *               Nano/Super checkpoints without re-quantizing them".
+ *   [DF-15170]  huggingface/diffusers issue #15170, "Cosmos 3 docs: FP8
+ *               snippet fails at the first W8A8 step without importing
+ *               ModelOpt's FP8 GEMM backend".
+ *
+ * Conventions shared by all GPU entry points:
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *     The library allocates no device memory and keeps no state between
+ *     calls apart from the launch counters of fp8lin_launch_count().
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default
+ *     stream); no call synchronizes the host with the device, and no call
+ *     reads device memory from the host, so calls are safe to capture into a
+ *     HIP graph.
+ *   - Scales are HOST floats: static, load-time constants of the checkpoint.
+ *     A scale must be finite and lie in [2^-126, 2^126] (so that its
+ *     reciprocal is a normal float) -> otherwise FP8LIN_ESCALE.
+ *   - All arguments are validated before anything is enqueued; a failing
+ *     call enqueues nothing. rows/M == 0 is a valid no-op (FP8LIN_OK); the
+ *     activation and output pointers may then be NULL (sizes, scales and
+ *     the weight pointer are still checked).
+ *   - Matrices are row-major. Activations x are [M, K], weights are
+ *     [N, K] (out_features x in_features, the nn.Linear layout, bias=False
+ *     as in [DF-15170] "Logs"), outputs y are [M, N] with row stride ldy
+ *     elements.
+ *   - E4M3 is the OCP FP8 "FN" format (bias 7, max 448, no infinities,
+ *     NaN = S.1111.111), one byte per element.
+ *   - Layout requirements (else FP8LIN_ELAYOUT): K and cols multiples of 16;
+ *     N and ldy multiples of 8 with ldy >= N; every pointer 16-byte aligned.
+ *   - Size limits (else FP8LIN_EUNSUPPORTED): M, N, rows < 2^31, K and cols
+ *     < 2^24, M*K and rows*cols < 2^40.
+ *   - A HIP launch error is reported as FP8LIN_EHIP.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8LIN_OK = 0,
+  FP8LIN_EINVAL = -1,       /* null pointer, negative size, unknown enum value */
+  FP8LIN_ELAYOUT = -2,      /* alignment, divisibility or leading dimension */
+  FP8LIN_EDTYPE = -3,       /* activation dtype this call does not accept */
+  FP8LIN_ESCALE = -4,       /* bad scale, or unequal input scales in a group */
+  FP8LIN_EPOLICY = -5,      /* step policy missing a field or holding a bad value */
+  FP8LIN_EUNSUPPORTED = -6, /* size beyond the stated limits */
+  FP8LIN_EHIP = -7          /* the HIP runtime rejected a launch */
+} fp8lin_status;
+
+typedef enum { FP8LIN_MODE_W8A8 = 0, FP8LIN_MODE_W8A16 = 1 } fp8lin_mode;
+
+typedef enum { FP8LIN_DT_BF16 = 0, FP8LIN_DT_E4M3 = 1 } fp8lin_dtype;
+
+typedef enum { FP8LIN_TOWER_GENERATION = 0, FP8LIN_TOWER_REASONER = 1 } fp8lin_tower;
+
+/* Values of the enumerated policy fields. A parser maps each JSON string it
+ * recognises to its value and anything else to FP8LIN_POLICY_UNKNOWN. */
+enum {
+  FP8LIN_POLICY_UNKNOWN = -1,
+  FP8LIN_POLICY_TYPE_FIRST_LAST_STEPS = 1, /* "type": "first_last_steps" */
+  FP8LIN_POLICY_INDEX_SCHEDULER_STEP = 1,  /* "index_space": "scheduler_step" (0-based) */
+  FP8LIN_POLICY_OVERLAP_A16 = 1            /* "overlap": "a16" */
+};
+
+/* present_mask bits: one per field of the policy document. */
+enum {
+  FP8LIN_PF_SCHEMA_VERSION = 1u << 0,
+  FP8LIN_PF_TYPE = 1u << 1,
+  FP8LIN_PF_INDEX_SPACE = 1u << 2,
+  FP8LIN_PF_DEFAULT_MODE = 1u << 3,
+  FP8LIN_PF_OVERLAP = 1u << 4,
+  FP8LIN_PF_FIRST_STEPS = 1u << 5,
+  FP8LIN_PF_LAST_STEPS = 1u << 6,
+  FP8LIN_PF_REASONER = 1u << 7,
+  FP8LIN_PF_ALL = 0xFFu,
+  FP8LIN_PF_UNKNOWN_FIELD = 1u << 31 /* the document held a field not listed above */
+};
+
+/* quantization_config.runtime.diffusion_step_policy, as parsed from the
+ * checkpoint ([DF-14664] "Behavior"; [TRT-17476] "Denoising-step activation
+ * precision"). default_mode and reasoner_mode hold fp8lin_mode values
+ * (default_mode must be FP8LIN_MODE_W8A8). */
+typedef struct {
+  int32_t schema_version; /* must be 1 */
+  int32_t type;           /* FP8LIN_POLICY_TYPE_FIRST_LAST_STEPS */
+  int32_t index_space;    /* FP8LIN_POLICY_INDEX_SCHEDULER_STEP */
+  int32_t default_mode;   /* FP8LIN_MODE_W8A8 */
+  int32_t overlap;        /* FP8LIN_POLICY_OVERLAP_A16 */
+  int32_t first_steps;    /* >= 0: steps [0, first_steps) run W8A16 */
+  int32_t last_steps;     /* >= 0: steps [num_steps - last_steps, num_steps) run W8A16 */
+  int32_t reasoner_mode;  /* mode of the understanding tower, not step-gated */
+  uint32_t present_mask;  /* FP8LIN_PF_* bits of the fields the document held */
+} fp8lin_policy;
+
+/*
+ * Static per-tensor activation quantization ([CF-157] "Verification": the
+ * quantizer divides by the exported input_scale, clamps, then rounds to FP8).
+ *   q[i] = E4M3_RNE( clamp( fl32(x[i]) / input_scale, -448, 448 ) )
+ * with the quotient the correctly rounded float32 division; ties go to the
+ * even code, -0 and a negative value that rounds to zero give 0x80, a NaN
+ * input gives 0x7F or 0xFF (its sign kept).
+ *   x_bf16  device, bf16 [rows, cols], contiguous, read only
+ *   q_e4m3  device, uint8 [rows, cols], contiguous, written
+ *   cols    multiple of 16
+ */
+int32_t fp8lin_quantize_static(const void* x_bf16, void* q_e4m3, int64_t rows, int64_t cols,
+                               float input_scale, hipStream_t stream);
+
+/*
+ * W8A8 GEMM ([CF-157] "Verification": a real FP8 x FP8 GEMM; [TRT-17476]
+ * "Description": one weight scale and one input scale per projection):
+ *   y[m, n] = bf16_RNE( (sum_k dec(qx[m, k]) * dec(qw[n, k])) * fl32(input_scale * weight_scale) )
+ * FP8 products accumulate in float32 on the FP8 matrix cores; the output is
+ * rounded to bf16 once.
+ *   qx  device, E4M3 [M, K], contiguous        (from fp8lin_quantize_static)
+ *   qw  device, E4M3 [N, K], contiguous        (the checkpoint weight)
+ *   y   device, bf16 [M, ldy], columns [0, N) written, the rest untouched
+ */
+int32_t fp8lin_gemm_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+                         int64_t ldy, float input_scale, float weight_scale, hipStream_t stream);
+
+/*
+ * W8A16 GEMM for the steps the policy sends to 16-bit activations
+ * ([TRT-17476] "Denoising-step activation precision": the resident FP8
+ * weight is dequantized with its own weight_scale, input_scale is unused, no
+ * dequantized weight copy is kept; [DF-14664] "Behavior"):
+ *   y[m, n] = bf16_RNE( weight_scale * sum_k x[m, k] * dec(qw[n, k]) )
+ * Weight tiles are staged in LDS as E4M3 and converted exactly to bf16 on
+ * the way to the bf16 matrix cores; no bf16 weight is written to memory.
+ *   x_dtype  must be FP8LIN_DT_BF16; an already-quantized activation
+ *            (FP8LIN_DT_E4M3) is refused with FP8LIN_EDTYPE, as the pages'
+ *            16-bit path refuses one.
+ *   x   device, bf16 [M, K], contiguous
+ *   qw  device, E4M3 [N, K], contiguous
+ *   y   device, bf16 [M, ldy]
+ */
+int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,
+                          int64_t K, int64_t ldy, float weight_scale, hipStream_t stream);
+
+/*
+ * Shared-input projections: Q/K/V (nproj = 3) or gate/up (nproj = 2)
+ * ([TRT-17476] "What changed": the group quantizes its shared activation once
+ * and hands the same FP8 tensor to every projection, each with its own
+ * weight_scale; the projections stay separate and write contiguous outputs,
+ * "It is also faster"). The group's input scales must be bitwise equal
+ * ("Description": the invariant the sharing rests on) -> else FP8LIN_ESCALE.
+ *   mode FP8LIN_MODE_W8A8:  one quantization of x into qx_workspace, then one
+ *                           grouped FP8 GEMM launch over all projections.
+ *   mode FP8LIN_MODE_W8A16: the sharing stands down ("Denoising-step
+ *                           activation precision"): no quantization, one
+ *                           grouped W8A16 launch; qx_workspace may be NULL.
+ *   x             device, bf16 [M, K]
+ *   nproj         1..4
+ *   qw[i]         device, E4M3 [n_out[i], K]
+ *   n_out[i]      host array: output width of projection i (multiple of 8)
+ *   weight_scale  host array [nproj]; input_scale host array [nproj]
+ *   y[i]          device, bf16 [M, n_out[i]], contiguous (ldy = n_out[i])
+ *   qx_workspace  device, M*K bytes; on return (W8A8) it holds the codes of x
+ *   The host arrays are read during the call only.
+ */
+int32_t fp8lin_qkv_shared(const void* x_bf16, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
+                          const int64_t n_out[], const float weight_scale[], const float input_scale[],
+                          void* const y_bf16[], void* qx_workspace, int32_t mode, hipStream_t stream);
+
+/*
+ * Two-input SwiGLU h = silu(gate) * up, silu(g) = g / (1 + exp(-g)), in
+ * float32, from two separate tensors ([TRT-17476] "What changed": the split
+ * MLP's SiLU(G) * U, quantized straight to FP8 for the down projection).
+ *   out_dtype FP8LIN_DT_E4M3: out[i] = E4M3_RNE(clamp(h / out_scale, +-448))
+ *                             (out_scale = the down projection's static
+ *                             input scale; h is not rounded to bf16 first)
+ *   out_dtype FP8LIN_DT_BF16: out[i] = bf16_RNE(h), for 16-bit steps;
+ *                             out_scale is ignored
+ *   gate, up  device, bf16 [rows, cols], contiguous (else the layout error)
+ *   out       device, [rows, cols] of E4M3 bytes or bf16
+ *   cols      multiple of 16
+ */
+int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void* out, int32_t out_dtype,
+                                int64_t rows, int64_t cols, float out_scale, hipStream_t stream);
+
+/*
+ * Fail-closed check of a parsed policy ([TRT-17476] "Denoising-step
+ * activation precision": unknown or missing fields, schema_version other than
+ * 1 and any other type / index_space / default_mode / overlap are refused).
+ * Returns FP8LIN_OK or FP8LIN_EPOLICY (FP8LIN_EINVAL for p == NULL). Host only.
+ */
+int32_t fp8lin_policy_validate(const fp8lin_policy* p);
+
+/*
+ * Mode of one transformer call ([DF-14664] "Behavior"; [TRT-17476]
+ * "Denoising-step activation precision"). A pure function of its arguments:
+ *   p == NULL (no policy, runtime: null)      -> W8A8 on every step
+ *   tower == FP8LIN_TOWER_REASONER            -> p->reasoner_mode
+ *   num_steps == 1 (one-step carve-out)       -> W8A8
+ *   step < first_steps or step >= num_steps - last_steps -> W8A16
+ *   otherwise                                 -> W8A8
+ * step is the 0-based scheduler step, 0 <= step < num_steps (else
+ * FP8LIN_EINVAL); an invalid policy gives FP8LIN_EPOLICY. Host only.
+ */
+int32_t fp8lin_step_policy(const fp8lin_policy* p, int32_t tower, int32_t step, int32_t num_steps,
+                           int32_t* mode_out);
+
+/* Static, NUL-terminated description of a status code. Host only. */
+const char* fp8lin_strerror(int32_t status);
+
+/* Kinds counted by fp8lin_launch_count(). */
+enum {
+  FP8LIN_KERNEL_QUANTIZE = 0,
+  FP8LIN_KERNEL_GEMM_W8A8 = 1,
+  FP8LIN_KERNEL_GEMM_W8A16 = 2,
+  FP8LIN_KERNEL_SWIGLU = 3,
+  FP8LIN_KERNEL_KINDS = 4
+};
+
+/* Number of kernels of `kind` this process has enqueued through the library
+ * (host-side atomic counter; -1 for an unknown kind). Lets a test check that a
+ * shared group quantizes exactly once per call. Host only, thread-safe. */
+int64_t fp8lin_launch_count(int32_t kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

@@ -1,0 +1,46 @@
+"""Small shared helpers for the GPU parity tests (conversion and reporting)."""
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import linear
+
+
+def announce(what):
+    """Print the case name before a GPU step (flushed, so a crash still names it)."""
+    print("\n[case] %s" % what, flush=True)
+    sys.stdout.flush()
+
+
+def f32(t):
+    """bf16 torch tensor (any device) -> float32 numpy array with the same values."""
+    return t.detach().float().cpu().numpy()
+
+
+def u8(t):
+    return t.detach().cpu().numpy().astype(np.uint8)
+
+
+def bf16_weight(w):
+    return f32(w)
+
+
+def assert_gemm_close(y_gpu, y_ref, what):
+    """GEMM acceptance rule: |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref), elementwise."""
+    y = f32(y_gpu).astype(np.float64) if isinstance(y_gpu, torch.Tensor) else np.asarray(y_gpu, np.float64)
+    ok = linear.within_gemm_tolerance(y, y_ref)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(
+            "%s: %d of %d outside tolerance; first at %s: gpu %r ref %r"
+            % (what, (~ok).sum(), ok.size, i, y[i], y_ref[i])
+        )
+
+
+def sample_rows(m, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(m, size=min(count, m), replace=False), [0, m - 1]]))
+    return rows

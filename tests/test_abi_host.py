@@ -1,0 +1,211 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every entry point include/fp8lin.h
+declares. The pure host calls (policy, strerror, counters) run for real; the
+GPU entry points are called only with arguments the validation refuses, or
+with zero rows (a no-op), so nothing touches a device.
+"""
+
+import copy
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import w8a16_linear_layers_amd as fp8lin
+from oracle import policy as opolicy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte aligned stand-in for a device pointer; never dereferenced
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "fp8lin.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^(?:int32_t|int64_t|const char\*)\s+(fp8lin_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_entry_point(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fp8lin.EXPORTS)
+
+
+def test_strerror_covers_every_status():
+    for st in range(0, -8, -1):
+        msg = fp8lin.fp8lin_strerror(st)
+        assert msg and msg != "unknown status"
+    assert fp8lin.fp8lin_strerror(-99) == "unknown status"
+
+
+def test_launch_count_rejects_unknown_kind():
+    assert fp8lin.fp8lin_launch_count(-1) == -1
+    assert fp8lin.fp8lin_launch_count(4) == -1
+    assert fp8lin.fp8lin_launch_count(0) >= 0
+
+
+# ---------------------------------------------------------------- policy
+
+
+@pytest.fixture(scope="module")
+def golden(golden_dir):
+    with open(os.path.join(golden_dir, "step_traces.json")) as f:
+        return json.load(f)
+
+
+def c_trace(pol, n, tower=fp8lin.TOWER_GENERATION):
+    names = {fp8lin.MODE_W8A8: "W8A8", fp8lin.MODE_W8A16: "W8A16"}
+    return [names[fp8lin.fp8lin_step_policy(pol, tower, i, n)] for i in range(n)]
+
+
+def test_c_policy_reproduces_printed_traces(golden):
+    pol = fp8lin.policy_from_json(golden["policy"])
+    assert fp8lin.fp8lin_policy_validate(pol) == 0
+    for case in golden["traces"]:
+        expected = []
+        for mode, n in case["runs"]:
+            expected += [mode] * n
+        assert c_trace(pol, case["num_steps"]) == expected, case["source"]
+
+
+def test_c_policy_matches_oracle_on_a_grid(golden):
+    for first in range(0, 5):
+        for last in range(0, 5):
+            for reasoner in ("a16", "a8"):
+                doc = dict(golden["policy"], first_steps=first, last_steps=last, reasoner=reasoner)
+                pol = fp8lin.policy_from_json(doc)
+                for n in range(1, 12):
+                    assert c_trace(pol, n) == opolicy.trace(doc, n)
+                    assert c_trace(pol, n, fp8lin.TOWER_REASONER) == opolicy.trace(doc, n, "reasoner")
+
+
+def test_null_policy_runs_w8a8():
+    assert fp8lin.policy_from_json("null") is None
+    assert c_trace(None, 8) == ["W8A8"] * 8
+
+
+def test_policy_step_bounds():
+    for step, n in ((-1, 8), (8, 8), (0, 0)):
+        with pytest.raises(fp8lin.Fp8LinError) as e:
+            fp8lin.fp8lin_step_policy(None, 0, step, n)
+        assert e.value.status == fp8lin.EINVAL
+    with pytest.raises(fp8lin.Fp8LinError):
+        fp8lin.fp8lin_step_policy(None, 2, 0, 8)
+
+
+MUTATIONS = [
+    lambda p: p.update(extra=1),
+    lambda p: p.pop("overlap"),
+    lambda p: p.pop("reasoner"),
+    lambda p: p.update(schema_version=2),
+    lambda p: p.update(schema_version=True),
+    lambda p: p.update(type="sigma_range"),
+    lambda p: p.update(index_space="timestep"),
+    lambda p: p.update(default_mode="w8a16"),
+    lambda p: p.update(overlap="a8"),
+    lambda p: p.update(first_steps=-1),
+    lambda p: p.update(last_steps=1.5),
+    lambda p: p.update(first_steps=None),
+    lambda p: p.update(reasoner="nvfp4"),
+]
+
+
+@pytest.mark.parametrize("mutate", MUTATIONS)
+def test_c_policy_fails_closed(golden, mutate):
+    doc = copy.deepcopy(golden["policy"])
+    mutate(doc)
+    with pytest.raises(opolicy.PolicyError):  # the oracle refuses it too
+        opolicy.validate(doc)
+    pol = fp8lin.policy_from_json(doc)
+    assert fp8lin.fp8lin_policy_validate(pol) == fp8lin.EPOLICY
+    with pytest.raises(fp8lin.Fp8LinError) as e:
+        fp8lin.fp8lin_step_policy(pol, 0, 0, 8)
+    assert e.value.status == fp8lin.EPOLICY
+
+
+def test_policy_validate_null_pointer(lib):
+    assert lib.fp8lin_policy_validate(None) == fp8lin.EINVAL
+
+
+# ---------------------------------------------------------------- argument validation
+
+
+def q(lib, x=FAKE, out=FAKE, rows=4, cols=64, s=0.01):
+    return lib.fp8lin_quantize_static(x, out, rows, cols, s, None)
+
+
+def test_quantize_validation(lib):
+    nan, inf = float("nan"), float("inf")
+    assert q(lib, x=None) == fp8lin.EINVAL
+    assert q(lib, rows=-1) == fp8lin.EINVAL
+    assert q(lib, cols=24) == fp8lin.ELAYOUT
+    assert q(lib, x=FAKE + 8) == fp8lin.ELAYOUT
+    assert q(lib, out=FAKE + 4) == fp8lin.ELAYOUT
+    for s in (0.0, -1.0, nan, inf, 1e-39, 2.0**127):
+        assert q(lib, s=s) == fp8lin.ESCALE, s
+    assert q(lib, cols=1 << 24) == fp8lin.EUNSUPPORTED
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_QUANTIZE)
+    assert q(lib, rows=0) == fp8lin.OK  # zero rows: a no-op that launches nothing
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_QUANTIZE) == before
+
+
+def g8(lib, qx=FAKE, qw=FAKE, y=FAKE, M=4, N=64, K=64, ldy=64, si=0.01, sw=0.001):
+    return lib.fp8lin_gemm_w8a8(qx, qw, y, M, N, K, ldy, si, sw, None)
+
+
+def test_gemm_w8a8_validation(lib):
+    assert g8(lib, qw=None) == fp8lin.EINVAL
+    assert g8(lib, K=0) == fp8lin.EINVAL
+    assert g8(lib, N=0) == fp8lin.EINVAL
+    assert g8(lib, K=40) == fp8lin.ELAYOUT
+    assert g8(lib, N=60, ldy=64) == fp8lin.ELAYOUT
+    assert g8(lib, ldy=56) == fp8lin.ELAYOUT
+    assert g8(lib, y=FAKE + 2) == fp8lin.ELAYOUT
+    assert g8(lib, si=float("nan")) == fp8lin.ESCALE
+    assert g8(lib, sw=0.0) == fp8lin.ESCALE
+    assert g8(lib, si=2.0**-100, sw=2.0**-100) == fp8lin.ESCALE  # product underflows
+    assert g8(lib, M=1 << 31) == fp8lin.EUNSUPPORTED
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
+    assert g8(lib, M=0) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before
+
+
+def test_gemm_w8a16_refuses_quantized_activation(lib):
+    args = (FAKE, FAKE, FAKE, 4, 64, 64, 64, 0.001, None)
+    assert lib.fp8lin_gemm_w8a16(args[0], fp8lin.DT_E4M3, *args[1:]) == fp8lin.EDTYPE
+    assert lib.fp8lin_gemm_w8a16(args[0], 7, *args[1:]) == fp8lin.EINVAL
+    assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_BF16, FAKE, FAKE, 4, 64, 40, 64, 0.001, None) == fp8lin.ELAYOUT
+    assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_BF16, FAKE, FAKE, 0, 64, 64, 64, 0.001, None) == fp8lin.OK
+
+
+def qkv(lib, scales_in=(0.01, 0.01, 0.01), n=(64, 64, 64), mode=0, ws=FAKE, nproj=3):
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    k = len(n)
+    return lib.fp8lin_qkv_shared(
+        FAKE, 4, 64, nproj, (vp * k)(*[FAKE] * k), (i64 * k)(*n), (f32 * k)(*[0.001] * k),
+        (f32 * k)(*scales_in), (vp * k)(*[FAKE] * k), ws, mode, None,
+    )
+
+
+def test_qkv_shared_validation(lib):
+    nudged = float(ctypes.c_float(0.01).value) * (1 + 2**-23)
+    assert qkv(lib, scales_in=(0.01, nudged, 0.01)) == fp8lin.ESCALE
+    assert qkv(lib, mode=fp8lin.MODE_W8A16, scales_in=(0.01, 0.02, 0.01)) == fp8lin.ESCALE
+    assert qkv(lib, n=(64, 60, 64)) == fp8lin.ELAYOUT
+    assert qkv(lib, ws=None) == fp8lin.EINVAL  # W8A8 needs the workspace
+    assert qkv(lib, mode=5) == fp8lin.EINVAL
+    assert qkv(lib, nproj=0) == fp8lin.EINVAL
+    assert qkv(lib, nproj=5, n=(64,) * 5, scales_in=(0.01,) * 5) == fp8lin.EINVAL
+
+
+def test_swiglu_validation(lib):
+    f = lib.fp8lin_swiglu_2in_quant
+    assert f(FAKE, FAKE, FAKE, 3, 4, 64, 0.1, None) == fp8lin.EINVAL
+    assert f(FAKE, FAKE, FAKE, fp8lin.DT_E4M3, 4, 40, 0.1, None) == fp8lin.ELAYOUT
+    assert f(FAKE, FAKE + 2, FAKE, fp8lin.DT_E4M3, 4, 64, 0.1, None) == fp8lin.ELAYOUT
+    assert f(FAKE, FAKE, FAKE, fp8lin.DT_E4M3, 4, 64, 0.0, None) == fp8lin.ESCALE
+    assert f(FAKE, FAKE, FAKE, fp8lin.DT_BF16, 0, 64, 0.0, None) == fp8lin.OK  # scale unused for bf16

@@ -1,0 +1,167 @@
+"""GPU parity: fp8lin_gemm_w8a8 and fp8lin_gemm_w8a16 against the oracle.
+
+Tolerance (elementwise): |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref), with
+y_ref the exact float64 result. Small cases are compared in full; the
+full-size 4096 x 4096 projections on sampled rows (every column).
+Weights are quantized on each side by its own quantizer from the same bf16
+weights, and the codes are checked equal first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import w8a16_linear_layers_amd as fp8lin
+from oracle import linear
+from tests.helpers import announce, assert_gemm_close, f32, sample_rows, u8
+from workloads import config1, config2, config3, normal_bf16, random_e4m3_codes
+
+pytestmark = pytest.mark.gpu
+
+
+def both_weights(w, s_w, gpu):
+    """The weight's E4M3 codes on the GPU (library) and on the host (oracle)."""
+    qw_gpu = fp8lin.fp8lin_quantize_static(w.to(gpu), s_w)
+    qw_ref = linear.quantize_static(f32(w), s_w)
+    assert np.array_equal(u8(qw_gpu), qw_ref)
+    return qw_gpu, qw_ref
+
+
+@pytest.mark.parametrize(
+    "m,n,k",
+    [(1, 8, 16), (7, 24, 48), (33, 40, 80), (64, 64, 64), (300, 520, 1040), (257, 264, 4096 + 16), (513, 1032, 272)],
+)
+def test_w8a8_random_codes(gpu, m, n, k):
+    announce("w8a8 random codes m=%d n=%d k=%d" % (m, n, k))
+    q = random_e4m3_codes((m, k), 1000 + m)
+    qw = random_e4m3_codes((n, k), 2000 + n)
+    s_in, s_w = 1.7e-3, 3.1e-5
+    y = fp8lin.fp8lin_gemm_w8a8(q.to(gpu), qw.to(gpu), s_in, s_w)
+    torch.cuda.synchronize()
+    assert_gemm_close(y, linear.gemm_w8a8(q.numpy(), qw.numpy(), s_in, s_w), "w8a8 %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 8, 16), (33, 40, 80), (300, 520, 1040), (257, 264, 4096 + 16)])
+def test_w8a16_random_codes(gpu, m, n, k):
+    announce("w8a16 random codes m=%d n=%d k=%d" % (m, n, k))
+    x = normal_bf16((m, k), 0.35, 3000 + m)
+    qw = random_e4m3_codes((n, k), 4000 + n)
+    s_w = 2.3e-4
+    y = fp8lin.fp8lin_gemm_w8a16(x.to(gpu), qw.to(gpu), s_w)
+    torch.cuda.synchronize()
+    assert_gemm_close(y, linear.gemm_w8a16(f32(x), qw.numpy(), s_w), "w8a16 %dx%dx%d" % (m, n, k))
+
+
+def test_config1_both_modes(gpu):
+    announce("config1 w8a8 + w8a16")
+    case = config1()
+    qw_gpu, qw_ref = both_weights(case.w, case.weight_scale, gpu)
+    x = case.x.to(gpu)
+    q = fp8lin.fp8lin_quantize_static(x, case.input_scale)
+    y8 = fp8lin.fp8lin_gemm_w8a8(q, qw_gpu, case.input_scale, case.weight_scale)
+    y16 = fp8lin.fp8lin_gemm_w8a16(x, qw_gpu, case.weight_scale)
+    torch.cuda.synchronize()
+    xr = f32(case.x)
+    qr = linear.quantize_static(xr, case.input_scale)
+    ref8 = linear.gemm_w8a8(qr, qw_ref, case.input_scale, case.weight_scale)
+    ref16 = linear.gemm_w8a16(xr, qw_ref, case.weight_scale)
+    assert_gemm_close(y8, ref8, "config1 w8a8")
+    assert_gemm_close(y16, ref16, "config1 w8a16")
+    # the two paths differ, and 16-bit activations land closer to the unquantized product
+    unq = xr.astype(np.float64) @ f32(case.w).astype(np.float64).T
+    e8 = np.sqrt(np.mean((f32(y8) - unq) ** 2))
+    e16 = np.sqrt(np.mean((f32(y16) - unq) ** 2))
+    assert not torch.equal(y8, y16)
+    assert e16 < e8
+
+
+@pytest.mark.parametrize("m", [1024, 8192])
+def test_config2_projection(gpu, m):
+    announce("config2 m=%d" % m)
+    case = config2(m)
+    qw_gpu, qw_ref = both_weights(case.w, case.weight_scale, gpu)
+    x = case.x.to(gpu)
+    q = fp8lin.fp8lin_quantize_static(x, case.input_scale)
+    y8 = fp8lin.fp8lin_gemm_w8a8(q, qw_gpu, case.input_scale, case.weight_scale)
+    y16 = fp8lin.fp8lin_gemm_w8a16(x, qw_gpu, case.weight_scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(m, 192, m)
+    xr = f32(case.x[rows])
+    qr = linear.quantize_static(xr, case.input_scale)
+    assert np.array_equal(u8(q[torch.from_numpy(rows).to(gpu)]), qr)
+    assert_gemm_close(f32(y8)[rows], linear.gemm_w8a8(qr, qw_ref, case.input_scale, case.weight_scale), "w8a8")
+    assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(xr, qw_ref, case.weight_scale), "w8a16")
+
+
+def test_headline_shape_sampled(gpu):
+    """M=16384, K=N=4096: the Q projection of the shared-QKV workload."""
+    announce("headline 16384x4096x4096")
+    case = config3()
+    qw_gpu, qw_ref = both_weights(case.ws[0], case.weight_scales[0], gpu)
+    x = case.x.to(gpu)
+    q = fp8lin.fp8lin_quantize_static(x, case.input_scale)
+    y8 = fp8lin.fp8lin_gemm_w8a8(q, qw_gpu, case.input_scale, case.weight_scales[0])
+    y16 = fp8lin.fp8lin_gemm_w8a16(x, qw_gpu, case.weight_scales[0])
+    torch.cuda.synchronize()
+    rows = sample_rows(16384, 160, 77)
+    xr = f32(case.x[rows])
+    qr = linear.quantize_static(xr, case.input_scale)
+    assert_gemm_close(f32(y8)[rows], linear.gemm_w8a8(qr, qw_ref, case.input_scale, case.weight_scales[0]), "w8a8")
+    assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(xr, qw_ref, case.weight_scales[0]), "w8a16")
+
+
+def test_w8a16_identity_weight_is_exact(gpu):
+    announce("w8a16 identity weight")
+    k = 512
+    x = normal_bf16((300, k), 0.35, 9)
+    ident = torch.where(torch.eye(k, dtype=torch.bool), 0x38, 0x00).to(torch.uint8)
+    y = fp8lin.fp8lin_gemm_w8a16(x.to(gpu), ident.to(gpu), 1.0)
+    assert torch.equal(y.cpu(), x)
+
+
+def test_w8a8_identity_weight(gpu):
+    announce("w8a8 identity weight")
+    k = 256
+    q = random_e4m3_codes((130, k), 21)
+    ident = torch.where(torch.eye(k, dtype=torch.bool), 0x38, 0x00).to(torch.uint8)
+    s_in = 0.01
+    y = fp8lin.fp8lin_gemm_w8a8(q.to(gpu), ident.to(gpu), s_in, 1.0)
+    ref = linear.gemm_w8a8(q.numpy(), ident.numpy(), s_in, 1.0)
+    assert_gemm_close(y, ref, "identity")
+
+
+def test_output_stride_and_guard(gpu):
+    """ldy > N: only columns [0, N) of each row are written."""
+    announce("w8a8 ldy > n")
+    m, n, k, ldy = 70, 136, 128, 200
+    q = random_e4m3_codes((m, k), 31).to(gpu)
+    qw = random_e4m3_codes((n, k), 32).to(gpu)
+    buf = torch.full((m, ldy), 7.0, dtype=torch.bfloat16, device=gpu)
+    fp8lin.fp8lin_gemm_w8a8(q, qw, 0.01, 0.02, out=buf, ldy=ldy)
+    fp8lin.fp8lin_gemm_w8a16(torch.zeros((m, k), dtype=torch.bfloat16, device=gpu), qw, 0.02, out=buf[:, 8:], ldy=ldy)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:, n + 8 :] == 7.0)
+    assert torch.all(buf[:, 8 : n + 8] == 0)
+    ref = linear.gemm_w8a8(u8(q), u8(qw), 0.01, 0.02)
+    assert_gemm_close(f32(buf[:, :8]), ref[:, :8], "ldy columns")
+
+
+def test_rank3_activation_and_empty(gpu):
+    announce("w8a8 rank-3 input and M=0")
+    q = random_e4m3_codes((2, 3, 64), 41).to(gpu)
+    qw = random_e4m3_codes((16, 64), 42).to(gpu)
+    y = fp8lin.fp8lin_gemm_w8a8(q, qw, 0.5, 0.25)
+    assert y.shape == (2, 3, 16)
+    ref = linear.gemm_w8a8(u8(q).reshape(6, 64), u8(qw), 0.5, 0.25)
+    assert_gemm_close(f32(y).reshape(6, 16), ref, "rank3")
+    empty = fp8lin.fp8lin_gemm_w8a8(q[:0], qw, 0.5, 0.25)
+    assert empty.shape == (0, 3, 16)
+
+
+def test_w8a16_refuses_fp8_activation(gpu):
+    announce("w8a16 refuses fp8")
+    q = torch.zeros((4, 64), dtype=torch.uint8, device=gpu)
+    qw = torch.zeros((16, 64), dtype=torch.uint8, device=gpu)
+    with pytest.raises(fp8lin.Fp8LinError) as e:
+        fp8lin.fp8lin_gemm_w8a16(q, qw, 1.0)
+    assert e.value.status == fp8lin.EDTYPE

@@ -1,0 +1,84 @@
+"""GPU parity: fp8lin_quantize_static against the oracle, bit-exact.
+
+Exhaustive over all 65,536 bf16 inputs for a set of scales (including the
+scale the calibration log of the pages implies), then the synthetic
+activations of the workloads at full size, ragged and empty shapes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import w8a16_linear_layers_amd as fp8lin
+from oracle import linear
+from tests.helpers import announce, f32, u8
+from workloads import all_bf16_patterns, config1, config2, config3, normal_bf16
+
+pytestmark = pytest.mark.gpu
+
+SCALES = [
+    1.0,
+    0.5430 / 448,  # input amax of the calibration log -> scale
+    0.5039 / 448,  # weight amax of the calibration log -> scale
+    1e-3,
+    3.7,
+    2.0**-7,
+    1.0 + 2.0**-23,
+    0.02 / 448,
+    2.0**-120,
+    2.0**100,
+]
+
+
+@pytest.mark.parametrize("scale", SCALES + list(np.random.default_rng(5).uniform(1e-5, 2.0, 6)))
+def test_every_bf16_input(gpu, scale):
+    announce("quantize all bf16 patterns, scale=%r" % scale)
+    x = all_bf16_patterns().reshape(4096, 16)
+    s = float(np.float32(scale))
+    q = fp8lin.fp8lin_quantize_static(x.to(gpu), s)
+    torch.cuda.synchronize()
+    ref = linear.quantize_static(f32(x), s)
+    got = u8(q)
+    assert np.array_equal(got, ref), "mismatches: %d" % np.count_nonzero(got != ref)
+
+
+def test_config1_activation(gpu):
+    announce("quantize config1 x [128, 512]")
+    case = config1()
+    q = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    assert np.array_equal(u8(q), linear.quantize_static(f32(case.x), case.input_scale))
+
+
+@pytest.mark.parametrize("cfg", ["config2", "config3"])
+def test_full_size_activation(gpu, cfg):
+    case = config2() if cfg == "config2" else config3()
+    announce("quantize %s x %s" % (cfg, tuple(case.x.shape)))
+    q = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(q), linear.quantize_static(f32(case.x), case.input_scale))
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (37, 208), (3, 5, 64), (1, 1040), (513, 4096 + 16)])
+def test_ragged_shapes(gpu, shape):
+    announce("quantize ragged %s" % (shape,))
+    x = normal_bf16(shape, 0.35, 17)
+    s = 0.35 * 3 / 448
+    q = fp8lin.fp8lin_quantize_static(x.to(gpu), s)
+    assert q.shape == x.shape
+    assert np.array_equal(u8(q), linear.quantize_static(f32(x), s))
+
+
+def test_zero_rows_is_a_noop(gpu):
+    announce("quantize zero rows")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=gpu)
+    q = fp8lin.fp8lin_quantize_static(x, 0.01)
+    assert q.shape == (0, 64)
+
+
+def test_writes_only_its_output(gpu):
+    announce("quantize guard bytes")
+    x = normal_bf16((10, 48), 1.0, 3).to(gpu)
+    buf = torch.full((10 * 48 + 64,), 0xA5, dtype=torch.uint8, device=gpu)
+    out = buf[:480].view(10, 48)
+    fp8lin.fp8lin_quantize_static(x, 0.01, out=out)
+    assert torch.all(buf[480:] == 0xA5)

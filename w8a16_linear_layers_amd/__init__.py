@@ -1,0 +1,332 @@
+"""Python binding of libfp8lin (static per-tensor FP8 linear layers, MI355X).
+
+Argument marshalling only: every function below forwards to the C entry
+point of the same name in ``libfp8lin.so`` (declared in ``include/fp8lin.h``),
+passing device pointers, sizes, host scales and the current HIP stream.
+torch provides device memory and streams; no arithmetic of the layer runs
+here. If the library is not built, loading fails loudly -- there is no
+fallback path.
+"""
+
+import ctypes
+import json
+import os
+
+import torch
+
+__all__ = [
+    "Fp8LinError",
+    "load_library",
+    "library_path",
+    "MODE_W8A8",
+    "MODE_W8A16",
+    "DT_BF16",
+    "DT_E4M3",
+    "TOWER_GENERATION",
+    "TOWER_REASONER",
+    "Policy",
+    "policy_from_json",
+    "fp8lin_quantize_static",
+    "fp8lin_gemm_w8a8",
+    "fp8lin_gemm_w8a16",
+    "fp8lin_qkv_shared",
+    "fp8lin_swiglu_2in_quant",
+    "fp8lin_policy_validate",
+    "fp8lin_step_policy",
+    "fp8lin_strerror",
+    "fp8lin_launch_count",
+    "KERNEL_QUANTIZE",
+    "KERNEL_GEMM_W8A8",
+    "KERNEL_GEMM_W8A16",
+    "KERNEL_SWIGLU",
+]
+
+MODE_W8A8, MODE_W8A16 = 0, 1
+DT_BF16, DT_E4M3 = 0, 1
+TOWER_GENERATION, TOWER_REASONER = 0, 1
+KERNEL_QUANTIZE, KERNEL_GEMM_W8A8, KERNEL_GEMM_W8A16, KERNEL_SWIGLU = 0, 1, 2, 3
+
+OK, EINVAL, ELAYOUT, EDTYPE, ESCALE, EPOLICY, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+EXPORTS = (
+    "fp8lin_quantize_static",
+    "fp8lin_gemm_w8a8",
+    "fp8lin_gemm_w8a16",
+    "fp8lin_qkv_shared",
+    "fp8lin_swiglu_2in_quant",
+    "fp8lin_policy_validate",
+    "fp8lin_step_policy",
+    "fp8lin_strerror",
+    "fp8lin_launch_count",
+)
+
+
+class Fp8LinError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, fp8lin_strerror(status), status))
+
+
+class Policy(ctypes.Structure):
+    """fp8lin_policy (see include/fp8lin.h)."""
+
+    _fields_ = [
+        ("schema_version", ctypes.c_int32),
+        ("type", ctypes.c_int32),
+        ("index_space", ctypes.c_int32),
+        ("default_mode", ctypes.c_int32),
+        ("overlap", ctypes.c_int32),
+        ("first_steps", ctypes.c_int32),
+        ("last_steps", ctypes.c_int32),
+        ("reasoner_mode", ctypes.c_int32),
+        ("present_mask", ctypes.c_uint32),
+    ]
+
+
+def library_path():
+    return os.path.join(_HERE, "libfp8lin.so")
+
+
+def load_library():
+    """Load libfp8lin.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libfp8lin.so is not built (%s); run `python -m w8a16_linear_layers_amd.build` "
+            "or __graft_entry__.build()" % path
+        )
+    lib = ctypes.CDLL(path)
+    i32, i64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.fp8lin_quantize_static.argtypes = [vp, vp, i64, i64, f32, vp]
+    lib.fp8lin_gemm_w8a8.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
+    lib.fp8lin_gemm_w8a16.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, f32, vp]
+    lib.fp8lin_qkv_shared.argtypes = [
+        vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32),
+        ctypes.POINTER(f32), ctypes.POINTER(vp), vp, i32, vp,
+    ]
+    lib.fp8lin_swiglu_2in_quant.argtypes = [vp, vp, vp, i32, i64, i64, f32, vp]
+    lib.fp8lin_policy_validate.argtypes = [ctypes.POINTER(Policy)]
+    lib.fp8lin_step_policy.argtypes = [ctypes.POINTER(Policy), i32, i32, i32, ctypes.POINTER(i32)]
+    lib.fp8lin_strerror.argtypes = [i32]
+    lib.fp8lin_strerror.restype = ctypes.c_char_p
+    lib.fp8lin_launch_count.argtypes = [i32]
+    lib.fp8lin_launch_count.restype = i64
+    for name in EXPORTS[:7]:
+        getattr(lib, name).restype = i32
+    _LIB = lib
+    return lib
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status, what):
+    if status != OK:
+        raise Fp8LinError(status, what)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _rows(t):
+    """Flatten the leading dimensions of a rank-N tensor: [..., K] -> (rows, K)."""
+    k = t.shape[-1] if t.dim() > 0 else 1
+    return (t.numel() // k if k else 0), k
+
+
+def fp8lin_quantize_static(x, input_scale, out=None, stream=None):
+    """E4M3 codes (torch.uint8, same shape as x) of a bf16 tensor x."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    rows, cols = _rows(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(
+        load_library().fp8lin_quantize_static(_ptr(x), _ptr(out), rows, cols, float(input_scale), _stream(stream)),
+        "fp8lin_quantize_static",
+    )
+    return out
+
+
+def _gemm_out(m_shape, n, device, out, ldy):
+    if out is None:
+        out = torch.empty(tuple(m_shape) + (n,), dtype=torch.bfloat16, device=device)
+        ldy = n
+    elif ldy is None:
+        ldy = out.stride(-2) if out.dim() >= 2 else n
+    return out, ldy
+
+
+def fp8lin_gemm_w8a8(qx, qw, input_scale, weight_scale, out=None, ldy=None, stream=None):
+    """y = (dec(qx) dec(qw)^T) * s_in * s_w in bf16; qx [..., K] uint8, qw [N, K] uint8."""
+    if qx.dtype != torch.uint8 or qw.dtype != torch.uint8:
+        raise TypeError("qx and qw must hold E4M3 codes as torch.uint8")
+    m, k = _rows(qx)
+    n = qw.shape[0]
+    out, ldy = _gemm_out(qx.shape[:-1], n, qx.device, out, ldy)
+    _check(
+        load_library().fp8lin_gemm_w8a8(
+            _ptr(qx), _ptr(qw), _ptr(out), m, n, k, ldy, float(input_scale), float(weight_scale), _stream(stream)
+        ),
+        "fp8lin_gemm_w8a8",
+    )
+    return out
+
+
+def fp8lin_gemm_w8a16(x, qw, weight_scale, out=None, ldy=None, stream=None):
+    """y = (x dec(qw)^T) * s_w in bf16; x [..., K] bf16 (FP8 input is refused)."""
+    dtype = DT_E4M3 if x.dtype in (torch.uint8, torch.float8_e4m3fn) else DT_BF16
+    if dtype == DT_BF16 and x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    m, k = _rows(x)
+    n = qw.shape[0]
+    out, ldy = _gemm_out(x.shape[:-1], n, x.device, out, ldy)
+    _check(
+        load_library().fp8lin_gemm_w8a16(
+            _ptr(x), dtype, _ptr(qw), _ptr(out), m, n, k, ldy, float(weight_scale), _stream(stream)
+        ),
+        "fp8lin_gemm_w8a16",
+    )
+    return out
+
+
+def fp8lin_qkv_shared(x, qws, weight_scales, input_scales, mode, outs=None, workspace=None, stream=None):
+    """Shared-input projections; returns (list of bf16 outputs, workspace codes or None)."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    m, k = _rows(x)
+    n = len(qws)
+    if outs is None:
+        outs = [torch.empty(tuple(x.shape[:-1]) + (w.shape[0],), dtype=torch.bfloat16, device=x.device) for w in qws]
+    if mode == MODE_W8A8 and workspace is None:
+        workspace = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    c_w = (vp * n)(*[w.data_ptr() for w in qws])
+    c_n = (i64 * n)(*[w.shape[0] for w in qws])
+    c_sw = (f32 * n)(*[float(s) for s in weight_scales])
+    c_si = (f32 * n)(*[float(s) for s in input_scales])
+    c_y = (vp * n)(*[o.data_ptr() for o in outs])
+    _check(
+        load_library().fp8lin_qkv_shared(
+            _ptr(x), m, k, n, c_w, c_n, c_sw, c_si, c_y, _ptr(workspace), int(mode), _stream(stream)
+        ),
+        "fp8lin_qkv_shared",
+    )
+    return outs, (workspace if mode == MODE_W8A8 else None)
+
+
+def fp8lin_swiglu_2in_quant(gate, up, out_scale=1.0, out_dtype=DT_E4M3, out=None, stream=None):
+    """silu(gate) * up as E4M3 codes (uint8) or bf16; gate/up contiguous bf16 of one shape."""
+    if gate.dtype != torch.bfloat16 or up.dtype != torch.bfloat16:
+        raise TypeError("gate and up must be bfloat16")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    if not (gate.is_contiguous() and up.is_contiguous()):
+        raise ValueError("gate and up must be contiguous")
+    rows, cols = _rows(gate)
+    if out is None:
+        dt = torch.uint8 if out_dtype == DT_E4M3 else torch.bfloat16
+        out = torch.empty(gate.shape, dtype=dt, device=gate.device)
+    _check(
+        load_library().fp8lin_swiglu_2in_quant(
+            _ptr(gate), _ptr(up), _ptr(out), int(out_dtype), rows, cols, float(out_scale), _stream(stream)
+        ),
+        "fp8lin_swiglu_2in_quant",
+    )
+    return out
+
+
+# ---------------------------------------------------------------- policy
+
+_POLICY_FIELDS = (
+    "schema_version",
+    "type",
+    "index_space",
+    "default_mode",
+    "overlap",
+    "first_steps",
+    "last_steps",
+    "reasoner",
+)
+_ENUMS = {
+    "type": {"first_last_steps": 1},
+    "index_space": {"scheduler_step": 1},
+    "default_mode": {"w8a8": MODE_W8A8, "w8a16": MODE_W8A16},
+    "overlap": {"a16": 1},
+    "reasoner": {"a8": MODE_W8A8, "a16": MODE_W8A16},
+}
+_UNKNOWN = -1
+
+
+def _int_field(v):
+    return v if isinstance(v, int) and not isinstance(v, bool) and -(2**31) <= v < 2**31 else None
+
+
+def policy_from_json(doc):
+    """Parse a diffusion_step_policy (dict or JSON text) into a Policy.
+
+    Returns None for a null policy (runtime: null). Field values are mapped
+    without judging them; fp8lin_policy_validate decides. Unknown fields set
+    the unknown-field bit; a non-integer count becomes -1 (refused).
+    """
+    if isinstance(doc, (str, bytes)):
+        doc = json.loads(doc)
+    if doc is None:
+        return None
+    p = Policy()
+    if not isinstance(doc, dict):
+        p.present_mask = 1 << 31
+        return p
+    mask = 0
+    for i, f in enumerate(_POLICY_FIELDS):
+        if f in doc:
+            mask |= 1 << i
+    if set(doc) - set(_POLICY_FIELDS):
+        mask |= 1 << 31
+    p.present_mask = mask
+    sv = _int_field(doc.get("schema_version"))
+    p.schema_version = sv if sv is not None else _UNKNOWN
+    for f, attr in (("type", "type"), ("index_space", "index_space"), ("default_mode", "default_mode"),
+                    ("overlap", "overlap"), ("reasoner", "reasoner_mode")):
+        v = doc.get(f)
+        setattr(p, attr, _ENUMS[f].get(v, _UNKNOWN) if isinstance(v, str) else _UNKNOWN)
+    for f in ("first_steps", "last_steps"):
+        v = _int_field(doc.get(f))
+        setattr(p, f, v if v is not None else _UNKNOWN)
+    return p
+
+
+def fp8lin_policy_validate(policy):
+    return load_library().fp8lin_policy_validate(ctypes.byref(policy) if policy is not None else None)
+
+
+def fp8lin_step_policy(policy, tower, step, num_steps):
+    """Mode (MODE_W8A8 / MODE_W8A16) of one call; raises Fp8LinError on a bad policy."""
+    out = ctypes.c_int32(-1)
+    st = load_library().fp8lin_step_policy(
+        ctypes.byref(policy) if policy is not None else None, int(tower), int(step), int(num_steps), ctypes.byref(out)
+    )
+    _check(st, "fp8lin_step_policy")
+    return out.value
+
+
+def fp8lin_strerror(status):
+    return load_library().fp8lin_strerror(int(status)).decode()
+
+
+def fp8lin_launch_count(kind):
+    return load_library().fp8lin_launch_count(int(kind))

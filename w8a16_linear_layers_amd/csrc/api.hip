@@ -1,0 +1,247 @@
+// C ABI of libfp8lin: argument validation, dispatch to the kernel launchers,
+// the diffusion step policy and the error strings. Everything is validated
+// before the first launch, so a failing call enqueues nothing.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "fp8lin.h"
+#include "internal.h"
+
+namespace {
+
+using fp8lin::GemmArgs;
+
+std::atomic<int64_t> g_launches[FP8LIN_KERNEL_KINDS];
+
+void count_launch(int kind) { g_launches[kind].fetch_add(1, std::memory_order_relaxed); }
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A static scale must be finite and in [2^-126, 2^126], so 1/s is normal.
+bool scale_ok(float s) { return std::isfinite(s) && s >= 0x1p-126f && s <= 0x1p126f; }
+
+int32_t check_matrix(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return FP8LIN_EINVAL;
+  if (rows > kMaxRows || cols >= kMaxK || rows * cols >= kMaxElems) return FP8LIN_EUNSUPPORTED;
+  if (cols % 16 != 0) return FP8LIN_ELAYOUT;
+  return FP8LIN_OK;
+}
+
+// Shared checks of one projection of a GEMM (weight [n, k], output [m, ldy]).
+int32_t check_output(const void* qw, const void* y, int64_t N, int64_t ldy, int64_t M) {
+  if (qw == nullptr || (M > 0 && y == nullptr)) return FP8LIN_EINVAL;
+  if (N <= 0 || ldy <= 0) return FP8LIN_EINVAL;
+  if (N > kMaxRows || ldy > kMaxRows) return FP8LIN_EUNSUPPORTED;
+  if (N % 8 != 0 || ldy % 8 != 0 || ldy < N) return FP8LIN_ELAYOUT;
+  if (!aligned16(qw) || !aligned16(y)) return FP8LIN_ELAYOUT;  // NULL is aligned
+  return FP8LIN_OK;
+}
+
+int32_t finish_plan(GemmArgs& a) {
+  int64_t tiles = 0;
+  const int64_t tm = (a.m + fp8lin::kTileM - 1) / fp8lin::kTileM;
+  for (int i = 0; i < a.ngroups; ++i) tiles += tm * ((a.g[i].n + fp8lin::kTileN - 1) / fp8lin::kTileN);
+  if (tiles >= (int64_t(1) << 31)) return FP8LIN_EUNSUPPORTED;
+  fp8lin::gemm_plan(a);
+  return FP8LIN_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? FP8LIN_OK : FP8LIN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp8lin_quantize_static(const void* x_bf16, void* q_e4m3, int64_t rows, int64_t cols, float input_scale,
+                               hipStream_t stream) {
+  int32_t st = check_matrix(rows, cols);
+  if (st != FP8LIN_OK) return st;
+  if (!scale_ok(input_scale)) return FP8LIN_ESCALE;
+  if (rows == 0 || cols == 0) return FP8LIN_OK;  // empty: pointers may be NULL
+  if (x_bf16 == nullptr || q_e4m3 == nullptr) return FP8LIN_EINVAL;
+  if (!aligned16(x_bf16) || !aligned16(q_e4m3)) return FP8LIN_ELAYOUT;
+  count_launch(FP8LIN_KERNEL_QUANTIZE);
+  return hip_status(fp8lin::launch_quantize(x_bf16, q_e4m3, rows * cols, input_scale, stream));
+}
+
+int32_t fp8lin_gemm_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                         float input_scale, float weight_scale, hipStream_t stream) {
+  int32_t st = check_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && qx == nullptr)) return FP8LIN_EINVAL;
+  if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
+  if (!aligned16(qx)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(input_scale) || !scale_ok(weight_scale)) return FP8LIN_ESCALE;
+  const float alpha = input_scale * weight_scale;
+  if (!std::isfinite(alpha) || alpha == 0.0f) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  GemmArgs a{};
+  a.x = qx;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = 1;
+  a.g[0].w = static_cast<const uint8_t*>(qw);
+  a.g[0].y = y_bf16;
+  a.g[0].n = (int32_t)N;
+  a.g[0].ldy = (int32_t)ldy;
+  a.g[0].alpha = alpha;
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  count_launch(FP8LIN_KERNEL_GEMM_W8A8);
+  return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
+}
+
+int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,
+                          int64_t K, int64_t ldy, float weight_scale, hipStream_t stream) {
+  if (x_dtype == FP8LIN_DT_E4M3) return FP8LIN_EDTYPE;
+  if (x_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
+  int32_t st = check_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && x == nullptr)) return FP8LIN_EINVAL;
+  if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
+  if (!aligned16(x)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(weight_scale)) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  GemmArgs a{};
+  a.x = x;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = 1;
+  a.g[0].w = static_cast<const uint8_t*>(qw);
+  a.g[0].y = y_bf16;
+  a.g[0].n = (int32_t)N;
+  a.g[0].ldy = (int32_t)ldy;
+  a.g[0].alpha = weight_scale;
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  count_launch(FP8LIN_KERNEL_GEMM_W8A16);
+  return hip_status(fp8lin::launch_gemm_w8a16(a, stream));
+}
+
+int32_t fp8lin_qkv_shared(const void* x_bf16, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
+                          const int64_t n_out[], const float weight_scale[], const float input_scale[],
+                          void* const y_bf16[], void* qx_workspace, int32_t mode, hipStream_t stream) {
+  if (qw == nullptr || n_out == nullptr || weight_scale == nullptr || input_scale == nullptr || y_bf16 == nullptr)
+    return FP8LIN_EINVAL;
+  if (nproj < 1 || nproj > fp8lin::kMaxGroups) return FP8LIN_EINVAL;
+  if (mode != FP8LIN_MODE_W8A8 && mode != FP8LIN_MODE_W8A16) return FP8LIN_EINVAL;
+  int32_t st = check_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && x_bf16 == nullptr)) return FP8LIN_EINVAL;
+  if (!aligned16(x_bf16)) return FP8LIN_ELAYOUT;
+  if (mode == FP8LIN_MODE_W8A8) {
+    if (M > 0 && qx_workspace == nullptr) return FP8LIN_EINVAL;
+    if (!aligned16(qx_workspace)) return FP8LIN_ELAYOUT;
+  }
+  uint32_t s0;
+  std::memcpy(&s0, &input_scale[0], sizeof s0);
+  for (int i = 0; i < nproj; ++i) {
+    if ((st = check_output(qw[i], y_bf16[i], n_out[i], n_out[i], M)) != FP8LIN_OK) return st;
+    uint32_t si;
+    std::memcpy(&si, &input_scale[i], sizeof si);
+    if (si != s0) return FP8LIN_ESCALE;  // the group must share one calibrated input scale
+    if (!scale_ok(weight_scale[i])) return FP8LIN_ESCALE;
+  }
+  if (!scale_ok(input_scale[0])) return FP8LIN_ESCALE;
+  GemmArgs a{};
+  a.x = mode == FP8LIN_MODE_W8A8 ? qx_workspace : x_bf16;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = nproj;
+  for (int i = 0; i < nproj; ++i) {
+    a.g[i].w = static_cast<const uint8_t*>(qw[i]);
+    a.g[i].y = y_bf16[i];
+    a.g[i].n = (int32_t)n_out[i];
+    a.g[i].ldy = (int32_t)n_out[i];
+    a.g[i].alpha = mode == FP8LIN_MODE_W8A8 ? input_scale[0] * weight_scale[i] : weight_scale[i];
+    if (!std::isfinite(a.g[i].alpha) || a.g[i].alpha == 0.0f) return FP8LIN_ESCALE;
+  }
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  if (M == 0) return FP8LIN_OK;
+  if (mode == FP8LIN_MODE_W8A8) {
+    count_launch(FP8LIN_KERNEL_QUANTIZE);
+    if ((st = hip_status(fp8lin::launch_quantize(x_bf16, qx_workspace, M * K, input_scale[0], stream))) != FP8LIN_OK)
+      return st;
+    count_launch(FP8LIN_KERNEL_GEMM_W8A8);
+    return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
+  }
+  count_launch(FP8LIN_KERNEL_GEMM_W8A16);
+  return hip_status(fp8lin::launch_gemm_w8a16(a, stream));
+}
+
+int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void* out, int32_t out_dtype, int64_t rows,
+                                int64_t cols, float out_scale, hipStream_t stream) {
+  if (out_dtype != FP8LIN_DT_E4M3 && out_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
+  int32_t st = check_matrix(rows, cols);
+  if (st != FP8LIN_OK) return st;
+  const bool fp8_out = out_dtype == FP8LIN_DT_E4M3;
+  if (fp8_out && !scale_ok(out_scale)) return FP8LIN_ESCALE;
+  if (rows == 0 || cols == 0) return FP8LIN_OK;  // empty: pointers may be NULL
+  if (gate_bf16 == nullptr || up_bf16 == nullptr || out == nullptr) return FP8LIN_EINVAL;
+  if (!aligned16(gate_bf16) || !aligned16(up_bf16) || !aligned16(out)) return FP8LIN_ELAYOUT;
+  count_launch(FP8LIN_KERNEL_SWIGLU);
+  return hip_status(fp8lin::launch_swiglu(gate_bf16, up_bf16, out, fp8_out, rows * cols, out_scale, stream));
+}
+
+int32_t fp8lin_policy_validate(const fp8lin_policy* p) {
+  if (p == nullptr) return FP8LIN_EINVAL;
+  if ((p->present_mask & FP8LIN_PF_UNKNOWN_FIELD) != 0) return FP8LIN_EPOLICY;
+  if ((p->present_mask & FP8LIN_PF_ALL) != FP8LIN_PF_ALL) return FP8LIN_EPOLICY;
+  if (p->schema_version != 1) return FP8LIN_EPOLICY;
+  if (p->type != FP8LIN_POLICY_TYPE_FIRST_LAST_STEPS) return FP8LIN_EPOLICY;
+  if (p->index_space != FP8LIN_POLICY_INDEX_SCHEDULER_STEP) return FP8LIN_EPOLICY;
+  if (p->default_mode != FP8LIN_MODE_W8A8) return FP8LIN_EPOLICY;
+  if (p->overlap != FP8LIN_POLICY_OVERLAP_A16) return FP8LIN_EPOLICY;
+  if (p->first_steps < 0 || p->last_steps < 0) return FP8LIN_EPOLICY;
+  if (p->reasoner_mode != FP8LIN_MODE_W8A8 && p->reasoner_mode != FP8LIN_MODE_W8A16) return FP8LIN_EPOLICY;
+  return FP8LIN_OK;
+}
+
+int32_t fp8lin_step_policy(const fp8lin_policy* p, int32_t tower, int32_t step, int32_t num_steps,
+                           int32_t* mode_out) {
+  if (mode_out == nullptr) return FP8LIN_EINVAL;
+  if (tower != FP8LIN_TOWER_GENERATION && tower != FP8LIN_TOWER_REASONER) return FP8LIN_EINVAL;
+  if (num_steps < 1 || step < 0 || step >= num_steps) return FP8LIN_EINVAL;
+  if (p == nullptr) {
+    *mode_out = FP8LIN_MODE_W8A8;
+    return FP8LIN_OK;
+  }
+  const int32_t st = fp8lin_policy_validate(p);
+  if (st != FP8LIN_OK) return st;
+  if (tower == FP8LIN_TOWER_REASONER) {
+    *mode_out = p->reasoner_mode;
+    return FP8LIN_OK;
+  }
+  if (num_steps == 1) {
+    *mode_out = FP8LIN_MODE_W8A8;
+    return FP8LIN_OK;
+  }
+  const bool first = step < p->first_steps;
+  const bool last = (int64_t)step >= (int64_t)num_steps - (int64_t)p->last_steps;
+  *mode_out = (first || last) ? FP8LIN_MODE_W8A16 : FP8LIN_MODE_W8A8;
+  return FP8LIN_OK;
+}
+
+const char* fp8lin_strerror(int32_t status) {
+  switch (status) {
+    case FP8LIN_OK: return "success";
+    case FP8LIN_EINVAL: return "invalid argument (null pointer, negative size or unknown enum value)";
+    case FP8LIN_ELAYOUT: return "unsupported layout (alignment, divisibility or leading dimension)";
+    case FP8LIN_EDTYPE: return "activation dtype not accepted by this call";
+    case FP8LIN_ESCALE: return "invalid scale, or input scales of a shared group differ";
+    case FP8LIN_EPOLICY: return "invalid diffusion step policy";
+    case FP8LIN_EUNSUPPORTED: return "size beyond the supported limits";
+    case FP8LIN_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int64_t fp8lin_launch_count(int32_t kind) {
+  if (kind < 0 || kind >= FP8LIN_KERNEL_KINDS) return -1;
+  return g_launches[kind].load(std::memory_order_relaxed);
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Device helpers shared by the elementwise kernels: bf16 unpacking and the
+// float -> OCP E4M3 conversion with saturation and round-to-nearest-even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Saturate to the finite E4M3 range; +-Inf become +-448.
+__device__ __forceinline__ float clamp448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
+// E4M3 code of a finite value already inside [-448, 448]: the gfx950
+// converter rounds to nearest even and keeps the sign of zero.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
+}
+
+// Bracketing factors 1 -+ 2^-21 (both exact in float32).
+constexpr float kBelow = 1.0f - 0x1p-21f;
+constexpr float kAbove = 1.0f + 0x1p-21f;
+
+// Fast static quantization of two bf16 values packed in `w`.
+//
+// The exact code is E4M3(RN32(x / s)). With r = RN32(1 / s) the product
+// q = RN32(x * r) is within 1.5 float32 ulp of RN32(x / s) whenever q is a
+// normal float, so RN32(x / s) lies between RN32(q * (1 - 2^-21)) and
+// RN32(q * (1 + 2^-21)) (each at least 3 ulp away from q). E4M3 rounding is
+// monotone, so when both bracket ends give the same code that code is exact.
+// If q is subnormal or zero, every candidate is below 2^-11 and the code is
+// a signed zero either way; if x * r overflows, the quotient saturates too.
+// A disagreement (a value within a few ulp of an E4M3 rounding midpoint) or
+// a NaN input sets `doubt`, and the caller redoes the vector exactly.
+//
+// Returns the two codes in bytes 0 and 2 (bytes 1 and 3 hold the upper
+// bracket's codes).
+__device__ __forceinline__ uint32_t quant_pair_fast(uint32_t w, float r, uint32_t& doubt) {
+  const float q0 = bf16_lo(w) * r;
+  const float q1 = bf16_hi(w) * r;
+  uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(q0 * kBelow), clamp448(q0 * kAbove), 0, false);
+  p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(q1 * kBelow), clamp448(q1 * kAbove), (int)p, true);
+  doubt |= (p ^ (p >> 8)) & 0x00ff00ffu;
+  // bf16 NaN: magnitude bits above 0x7f80 (adding 0x7f carries into bit 15)
+  doubt |= ((w & 0x7fff7fffu) + 0x007f007fu) & 0x80008000u;
+  return p;
+}
+
+// Four codes from two quant_pair_fast results: bytes 0 and 2 of each.
+__device__ __forceinline__ uint32_t pick_codes(uint32_t p0, uint32_t p1) {
+  return (p0 & 0xffu) | ((p0 >> 8) & 0xff00u) | ((p1 & 0xffu) << 16) | ((p1 << 8) & 0xff000000u);
+}
+
+// Exact static quantization of one bf16 value (bits in the low 16 bits):
+// the IEEE correctly rounded float32 quotient, then saturate and round.
+__device__ __forceinline__ uint32_t quant_one_exact(uint32_t bits, float s) {
+  const float x = __uint_as_float(bits << 16);
+  if (__builtin_isnan(x)) return 0x7fu | ((bits >> 8) & 0x80u);
+  const float q = x / s;  // correctly rounded division (hipcc default)
+  return e4m3_code(clamp448(q));
+}
+
+__device__ __forceinline__ uint32_t quant_word_exact(uint32_t w, float s) {
+  return quant_one_exact(w & 0xffffu, s) | (quant_one_exact(w >> 16, s) << 8);
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel
+// translation units. Launchers assume validated arguments: they do no checks
+// of their own and return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+// Tile shape shared by both GEMMs: a workgroup computes a 256 (M) x 256 (N)
+// output tile with four waves of 128 x 128.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kMaxGroups = 4;
+
+// One projection of a grouped GEMM: all groups share the activation.
+struct GemmGroup {
+  const uint8_t* w;  // E4M3 [n, k]
+  void* y;           // bf16 [m, ldy]
+  int32_t n;
+  int32_t ldy;
+  float alpha;       // output scale: s_in * s_w (W8A8) or s_w (W8A16)
+  int32_t tile_begin;  // first global tile index of this group
+  int32_t tiles_n;     // ceil(n / kTileN)
+  int32_t pad_;
+};
+
+struct GemmArgs {
+  const void* x;  // E4M3 [m, k] (W8A8) or bf16 [m, k] (W8A16)
+  int32_t m;
+  int32_t k;
+  int32_t tiles_m;
+  int32_t ngroups;
+  int32_t total_tiles;
+  int32_t pad_;
+  GemmGroup g[kMaxGroups];
+};
+
+// Fills tile_begin / tiles_n / tiles_m / total_tiles from m, n of each group.
+void gemm_plan(GemmArgs& a);
+
+hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipStream_t s);
+hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, int64_t n, float scale,
+                         hipStream_t s);
+
+}  // namespace fp8lin

@@ -1,0 +1,102 @@
+// Two-input SwiGLU: h = silu(gate) * up from two separate bf16 tensors,
+// emitted as E4M3 codes (scaled by the down projection's static input
+// scale) or as bf16 on 16-bit steps.
+//
+// [TRT-17476] "What changed": the split gated MLP feeds SiLU(G) * U from
+// two tensors straight into an FP8 output, avoiding the concatenated
+// [M, 2I] intermediate; the pages attribute its speed to DRAM utilization,
+// so this is one streaming pass: 4 bytes read and 1 (or 2) written per
+// element, 8 elements per lane-vector, consecutive lanes on consecutive
+// vectors.
+#include "device.h"
+#include "internal.h"
+
+namespace fp8lin {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 2;
+
+// silu(g) * u = g * u / (1 + exp(-g)) in float32. expf is the accurate
+// (about 1 ulp) libm exponential, so h stays within a few float32 ulp of
+// the exact value for every finite input; a very negative gate gives
+// exp(-g) = inf and h = -0 or 0, a large gate gives g * u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = expf(-g);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ uint32_t code_of(float h, float rs) {
+  const float t = h * rs;
+  if (__builtin_isnan(t)) return 0x7fu | ((__float_as_uint(t) >> 24) & 0x80u);
+  return e4m3_code(clamp448(t));
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  const __bf16 lo = (__bf16)a;
+  const __bf16 hi = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+template <bool kFp8Out>
+__global__ __launch_bounds__(kThreads) void swiglu_2in_kernel(const u32x4* __restrict__ g,
+                                                              const u32x4* __restrict__ u, void* __restrict__ out,
+                                                              int64_t nvec, float rs) {
+  const int64_t step = (int64_t)gridDim.x * (kThreads * kUnroll);
+  for (int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll); base < nvec; base += step) {
+    u32x4 gv[kUnroll], uv[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = base + k * kThreads + threadIdx.x;
+      if (i < nvec) {
+        gv[k] = __builtin_nontemporal_load(g + i);
+        uv[k] = __builtin_nontemporal_load(u + i);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = base + k * kThreads + threadIdx.x;
+      if (i >= nvec) continue;
+      float h[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[2 * e] = silu_mul(bf16_lo(gv[k][e]), bf16_lo(uv[k][e]));
+        h[2 * e + 1] = silu_mul(bf16_hi(gv[k][e]), bf16_hi(uv[k][e]));
+      }
+      if constexpr (kFp8Out) {
+        u32x2 o;
+        o.x = code_of(h[0], rs) | (code_of(h[1], rs) << 8) | (code_of(h[2], rs) << 16) | (code_of(h[3], rs) << 24);
+        o.y = code_of(h[4], rs) | (code_of(h[5], rs) << 8) | (code_of(h[6], rs) << 16) | (code_of(h[7], rs) << 24);
+        __builtin_nontemporal_store(o, static_cast<u32x2*>(out) + i);
+      } else {
+        u32x4 o;
+        o.x = bf16_pair(h[0], h[1]);
+        o.y = bf16_pair(h[2], h[3]);
+        o.z = bf16_pair(h[4], h[5]);
+        o.w = bf16_pair(h[6], h[7]);
+        __builtin_nontemporal_store(o, static_cast<u32x4*>(out) + i);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, int64_t n, float scale,
+                         hipStream_t s) {
+  const int64_t nvec = n / 8;
+  const int64_t per_block = kThreads * kUnroll;
+  int64_t blocks = (nvec + per_block - 1) / per_block;
+  if (blocks > 8192) blocks = 8192;
+  const float rs = fp8_out ? 1.0f / scale : 1.0f;
+  if (fp8_out) {
+    hipLaunchKernelGGL(swiglu_2in_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       static_cast<const u32x4*>(g), static_cast<const u32x4*>(u), out, nvec, rs);
+  } else {
+    hipLaunchKernelGGL(swiglu_2in_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       static_cast<const u32x4*>(g), static_cast<const u32x4*>(u), out, nvec, rs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin

@@ -38,6 +38,9 @@ __all__ = [
     "config3",
     "config4",
     "QKV_RATIOS",
+    "BlockCase",
+    "config5",
+    "config5_step_input",
 ]
 
 QKV_RATIOS = (1.0, 0.7, 0.45)
@@ -181,3 +184,78 @@ def config4(m=8192, hidden=4096, inter=16384, cal_rows=1024, device="cpu"):
         max_calibrated_scale(w_down),
         s_h,
     )
+
+
+@dataclass
+class BlockCase:
+    """Unquantized bf16 weights and calibrated static scales of one block."""
+
+    w_qkv: List[torch.Tensor]
+    w_out: torch.Tensor
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    s_qkv: List[float]
+    s_out: float
+    s_gate: float
+    s_up: float
+    s_down: float
+    s_in_qkv: float
+    s_in_out: float
+    s_in_mlp: float
+    s_h: float
+
+
+def config5(num_blocks=4, hidden=4096, inter=16384, cal_rows=256, device="cpu"):
+    """A stack of synthetic blocks for the denoising-schedule workload.
+
+    Block b: QKV (3 x hidden^2), output projection (hidden^2), gate/up
+    (inter x hidden each), down (hidden x inter), all ~ N(0, 0.02) with seeds
+    5000 + 10 b + i. The down weight is rescaled once so that a calibration
+    pass leaves the block output with standard deviation 0.35, like its
+    input. Input scales are max-calibrated on an unquantized float32 forward
+    of `cal_rows` fresh N(0, 0.35) rows (seed 700) -- the calibration
+    trajectory of a sampler without latent feedback; `device` only selects
+    where that float32 forward runs. Attention is the identity on V.
+    """
+    cal = normal_bf16((cal_rows, hidden), 0.35, 700).to(device).float()
+    blocks = []
+    for b in range(num_blocks):
+        seed = 5000 + 10 * b
+        w_qkv = [normal_bf16((hidden, hidden), 0.02, seed + i) for i in range(3)]
+        w_out = normal_bf16((hidden, hidden), 0.02, seed + 3)
+        w_gate = normal_bf16((inter, hidden), 0.02, seed + 4)
+        w_up = normal_bf16((inter, hidden), 0.02, seed + 5)
+        w_down = normal_bf16((hidden, inter), 0.02, seed + 6)
+        with torch.no_grad():
+            s_in_qkv = max_calibrated_scale(cal)
+            v = cal @ w_qkv[2].to(device).float().t()
+            s_in_out = max_calibrated_scale(v)
+            o = v @ w_out.to(device).float().t()
+            s_in_mlp = max_calibrated_scale(o)
+            g = o @ w_gate.to(device).float().t()
+            u = o @ w_up.to(device).float().t()
+            h = torch.nn.functional.silu(g) * u
+            s_h = max_calibrated_scale(h)
+            y = h @ w_down.to(device).float().t()
+            gain = 0.35 / float(y.std())
+            w_down = (w_down.float() * gain).to(torch.bfloat16)
+            cal = (h @ w_down.to(device).float().t())
+            del v, o, g, u, h, y
+        blocks.append(
+            BlockCase(
+                w_qkv, w_out, w_gate, w_up, w_down,
+                [max_calibrated_scale(w) for w in w_qkv],
+                max_calibrated_scale(w_out),
+                max_calibrated_scale(w_gate),
+                max_calibrated_scale(w_up),
+                max_calibrated_scale(w_down),
+                s_in_qkv, s_in_out, s_in_mlp, s_h,
+            )
+        )
+    return blocks
+
+
+def config5_step_input(step, branch, m=16384, hidden=4096):
+    """Fresh input of one CFG pass of one denoising step: N(0, 0.35), seed 600 + 2 step + branch."""
+    return normal_bf16((m, hidden), 0.35, 600 + 2 * step + branch)
