@@ -1,0 +1,355 @@
+"""Benchmark of the static per-tensor FP8 linear layer on one MI355X.
+
+One step = the shared-QKV projection group in W8A8 mode at its full size:
+x bf16 [16384, 4096] is quantized once to E4M3 with its static input scale
+(fp8lin_quantize_static), then three E4M3 4096 -> 4096 projections with
+distinct weight scales run on it (fp8lin_gemm_w8a8, one call each, HIP
+events around every GEMM). `value` is the GEMM work of the step,
+3 x 2 M N K, over the step's wall time (quantization included), in TFLOP/s.
+
+In the same run, on the same resident inputs:
+  * w8a16     the 16-bit step of the same projections (fp8lin_gemm_w8a16 x3)
+  * rows      every other hot-path call at its workload size: the grouped
+              fp8lin_qkv_shared in both modes, quantize and SwiGLU (GB/s,
+              input/output buffers rotated over > 512 MB so the 256 MB
+              last-level cache cannot serve repeats), the gated-MLP GEMMs,
+              the 1024- and 8192-row projections, and the step policy
+  * roofline  the W8A8 GEMM kernel against the dense FP8 matrix-core peak
+  * cpu_baseline  the CPU oracle on a bounded sample of the same step
+
+Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --pmc   (a few launches of each kernel and a plain
+                                copy, for rocprofv3 counter runs)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import w8a16_linear_layers_amd as fp8lin  # noqa: E402
+from workloads import config2, config3, normal_bf16  # noqa: E402
+
+METRIC = "W8A8 FP8 GEMM TFLOP/s (% FP8 MFMA peak) at M=16384,K=N=4096; W8A16 TFLOP/s"
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix-core peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+M, K, N = 16384, 4096, 4096
+GEMM_FLOP = 2.0 * M * N * K
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_16384x4096x4096_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "w8a16_linear_layers_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def timed(fn, reps, warmup=3):
+    """Average device time of fn() over `reps` calls (HIP events on the current stream), ms."""
+    for _ in range(warmup):
+        fn()
+    e0, e1 = events(2)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def rotating(make, total_bytes, per_set_bytes):
+    sets = max(2, int(np.ceil(total_bytes / per_set_bytes)))
+    return [make(i) for i in range(sets)]
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    with open(GEMM_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("gemm_source_sha256") != digest:
+        return None  # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, rows=2048, cols=1024):
+    """The oracle's W8A8 step on a bounded sample: `rows` rows x `cols` output columns per projection."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import linear
+
+    x = case.x[:rows].float().numpy()
+    qws = [linear.quantize_static(w[:cols].float().numpy(), s) for w, s in zip(case.ws, case.weight_scales)]
+    t0 = time.perf_counter()
+    q = linear.quantize_static(x, case.input_scale)
+    for qw, s in zip(qws, case.weight_scales):
+        linear.gemm_w8a8(q, qw, case.input_scale, s)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    flop = 3 * 2.0 * rows * cols * K
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d rows x first %d output columns of each of the 3 projections (activation quantization + "
+        "3 float64 W8A8 GEMMs), %.1f s" % (rows, cols, dt),
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def pmc_mode(dev):
+    """A few launches of each kernel plus a plain copy of known size, for counter runs."""
+    case = config3()
+    x = case.x.to(dev)
+    qws = [fp8lin.fp8lin_quantize_static(w.to(dev), s) for w, s in zip(case.ws, case.weight_scales)]
+    qx = fp8lin.fp8lin_quantize_static(x, case.input_scale)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    src = torch.ones(256 * 2**20, dtype=torch.uint8, device=dev)  # 256 MiB plain copy
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        fp8lin.fp8lin_quantize_static(x, case.input_scale, out=qx)
+        fp8lin.fp8lin_gemm_w8a8(qx, qws[0], case.input_scale, case.weight_scales[0], out=y)
+        fp8lin.fp8lin_gemm_w8a16(x, qws[0], case.weight_scales[0], out=y)
+    torch.cuda.synchronize()
+    log("pmc mode done: 3 x (copy 256 MiB, quantize, gemm_w8a8, gemm_w8a16)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--pmc", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(
+            "bench.py measures one MI355X: the static-FP8 linear layer has no cross-GPU exchange in this build "
+            "(--gpus %d, WORLD_SIZE %d requested). Run with --gpus 1." % (args.gpus, world),
+            file=sys.stderr,
+        )
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    fp8lin.load_library()
+    dev = torch.device("cuda", 0)
+    if args.pmc:
+        pmc_mode(dev)
+        return
+
+    log("generating the shared-QKV workload (x [16384, 4096], three 4096x4096 weights)")
+    case = config3()
+    x = case.x.to(dev)
+    s_in = case.input_scale
+    qws = [fp8lin.fp8lin_quantize_static(w.to(dev), s) for w, s in zip(case.ws, case.weight_scales)]
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    stream = torch.cuda.current_stream()
+
+    def step_w8a8(ev=None):
+        fp8lin.fp8lin_quantize_static(x, s_in, out=qx)
+        for i in range(3):
+            if ev is not None:
+                ev[2 * i].record(stream)
+            fp8lin.fp8lin_gemm_w8a8(qx, qws[i], s_in, case.weight_scales[i], out=ys[i])
+            if ev is not None:
+                ev[2 * i + 1].record(stream)
+
+    def step_w8a16():
+        for i in range(3):
+            fp8lin.fp8lin_gemm_w8a16(x, qws[i], case.weight_scales[i], out=ys[i])
+
+    for _ in range(args.warmup):
+        step_w8a8()
+    torch.cuda.synchronize()
+    log("timing %d W8A8 steps" % args.steps)
+    gemm_ev = [events(6) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step_w8a8(gemm_ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gemm_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for ev in gemm_ev for i in range(3)]
+    gemm_avg_ms = float(np.mean(gemm_ms))
+    value = 3 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
+
+    for _ in range(args.warmup):
+        step_w8a16()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_w8a16()
+    torch.cuda.synchronize()
+    ms16 = (time.perf_counter() - t0) * 1e3 / args.steps
+    tf16 = 3 * GEMM_FLOP / (ms16 * 1e-3) / 1e12
+
+    achieved = GEMM_FLOP / (gemm_avg_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "shared-QKV W8A8 projection group: x bf16 [16384,4096] quantized once to E4M3, then three "
+            "E4M3 4096->4096 GEMMs with weight-scale ratios 1:0.7:0.45, bf16 outputs",
+            "M": M,
+            "K": K,
+            "N": N,
+            "projections": 3,
+        },
+        "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "w8a16": {
+            "value": round(tf16, 2),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(ms16, 4),
+            "pct_bf16_peak": round(100 * tf16 / PEAK_BF16_TFLOPS, 2),
+            "dtype": "bf16 activations x E4M3 weights (exact bf16 dequant), fp32 accumulate",
+        },
+        "roofline": {
+            "kernel": "gemm_w8a8 (v_mfma_f32_32x32x64_f8f6f4), M=16384 N=4096 K=4096",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "avg_launch_ms": round(gemm_avg_ms, 5),
+            "traffic": gemm_traffic(),
+        },
+    }
+
+    if not args.no_rows:
+        out["rows"] = other_rows(dev, case, x, qws, qx, ys)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+
+
+def other_rows(dev, case, x, qws, qx, ys):
+    rows = {}
+    s_in, sw = case.input_scale, case.weight_scales
+    reps = 20
+
+    # grouped shared-QKV call, both modes (one quantize + one grouped GEMM launch / one grouped W8A16 launch)
+    t8 = timed(lambda: fp8lin.fp8lin_qkv_shared(x, qws, sw, [s_in] * 3, fp8lin.MODE_W8A8, outs=ys, workspace=qx), reps)
+    t16 = timed(lambda: fp8lin.fp8lin_qkv_shared(x, qws, sw, [s_in] * 3, fp8lin.MODE_W8A16, outs=ys), reps)
+    rows["qkv_shared_w8a8"] = {"ms": round(t8, 4), "tflops": round(3 * GEMM_FLOP / t8 / 1e9, 2)}
+    rows["qkv_shared_w8a16"] = {"ms": round(t16, 4), "tflops": round(3 * GEMM_FLOP / t16 / 1e9, 2)}
+
+    # quantize at [16384, 4096]: 2 bytes in + 1 byte out per element, buffers rotated over > 512 MB
+    n = M * K
+    xs = rotating(lambda i: normal_bf16((M, K), 0.35, 900 + i).to(dev), 600e6, 3 * n)
+    qs = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in xs]
+    it = [0]
+
+    def q_once():
+        i = it[0] % len(xs)
+        it[0] += 1
+        fp8lin.fp8lin_quantize_static(xs[i], s_in, out=qs[i])
+
+    tq = timed(q_once, 30)
+    rows["quantize_16384x4096"] = {"ms": round(tq, 4), "gbps": round(3 * n / tq / 1e6, 1),
+                                   "pct_hbm_peak": round(100 * 3 * n / tq / 1e6 / PEAK_HBM_GBPS, 2),
+                                   "rotated_sets": len(xs)}
+    del xs, qs
+
+    # SwiGLU at [8192, 16384]: 4 bytes in + 1 (E4M3) or 2 (bf16) bytes out per element
+    mi, inter = 8192, 16384
+    n2 = mi * inter
+    gs = [(normal_bf16((mi, inter), 0.45, 910 + 2 * i).to(dev), normal_bf16((mi, inter), 0.45, 911 + 2 * i).to(dev))
+          for i in range(2)]
+    o8 = [torch.empty((mi, inter), dtype=torch.uint8, device=dev) for _ in gs]
+    o16 = torch.empty((mi, inter), dtype=torch.bfloat16, device=dev)
+    it[0] = 0
+
+    def sw8():
+        i = it[0] % len(gs)
+        it[0] += 1
+        fp8lin.fp8lin_swiglu_2in_quant(gs[i][0], gs[i][1], 2.1 / 448, fp8lin.DT_E4M3, out=o8[i])
+
+    def sw16():
+        i = it[0] % len(gs)
+        it[0] += 1
+        fp8lin.fp8lin_swiglu_2in_quant(gs[i][0], gs[i][1], 1.0, fp8lin.DT_BF16, out=o16)
+
+    ts8 = timed(sw8, 20)
+    ts16 = timed(sw16, 20)
+    rows["swiglu_fp8_8192x16384"] = {"ms": round(ts8, 4), "gbps": round(5 * n2 / ts8 / 1e6, 1),
+                                     "pct_hbm_peak": round(100 * 5 * n2 / ts8 / 1e6 / PEAK_HBM_GBPS, 2)}
+    rows["swiglu_bf16_8192x16384"] = {"ms": round(ts16, 4), "gbps": round(6 * n2 / ts16 / 1e6, 1),
+                                      "pct_hbm_peak": round(100 * 6 * n2 / ts16 / 1e6 / PEAK_HBM_GBPS, 2)}
+
+    # gated-MLP GEMMs (gate/up 4096 -> 16384 on 8192 rows; down 16384 -> 4096) in both modes
+    g_in = gs[0][0][:, :K].contiguous()  # any [8192, 4096] bf16 activation
+    w_gu = torch.randint(0, 0x7E, (inter, K), dtype=torch.uint8, device=dev)
+    w_dn = torch.randint(0, 0x7E, (K, inter), dtype=torch.uint8, device=dev)
+    q_gu = fp8lin.fp8lin_quantize_static(g_in, 0.01)
+    y_gu = torch.empty((mi, inter), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((mi, K), dtype=torch.bfloat16, device=dev)
+    f_gu = 2.0 * mi * inter * K
+    tg8 = timed(lambda: fp8lin.fp8lin_gemm_w8a8(q_gu, w_gu, 0.01, 1e-4, out=y_gu), reps)
+    tg16 = timed(lambda: fp8lin.fp8lin_gemm_w8a16(g_in, w_gu, 1e-4, out=y_gu), reps)
+    td8 = timed(lambda: fp8lin.fp8lin_gemm_w8a8(o8[0], w_dn, 0.01, 1e-4, out=y_dn), reps)
+    td16 = timed(lambda: fp8lin.fp8lin_gemm_w8a16(o16, w_dn, 1e-4, out=y_dn), reps)
+    rows["gate_or_up_8192x16384x4096"] = {"w8a8_tflops": round(f_gu / tg8 / 1e9, 1), "w8a16_tflops": round(f_gu / tg16 / 1e9, 1)}
+    rows["down_8192x4096x16384"] = {"w8a8_tflops": round(f_gu / td8 / 1e9, 1), "w8a16_tflops": round(f_gu / td16 / 1e9, 1)}
+    del gs, o8, o16, y_gu, y_dn
+
+    # 4096 -> 4096 projection at 1024 and 8192 rows
+    c2 = config2()
+    x2 = c2.x.to(dev)
+    qw2 = fp8lin.fp8lin_quantize_static(c2.w.to(dev), c2.weight_scale)
+    q2 = fp8lin.fp8lin_quantize_static(x2, c2.input_scale)
+    for m in (1024, 8192):
+        y2 = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        f = 2.0 * m * N * K
+        a = timed(lambda: fp8lin.fp8lin_gemm_w8a8(q2[:m], qw2, c2.input_scale, c2.weight_scale, out=y2), reps)
+        b = timed(lambda: fp8lin.fp8lin_gemm_w8a16(x2[:m], qw2, c2.weight_scale, out=y2), reps)
+        rows["proj_%dx4096x4096" % m] = {"w8a8_tflops": round(f / a / 1e9, 1), "w8a16_tflops": round(f / b / 1e9, 1)}
+
+    # step policy: host call per transformer forward
+    pol = fp8lin.policy_from_json({"schema_version": 1, "type": "first_last_steps", "index_space": "scheduler_step",
+                                   "default_mode": "w8a8", "overlap": "a16", "first_steps": 3, "last_steps": 3,
+                                   "reasoner": "a16"})
+    trace = [fp8lin.fp8lin_step_policy(pol, 0, i, 8) for i in range(8)]
+    t0 = time.perf_counter()
+    for i in range(10000):
+        fp8lin.fp8lin_step_policy(pol, 0, i % 8, 8)
+    rows["step_policy"] = {"us_per_call_incl_python": round((time.perf_counter() - t0) * 100, 3),
+                           "trace_8": "".join("8" if t == fp8lin.MODE_W8A8 else "6" for t in trace)}
+    return rows
+
+
+if __name__ == "__main__":
+    main()

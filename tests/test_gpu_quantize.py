@@ -27,6 +27,11 @@ SCALES = [
     0.02 / 448,
     2.0**-120,
     2.0**100,
+    2.0**-8,  # the calibrated input scale of the shared-QKV workload (amax 1.75)
+    3 * 2.0**-10,  # a non-power-of-two scale with many exactly representable quotients
+    5 * 2.0**-100,
+    2.0**-92,  # boundaries of the exact-residual shortcut
+    1.5 * 2.0**-93,
 ]
 
 

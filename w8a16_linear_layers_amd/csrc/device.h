@@ -56,17 +56,35 @@ __device__ __forceinline__ uint32_t pick_codes(uint32_t p0, uint32_t p1) {
   return (p0 & 0xffu) | ((p0 >> 8) & 0xff00u) | ((p1 & 0xffu) << 16) | ((p1 << 8) & 0xff000000u);
 }
 
-// Exact static quantization of one bf16 value (bits in the low 16 bits):
-// the IEEE correctly rounded float32 quotient, then saturate and round.
-__device__ __forceinline__ uint32_t quant_one_exact(uint32_t bits, float s) {
+// Static quantization of two bf16 values for a power-of-two scale s = 2^k:
+// r = 2^-k exactly, so q = x * r IS the exact quotient (or is below 2^-126,
+// where every candidate code is a signed zero, or overflows, where the
+// quotient saturates either way) and needs no bracket. Only a NaN input
+// sets `doubt`.
+__device__ __forceinline__ uint32_t quant_pair_pow2(uint32_t w, float r, uint32_t& doubt) {
+  uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_lo(w) * r), 0.0f, 0, false);
+  p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_hi(w) * r), 0.0f, (int)p, true);
+  doubt |= ((w & 0x7fff7fffu) + 0x007f007fu) & 0x80008000u;
+  return p;  // codes in bytes 0 and 2, like quant_pair_fast
+}
+
+// Exact static quantization of one bf16 value (bits in the low 16 bits).
+// If q = x * (1/s) satisfies q * s == x exactly (FMA residual zero), q is
+// the exact quotient and its code is final. That test is sound when the
+// residual cannot underflow to zero, i.e. for s >= 2^-92 (`exact_ok`): a
+// nonzero residual of a code-relevant quotient (|q| >= 2^-11) is then at
+// least 2^-149. Otherwise the IEEE correctly rounded float32 division.
+__device__ __forceinline__ uint32_t quant_one_exact(uint32_t bits, float s, float r, bool exact_ok) {
   const float x = __uint_as_float(bits << 16);
   if (__builtin_isnan(x)) return 0x7fu | ((bits >> 8) & 0x80u);
+  const float q0 = x * r;
+  if (exact_ok && __builtin_fmaf(-q0, s, x) == 0.0f) return e4m3_code(clamp448(q0));
   const float q = x / s;  // correctly rounded division (hipcc default)
   return e4m3_code(clamp448(q));
 }
 
-__device__ __forceinline__ uint32_t quant_word_exact(uint32_t w, float s) {
-  return quant_one_exact(w & 0xffffu, s) | (quant_one_exact(w >> 16, s) << 8);
+__device__ __forceinline__ uint32_t quant_word_exact(uint32_t w, float s, float r, bool exact_ok) {
+  return quant_one_exact(w & 0xffffu, s, r, exact_ok) | (quant_one_exact(w >> 16, s, r, exact_ok) << 8);
 }
 
 }  // namespace fp8lin

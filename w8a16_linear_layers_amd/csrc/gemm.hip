@@ -62,15 +62,40 @@ constexpr int kXcds = 8;
 constexpr int kBandM = 8;        // M-tiles per raster band
 
 
-__shared__ __attribute__((aligned(16))) uint8_t lds_w8[kStages8][kTileN * kBK];   // E4M3 weight tiles
-__shared__ __attribute__((aligned(16))) uint8_t lds_x8[kStages8][kTileM * kBK];   // E4M3 activation tiles
-__shared__ __attribute__((aligned(16))) uint8_t lds_w16[kStages16][kTileN * kBK];      // E4M3 weight tiles
-__shared__ __attribute__((aligned(16))) uint8_t lds_x16[kStages16][kTileM * kBK * 2];  // bf16 activation tiles
+// One LDS arena per workgroup. W8A8: E4M3 weight stages, then E4M3
+// activation stages (16 KiB each). W8A16: E4M3 weight stages (16 KiB), then
+// bf16 activation stages (32 KiB). After the K loop the epilogue reuses the
+// first 128 KiB as four 32 KiB per-wave output tiles.
+constexpr int kStageE4M3 = kTileN * kBK;     // 16 KiB
+constexpr int kStageBf16 = kTileM * kBK * 2;  // 32 KiB
+constexpr int kLdsW8A8 = 2 * kStages8 * kStageE4M3;
+constexpr int kLdsW8A16 = kStages16 * (kStageE4M3 + kStageBf16);
+constexpr int kLdsBytes = kLdsW8A8 > kLdsW8A16 ? kLdsW8A8 : kLdsW8A16;
+static_assert(kLdsBytes >= 4 * 128 * 256, "epilogue staging needs 128 KiB");
+static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS per workgroup");
+__shared__ __attribute__((aligned(16))) uint8_t lds_mem[kLdsBytes];
 
-// Permutation of the four 16-byte chunks of a 64-byte row, and of the eight
-// chunks of a 128-byte row (XOR with a per-row constant: a bijection).
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ uint8_t* lds_w8(int s) { return lds_mem + s * kStageE4M3; }
+__device__ __forceinline__ uint8_t* lds_x8(int s) { return lds_mem + (kStages8 + s) * kStageE4M3; }
+__device__ __forceinline__ uint8_t* lds_w16(int s) { return lds_mem + s * kStageE4M3; }
+__device__ __forceinline__ uint8_t* lds_x16(int s) { return lds_mem + kStages16 * kStageE4M3 + s * kStageBf16; }
+
+// LDS tile layouts. A ds_read_b128 wave is served 16 lanes per cycle; the
+// layouts below keep every MFMA fragment read free of bank conflicts for
+// the lane groupings a 64-bank LDS may use (16 consecutive lanes, lanes
+// {8k..8k+7} with {8k+32..8k+39}, or lanes sharing lane-index bits 1 and
+// 4 -- the grouping the LDS bank-conflict counters of the first layout
+// pointed to), for every read pattern of both kernels.
+//   E4M3 tiles, 64-byte rows: logical row r sits in physical row
+//     row64(r) = r ^ (bit3(r) << 1)   (a swap inside groups of 4 rows)
+//   and its 16-byte chunk c in physical chunk c ^ swz4(r).
+//   bf16 tiles, 128-byte rows: chunk c of row r in physical chunk c ^ swz8(r).
+// All three are involutions / XORs, hence bijections on the tile.
+__device__ __forceinline__ int row64(int r) { return r ^ (((r >> 3) & 1) << 1); }
+__device__ __forceinline__ int swz4(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
+__device__ __forceinline__ int swz8(int r) {
+  return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -141,8 +166,9 @@ __device__ __forceinline__ TileCoord tile_of(const GemmArgs& a) {
 }
 
 // Per-thread copy plan of one operand tile. The tile holds 256 rows of 64
-// K-elements; chunk position p (16 bytes) = j * 256 + tid holds logical
-// chunk (p % cpr) ^ swizzle(row) of row p / cpr (cpr = chunks per row).
+// K-elements; chunk position p (16 bytes) = j * 256 + tid of physical row
+// P = p / cpr (cpr = chunks per row) holds logical chunk (p % cpr) ^ swz(r)
+// of logical row r = row64(P) (E4M3) or P (bf16).
 // voff[j] is the byte offset of that chunk inside the tile's resource at
 // K = 0; the stage's K offset travels in the scalar offset.
 template <int kChunks>  // 4: E4M3 rows of 64 B; 8: bf16 rows of 128 B
@@ -158,11 +184,18 @@ struct CopyPlan {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int p = j * kThreads + tid;
-      const int r = p / kChunks;
+      const int r = kChunks == 4 ? row64(p / kChunks) : p / kChunks;  // logical row stored there
       const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : swz8(r));
       voff[j] = (uint32_t)(r * ld_bytes) + (uint32_t)c * 16u;
       kchunk[j] = c * (kChunks == 4 ? 16 : 8);
     }
+  }
+
+  // Copy chunk j of stage `kt` (no K tail: the stage lies inside [0, k)).
+  __device__ __forceinline__ void copy_one(const uint8_t* lds_tile, int kt, int j, int tid) const {
+    const uint32_t soff = (uint32_t)(kt * kBK) * (kChunks == 4 ? 1u : 2u);
+    dma16(rsrc, voff[j], soff,
+          __builtin_amdgcn_readfirstlane(lds_addr(lds_tile) + (j * kThreads + (tid >> 6) * 64) * 16));
   }
 
   // Copy stage `kt` into the LDS tile; chunks at K >= k read as zero.
@@ -187,61 +220,80 @@ __device__ __forceinline__ u32x4 lds_chunk(const uint8_t* tile, int byte_offset)
 // 32 x 64 E4M3 fragment of rows [row, row+32): lane (r, g) holds logical
 // chunks 2g and 2g+1 (32 bytes of K) of row + r.
 __device__ __forceinline__ v8i frag_e4m3(const uint8_t* tile, int row, int g) {
-  const int s = swz4(row);
-  const u32x4 a = lds_chunk(tile, row * 64 + ((2 * g) ^ s) * 16);
-  const u32x4 b = lds_chunk(tile, row * 64 + ((2 * g + 1) ^ s) * 16);
+  const int s = swz4(row), base = row64(row) * 64;
+  const u32x4 a = lds_chunk(tile, base + ((2 * g) ^ s) * 16);
+  const u32x4 b = lds_chunk(tile, base + ((2 * g + 1) ^ s) * 16);
   v8i v;
   v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
   v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
   return v;
 }
 
-// Store four consecutive bf16 outputs (n .. n+3 of row m).
-__device__ __forceinline__ void store_quad(void* y, int64_t ldy, int m, int n, float a, float b, float c, float d) {
-  const __bf16 h0 = (__bf16)a, h1 = (__bf16)b, h2 = (__bf16)c, h3 = (__bf16)d;
-  u32x2 v;
-  v[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-  v[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + (int64_t)m * ldy + n) = v;
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  const __bf16 lo = (__bf16)a, hi = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-// acc[i][j] holds D[n][m] of the 32 x 32 block (n-block i, m-block j):
-// lane l, register v -> m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4.
+// Epilogue: scale by alpha, round to bf16 and write the wave's 128 x 128
+// output. acc[i][j] holds D[n][m] of the 32 x 32 block (n-block i, m-block
+// j): lane l, register v -> m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4,
+// i.e. four consecutive n of one row per register quad. Written straight to
+// memory that would scatter every store over 32 rows, so the tile goes
+// through LDS first: the wave's 32 KiB staging area holds row m (0..127) as
+// 16 chunks of 16 bytes, chunk c at physical chunk c ^ (m % 16). Read back
+// row by row, 16 lanes cover a row's 256 contiguous bytes and every global
+// store is a full 16-byte-per-lane, row-contiguous write.
 __device__ __forceinline__ void epilogue(const v16f (&acc)[4][4], const GemmGroup& grp, int M, int m_base, int n_base,
-                                         int lane) {
+                                         int lane, int wave) {
+  __syncthreads();  // every wave is done with the pipeline buffers
+  uint8_t* stage = lds_mem + wave * (128 * 256);
   const float alpha = grp.alpha;
+  const int h = lane >> 5;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = m_base + j * 32 + (lane & 31);
-    if (m >= M) continue;
+    const int m = j * 32 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int n = n_base + i * 32 + 8 * t + 4 * (lane >> 5);
-        if (n < grp.n)
-          store_quad(grp.y, grp.ldy, m, n, acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha,
-                     acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
+        const int c = i * 4 + t;  // 16-byte chunk of n = 32 i + 8 t + 4 h
+        u32x2 v;
+        v[0] = bf16x2(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
+        v[1] = bf16x2(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
+        *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
       }
     }
   }
+  const int c = lane & 15;
+  const int n = n_base + c * 8;
+  const bool n_ok = n < grp.n;
+#pragma unroll 8
+  for (int q = 0; q < 32; ++q) {
+    const int ml = q * 4 + (lane >> 4);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) * 16));
+    const int m = m_base + ml;
+    if (n_ok && m < M) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(grp.y) + (int64_t)m * grp.ldy + n) = v;
+  }
 }
 
-// Wait until stage `kt + 1` has landed in LDS, given that the loads of at
-// most one later stage may still be in flight (8 DMA loads per thread per
-// stage), then synchronize the workgroup.
-__device__ __forceinline__ void w8a8_wait_next(int kt, int KT) {
-  if (kt + 2 < KT)
-    wait_vmem_and_barrier<8>();
-  else
-    wait_vmem_and_barrier<0>();
+// Wait until every DMA load except those of the last `later` stages issued
+// has landed (`per_stage` loads per thread per stage), then synchronize the
+// workgroup. vmcnt needs an immediate, hence the switch.
+template <int kPerStage>
+__device__ __forceinline__ void wait_stages(int later) {
+  switch (later) {
+    case 0: wait_vmem_and_barrier<0>(); break;
+    case 1: wait_vmem_and_barrier<kPerStage>(); break;
+    case 2: wait_vmem_and_barrier<2 * kPerStage>(); break;
+    default: wait_vmem_and_barrier<3 * kPerStage>(); break;
+  }
 }
 
 __device__ __forceinline__ void w8a8_frags(int buf, int row_w, int row_x, int g, v8i (&wf)[4], v8i (&xf)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wf[i] = frag_e4m3(lds_w8[buf], row_w + i * 32, g);
+  for (int i = 0; i < 4; ++i) wf[i] = frag_e4m3(lds_w8(buf), row_w + i * 32, g);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) xf[j] = frag_e4m3(lds_x8[buf], row_x + j * 32, g);
+  for (int j = 0; j < 4; ++j) xf[j] = frag_e4m3(lds_x8(buf), row_x + j * 32, g);
 }
 
 __device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], const v8i (&xf)[4]) {
@@ -252,10 +304,60 @@ __device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], 
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], xf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
 }
 
-// Pipeline: stage s is copied into LDS buffer s % 4 three stages ahead; the
-// MFMA fragments of stage kt + 1 are read from LDS while the matrix cores
-// work on stage kt. The buffer refilled in iteration kt held stage kt - 1,
-// whose fragments were read in iteration kt - 2, before the barrier.
+// One steady-state half step: the 16 MFMAs of the stage whose fragments are
+// in (wc, xc), interleaved one by one with the 8 LDS copies of stage
+// `copy_kt` (into buffer `copy_buf`) and the 16 fragment reads of the next
+// stage (from buffer `read_buf` into (wn, xn)), read in the order the next
+// half consumes them (W0, X0..X3, W1..W3), so each read has at least seven
+// MFMAs of cover before its first use. sched_barrier keeps the compiler from
+// regrouping the slots, so copies and reads issue in the shadow of the
+// matrix-core work instead of in a burst before it.
+__device__ __forceinline__ void w8a8_half(v16f (&acc)[4][4], const v8i (&wc)[4], const v8i (&xc)[4], v8i (&wn)[4],
+                                          v8i (&xn)[4], const CopyPlan<4>& pw, const CopyPlan<4>& px, int copy_kt,
+                                          int copy_buf, int read_buf, int row_w, int row_x, int g, int tid) {
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int i = t >> 2, j = t & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wc[i], xc[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    if (t < 4)
+      pw.copy_one(lds_w8(copy_buf), copy_kt, t, tid);
+    else if (t < 8)
+      px.copy_one(lds_x8(copy_buf), copy_kt, t - 4, tid);
+    else if (t == 8)
+      wn[0] = frag_e4m3(lds_w8(read_buf), row_w, g);
+    else if (t < 13)
+      xn[t - 9] = frag_e4m3(lds_x8(read_buf), row_x + (t - 9) * 32, g);
+    else
+      wn[t - 12] = frag_e4m3(lds_w8(read_buf), row_w + (t - 12) * 32, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Guarded step for the first and last stages: stage kt + 1 must have
+// landed before its fragments are read; stage kt + S - 1 is copied if it
+// exists (with the K-tail masking).
+__device__ __forceinline__ void w8a8_edge_step(v16f (&acc)[4][4], const v8i (&wc)[4], const v8i (&xc)[4],
+                                               v8i (&wn)[4], v8i (&xn)[4], const CopyPlan<4>& pw,
+                                               const CopyPlan<4>& px, int kt, int KT, int K, int row_w, int row_x,
+                                               int g, int tid) {
+  if (kt + 1 < KT) {
+    // stages issued after kt + 1: up to kt + S - 2
+    wait_stages<8>(min(kt + kStages8 - 2, KT - 1) - (kt + 1));
+    const int c = kt + kStages8 - 1;
+    if (c < KT) {
+      pw.copy(lds_w8(c % kStages8), c, K, tid);
+      px.copy(lds_x8(c % kStages8), c, K, tid);
+    }
+    w8a8_frags((kt + 1) % kStages8, row_w, row_x, g, wn, xn);
+  }
+  w8a8_mma(acc, wc, xc);
+}
+
+// Pipeline over kStages8 LDS buffers: stage s is copied into buffer
+// s % kStages8 kStages8 - 1 stages ahead; the MFMA fragments of stage
+// s + 1 are read from LDS while the matrix cores work on stage s. The buffer
+// refilled while stage s computes held stage s - 1, whose fragments were
+// read during stage s - 2, before the barrier that opens stage s.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a8_kernel(const GemmArgs a) {
   const TileCoord tc = tile_of(a);
@@ -277,8 +379,8 @@ gemm_w8a8_kernel(const GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < kStages8 - 1; ++s) {
     if (s < KT) {
-      pw.copy(lds_w8[s], s, K, tid);
-      px.copy(lds_x8[s], s, K, tid);
+      pw.copy(lds_w8(s), s, K, tid);
+      px.copy(lds_x8(s), s, K, tid);
     }
   }
 
@@ -286,58 +388,32 @@ gemm_w8a8_kernel(const GemmArgs a) {
   const int row_x = wm * 128 + (lane & 31);
   const int g = lane >> 5;
 
-  // stage 0: at most two later stages in flight
-  if (KT >= 3)
-    wait_vmem_and_barrier<16>();
-  else if (KT == 2)
-    wait_vmem_and_barrier<8>();
-  else
-    wait_vmem_and_barrier<0>();
+  wait_stages<8>(min(kStages8 - 2, KT - 1));  // stage 0 landed
   v8i wa[4], xa[4], wb[4], xb[4];
   w8a8_frags(0, row_w, row_x, g, wa, xa);
 
   // Stages in pairs: the even one's fragments sit in (wa, xa), the odd
-  // one's in (wb, xb). The steady-state loop has no branches besides its
-  // back edge (every prefetch it issues exists), so the compiler tracks the
-  // LDS-read counters exactly; the last stages drain in a guarded loop. Both
-  // loops have a single exit, so the accumulators stay in place; an odd last
-  // stage is already in (wa, xa) when they end.
+  // one's in (wb, xb). The steady-state loop runs while every copy it
+  // issues is a full stage (stage kt + S <= KT - 2), so it has no branches
+  // besides its back edge and the compiler tracks the LDS-read counters
+  // exactly; the remaining stages take guarded steps. Both loops have a
+  // single exit, so the accumulators stay in place; an odd last stage is
+  // already in (wa, xa) when they end.
   int kt = 0;
-  for (; kt + 5 < KT; kt += 2) {
-    wait_vmem_and_barrier<8>();
-    pw.copy(lds_w8[(kt + 3) % kStages8], kt + 3, K, tid);
-    px.copy(lds_x8[(kt + 3) % kStages8], kt + 3, K, tid);
-    w8a8_frags((kt + 1) % kStages8, row_w, row_x, g, wb, xb);
-    w8a8_mma(acc, wa, xa);
-    wait_vmem_and_barrier<8>();
-    pw.copy(lds_w8[kt % kStages8], kt + 4, K, tid);
-    px.copy(lds_x8[kt % kStages8], kt + 4, K, tid);
-    w8a8_frags((kt + 2) % kStages8, row_w, row_x, g, wa, xa);
-    w8a8_mma(acc, wb, xb);
+  for (; kt + kStages8 + 2 <= KT; kt += 2) {
+    wait_vmem_and_barrier<8 * (kStages8 - 3)>();
+    w8a8_half(acc, wa, xa, wb, xb, pw, px, kt + kStages8 - 1, (kt + kStages8 - 1) % kStages8, (kt + 1) % kStages8,
+              row_w, row_x, g, tid);
+    wait_vmem_and_barrier<8 * (kStages8 - 3)>();
+    w8a8_half(acc, wb, xb, wa, xa, pw, px, kt + kStages8, kt % kStages8, (kt + 2) % kStages8, row_w, row_x, g, tid);
   }
   for (; kt + 1 < KT; kt += 2) {
-    w8a8_wait_next(kt, KT);
-    if (kt + 3 < KT) {
-      const int sb = (kt + 3) % kStages8;
-      pw.copy(lds_w8[sb], kt + 3, K, tid);
-      px.copy(lds_x8[sb], kt + 3, K, tid);
-    }
-    w8a8_frags((kt + 1) % kStages8, row_w, row_x, g, wb, xb);
-    w8a8_mma(acc, wa, xa);
-    if (kt + 2 < KT) {
-      w8a8_wait_next(kt + 1, KT);
-      if (kt + 4 < KT) {
-        const int sb = (kt + 4) % kStages8;
-        pw.copy(lds_w8[sb], kt + 4, K, tid);
-        px.copy(lds_x8[sb], kt + 4, K, tid);
-      }
-      w8a8_frags((kt + 2) % kStages8, row_w, row_x, g, wa, xa);
-    }
-    w8a8_mma(acc, wb, xb);
+    w8a8_edge_step(acc, wa, xa, wb, xb, pw, px, kt, KT, K, row_w, row_x, g, tid);
+    w8a8_edge_step(acc, wb, xb, wa, xa, pw, px, kt + 1, KT, K, row_w, row_x, g, tid);
   }
   if (kt < KT) w8a8_mma(acc, wa, xa);
 
-  epilogue(acc, grp, a.m, tc.m0 + wm * 128, tc.n0 + wn * 128, lane);
+  epilogue(acc, grp, a.m, tc.m0 + wm * 128, tc.n0 + wn * 128, lane, wave);
 }
 
 // Eight exact E4M3 -> bf16 conversions of one dword pair.
@@ -376,8 +452,8 @@ gemm_w8a16_kernel(const GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < kStages16 - 1; ++s) {
     if (s < KT) {
-      pw.copy(lds_w16[s], s, K, tid);
-      px.copy(lds_x16[s], s, K, tid);
+      pw.copy(lds_w16(s), s, K, tid);
+      px.copy(lds_x16(s), s, K, tid);
     }
   }
 
@@ -395,8 +471,8 @@ gemm_w8a16_kernel(const GemmArgs a) {
     const int next = kt + kStages16 - 1;
     if (next < KT) {
       const int sb = next % kStages16;
-      pw.copy(lds_w16[sb], next, K, tid);
-      px.copy(lds_x16[sb], next, K, tid);
+      pw.copy(lds_w16(sb), next, K, tid);
+      px.copy(lds_x16(sb), next, K, tid);
     }
 
     const int cb = kt % kStages16;
@@ -410,15 +486,15 @@ gemm_w8a16_kernel(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = row_w + i * 32;
-        const u32x4 c = lds_chunk(lds_w16[cb], r * 64 + ((2 * h + g) ^ swz4(r)) * 16);
+        const u32x4 c = lds_chunk(lds_w16(cb), row64(r) * 64 + ((2 * h + g) ^ swz4(r)) * 16);
         wf[i][0] = dequant8(c[0], c[1]);
         wf[i][1] = dequant8(c[2], c[3]);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = row_x + j * 32;
-        xf[j][0] = as_v8bf(lds_chunk(lds_x16[cb], r * 128 + ((4 * h + 2 * g) ^ swz8(r)) * 16));
-        xf[j][1] = as_v8bf(lds_chunk(lds_x16[cb], r * 128 + ((4 * h + 2 * g + 1) ^ swz8(r)) * 16));
+        xf[j][0] = as_v8bf(lds_chunk(lds_x16(cb), r * 128 + ((4 * h + 2 * g) ^ swz8(r)) * 16));
+        xf[j][1] = as_v8bf(lds_chunk(lds_x16(cb), r * 128 + ((4 * h + 2 * g + 1) ^ swz8(r)) * 16));
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e)
@@ -430,7 +506,7 @@ gemm_w8a16_kernel(const GemmArgs a) {
     }
   }
 
-  epilogue(acc, grp, a.m, tc.m0 + wm * 128, tc.n0 + wn * 128, lane);
+  epilogue(acc, grp, a.m, tc.m0 + wm * 128, tc.n0 + wn * 128, lane, wave);
 }
 
 }  // namespace

@@ -9,6 +9,8 @@
 // (16 bytes of bf16 in, 8 bytes of codes out). Consecutive lanes take
 // consecutive vectors, so every load and store instruction of a wave covers
 // one contiguous 1 KiB / 512 B span.
+#include <cmath>
+
 #include "device.h"
 #include "internal.h"
 
@@ -18,37 +20,51 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;  // vectors in flight per thread
 
+template <bool kPow2>
+__device__ __forceinline__ u32x2 quantize8(const u32x4 v, float s, float r, bool exact_ok) {
+  uint32_t doubt = 0;
+  uint32_t p0, p1, p2, p3;
+  if constexpr (kPow2) {
+    p0 = quant_pair_pow2(v.x, r, doubt);
+    p1 = quant_pair_pow2(v.y, r, doubt);
+    p2 = quant_pair_pow2(v.z, r, doubt);
+    p3 = quant_pair_pow2(v.w, r, doubt);
+  } else {
+    p0 = quant_pair_fast(v.x, r, doubt);
+    p1 = quant_pair_fast(v.y, r, doubt);
+    p2 = quant_pair_fast(v.z, r, doubt);
+    p3 = quant_pair_fast(v.w, r, doubt);
+  }
+  u32x2 out;
+  out.x = pick_codes(p0, p1);
+  out.y = pick_codes(p2, p3);
+  if (doubt) {
+    out.x = quant_word_exact(v.x, s, r, exact_ok) | (quant_word_exact(v.y, s, r, exact_ok) << 16);
+    out.y = quant_word_exact(v.z, s, r, exact_ok) | (quant_word_exact(v.w, s, r, exact_ok) << 16);
+  }
+  return out;
+}
+
+// Full chunks of kThreads * kUnroll vectors are processed with all loads
+// issued back to back (no per-load guard, so nothing serializes them); the
+// remaining vectors, fewer than one chunk, one per thread with a guard.
+template <bool kPow2>
 __global__ __launch_bounds__(kThreads) void quantize_static_kernel(const u32x4* __restrict__ x,
                                                                    u32x2* __restrict__ q, int64_t nvec,
-                                                                   float s, float r) {
-  const int64_t step = (int64_t)gridDim.x * (kThreads * kUnroll);
-  for (int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll); base < nvec; base += step) {
+                                                                   float s, float r, bool exact_ok) {
+  constexpr int64_t kChunk = kThreads * kUnroll;
+  const int64_t full = nvec / kChunk * kChunk;
+  const int64_t step = (int64_t)gridDim.x * kChunk;
+  for (int64_t base = (int64_t)blockIdx.x * kChunk + threadIdx.x; base < full; base += step) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < nvec) v[u] = __builtin_nontemporal_load(x + i);
-    }
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < nvec) {
-        uint32_t doubt = 0;
-        const uint32_t p0 = quant_pair_fast(v[u].x, r, doubt);
-        const uint32_t p1 = quant_pair_fast(v[u].y, r, doubt);
-        const uint32_t p2 = quant_pair_fast(v[u].z, r, doubt);
-        const uint32_t p3 = quant_pair_fast(v[u].w, r, doubt);
-        u32x2 out;
-        out.x = pick_codes(p0, p1);
-        out.y = pick_codes(p2, p3);
-        if (doubt) {
-          out.x = quant_word_exact(v[u].x, s) | (quant_word_exact(v[u].y, s) << 16);
-          out.y = quant_word_exact(v[u].z, s) | (quant_word_exact(v[u].w, s) << 16);
-        }
-        __builtin_nontemporal_store(out, q + i);
-      }
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      __builtin_nontemporal_store(quantize8<kPow2>(v[u], s, r, exact_ok), q + base + u * kThreads);
   }
+  for (int64_t i = full + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads)
+    q[i] = quantize8<kPow2>(x[i], s, r, exact_ok);
 }
 
 }  // namespace
@@ -59,8 +75,15 @@ hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipSt
   int64_t blocks = (nvec + per_block - 1) / per_block;
   if (blocks > 4096) blocks = 4096;
   const float r = 1.0f / scale;  // correctly rounded on the host
-  hipLaunchKernelGGL(quantize_static_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     static_cast<const u32x4*>(x), static_cast<u32x2*>(q), nvec, scale, r);
+  int e = 0;
+  const bool pow2 = std::frexp(scale, &e) == 0.5f;  // scale = 2^(e-1), and 1/scale is normal
+  const bool exact_ok = scale >= 0x1p-92f;
+  if (pow2)
+    hipLaunchKernelGGL(quantize_static_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       static_cast<const u32x4*>(x), static_cast<u32x2*>(q), nvec, scale, r, exact_ok);
+  else
+    hipLaunchKernelGGL(quantize_static_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       static_cast<const u32x4*>(x), static_cast<u32x2*>(q), nvec, scale, r, exact_ok);
   return hipGetLastError();
 }
 

@@ -39,45 +39,48 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
 }
 
 template <bool kFp8Out>
+__device__ __forceinline__ void swiglu8(const u32x4 gv, const u32x4 uv, void* out, int64_t i, float rs) {
+  float h[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[2 * e] = silu_mul(bf16_lo(gv[e]), bf16_lo(uv[e]));
+    h[2 * e + 1] = silu_mul(bf16_hi(gv[e]), bf16_hi(uv[e]));
+  }
+  if constexpr (kFp8Out) {
+    u32x2 o;
+    o.x = code_of(h[0], rs) | (code_of(h[1], rs) << 8) | (code_of(h[2], rs) << 16) | (code_of(h[3], rs) << 24);
+    o.y = code_of(h[4], rs) | (code_of(h[5], rs) << 8) | (code_of(h[6], rs) << 16) | (code_of(h[7], rs) << 24);
+    __builtin_nontemporal_store(o, static_cast<u32x2*>(out) + i);
+  } else {
+    u32x4 o;
+    o.x = bf16_pair(h[0], h[1]);
+    o.y = bf16_pair(h[2], h[3]);
+    o.z = bf16_pair(h[4], h[5]);
+    o.w = bf16_pair(h[6], h[7]);
+    __builtin_nontemporal_store(o, static_cast<u32x4*>(out) + i);
+  }
+}
+
+// Full chunks with unguarded back-to-back loads, then a guarded tail.
+template <bool kFp8Out>
 __global__ __launch_bounds__(kThreads) void swiglu_2in_kernel(const u32x4* __restrict__ g,
                                                               const u32x4* __restrict__ u, void* __restrict__ out,
                                                               int64_t nvec, float rs) {
-  const int64_t step = (int64_t)gridDim.x * (kThreads * kUnroll);
-  for (int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll); base < nvec; base += step) {
+  constexpr int64_t kChunk = kThreads * kUnroll;
+  const int64_t full = nvec / kChunk * kChunk;
+  const int64_t step = (int64_t)gridDim.x * kChunk;
+  for (int64_t base = (int64_t)blockIdx.x * kChunk + threadIdx.x; base < full; base += step) {
     u32x4 gv[kUnroll], uv[kUnroll];
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) {
-      const int64_t i = base + k * kThreads + threadIdx.x;
-      if (i < nvec) {
-        gv[k] = __builtin_nontemporal_load(g + i);
-        uv[k] = __builtin_nontemporal_load(u + i);
-      }
+      gv[k] = __builtin_nontemporal_load(g + base + k * kThreads);
+      uv[k] = __builtin_nontemporal_load(u + base + k * kThreads);
     }
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t i = base + k * kThreads + threadIdx.x;
-      if (i >= nvec) continue;
-      float h[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[2 * e] = silu_mul(bf16_lo(gv[k][e]), bf16_lo(uv[k][e]));
-        h[2 * e + 1] = silu_mul(bf16_hi(gv[k][e]), bf16_hi(uv[k][e]));
-      }
-      if constexpr (kFp8Out) {
-        u32x2 o;
-        o.x = code_of(h[0], rs) | (code_of(h[1], rs) << 8) | (code_of(h[2], rs) << 16) | (code_of(h[3], rs) << 24);
-        o.y = code_of(h[4], rs) | (code_of(h[5], rs) << 8) | (code_of(h[6], rs) << 16) | (code_of(h[7], rs) << 24);
-        __builtin_nontemporal_store(o, static_cast<u32x2*>(out) + i);
-      } else {
-        u32x4 o;
-        o.x = bf16_pair(h[0], h[1]);
-        o.y = bf16_pair(h[2], h[3]);
-        o.z = bf16_pair(h[4], h[5]);
-        o.w = bf16_pair(h[6], h[7]);
-        __builtin_nontemporal_store(o, static_cast<u32x4*>(out) + i);
-      }
-    }
+    for (int k = 0; k < kUnroll; ++k) swiglu8<kFp8Out>(gv[k], uv[k], out, base + k * kThreads, rs);
   }
+  for (int64_t i = full + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads)
+    swiglu8<kFp8Out>(g[i], u[i], out, i, rs);
 }
 
 }  // namespace
