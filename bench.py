@@ -88,7 +88,7 @@ def gemm_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(case, rows=2048, cols=1024):
+def cpu_baseline(case, rows=4096, cols=2048):
     """The oracle's W8A8 step on a bounded sample: `rows` rows x `cols` output columns per projection."""
     from threadpoolctl import threadpool_info
 
