@@ -169,6 +169,9 @@ def test_gemm_w8a8_validation(lib):
     assert g8(lib, sw=0.0) == fp8lin.ESCALE
     assert g8(lib, si=2.0**-100, sw=2.0**-100) == fp8lin.ESCALE  # product underflows
     assert g8(lib, M=1 << 31) == fp8lin.EUNSUPPORTED
+    assert g8(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
+    assert g8(lib, N=1 << 22, ldy=1 << 22) == fp8lin.EUNSUPPORTED
+    assert g8(lib, ldy=1 << 22) == fp8lin.EUNSUPPORTED
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
     assert g8(lib, M=0) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before

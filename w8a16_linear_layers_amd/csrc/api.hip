@@ -19,6 +19,10 @@ void count_launch(int kind) { g_launches[kind].fetch_add(1, std::memory_order_re
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxK = int64_t(1) << 24;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// GEMM tiles are addressed through buffer resources with 32-bit offsets: 256
+// rows of a bf16 activation (2 K bytes each) and 128 output rows (2 ldy bytes
+// each) must stay below the 2^31 out-of-range offset.
+constexpr int64_t kMaxGemmDim = int64_t(1) << 22;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -32,11 +36,17 @@ int32_t check_matrix(int64_t rows, int64_t cols) {
   return FP8LIN_OK;
 }
 
+int32_t check_gemm_matrix(int64_t M, int64_t K) {
+  const int32_t st = check_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  return K >= kMaxGemmDim ? FP8LIN_EUNSUPPORTED : FP8LIN_OK;
+}
+
 // Shared checks of one projection of a GEMM (weight [n, k], output [m, ldy]).
 int32_t check_output(const void* qw, const void* y, int64_t N, int64_t ldy, int64_t M) {
   if (qw == nullptr || (M > 0 && y == nullptr)) return FP8LIN_EINVAL;
   if (N <= 0 || ldy <= 0) return FP8LIN_EINVAL;
-  if (N > kMaxRows || ldy > kMaxRows) return FP8LIN_EUNSUPPORTED;
+  if (N >= kMaxGemmDim || ldy >= kMaxGemmDim) return FP8LIN_EUNSUPPORTED;
   if (N % 8 != 0 || ldy % 8 != 0 || ldy < N) return FP8LIN_ELAYOUT;
   if (!aligned16(qw) || !aligned16(y)) return FP8LIN_ELAYOUT;  // NULL is aligned
   return FP8LIN_OK;
@@ -71,7 +81,7 @@ int32_t fp8lin_quantize_static(const void* x_bf16, void* q_e4m3, int64_t rows, i
 
 int32_t fp8lin_gemm_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K, int64_t ldy,
                          float input_scale, float weight_scale, hipStream_t stream) {
-  int32_t st = check_matrix(M, K);
+  int32_t st = check_gemm_matrix(M, K);
   if (st != FP8LIN_OK) return st;
   if (K == 0 || (M > 0 && qx == nullptr)) return FP8LIN_EINVAL;
   if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
@@ -99,7 +109,7 @@ int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* 
                           int64_t K, int64_t ldy, float weight_scale, hipStream_t stream) {
   if (x_dtype == FP8LIN_DT_E4M3) return FP8LIN_EDTYPE;
   if (x_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
-  int32_t st = check_matrix(M, K);
+  int32_t st = check_gemm_matrix(M, K);
   if (st != FP8LIN_OK) return st;
   if (K == 0 || (M > 0 && x == nullptr)) return FP8LIN_EINVAL;
   if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
@@ -128,7 +138,7 @@ int32_t fp8lin_qkv_shared(const void* x_bf16, int64_t M, int64_t K, int32_t npro
     return FP8LIN_EINVAL;
   if (nproj < 1 || nproj > fp8lin::kMaxGroups) return FP8LIN_EINVAL;
   if (mode != FP8LIN_MODE_W8A8 && mode != FP8LIN_MODE_W8A16) return FP8LIN_EINVAL;
-  int32_t st = check_matrix(M, K);
+  int32_t st = check_gemm_matrix(M, K);
   if (st != FP8LIN_OK) return st;
   if (K == 0 || (M > 0 && x_bf16 == nullptr)) return FP8LIN_EINVAL;
   if (!aligned16(x_bf16)) return FP8LIN_ELAYOUT;
