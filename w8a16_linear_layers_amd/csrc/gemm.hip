@@ -56,8 +56,8 @@ constexpr int kBandM = 8;  // M-tiles per raster band
 // W8A8: two stages of 256 x 128-byte E4M3 tiles for each operand (128 KiB),
 //       then a 32 KiB epilogue area (8 KiB per wave).
 // W8A16: three stages of a 256 x 64-byte E4M3 weight tile (16 KiB) and a
-//       256 x 64-element bf16 activation tile (32 KiB); its epilogue reuses the
-//       first 128 KiB after the K loop.
+//       256 x 64-element bf16 activation tile (32 KiB); its epilogue stages
+//       rows in the activation tile of the buffer the tile's last stage used.
 constexpr int kW8A8Stage = kTileN * 128;  // 32 KiB per operand per stage
 constexpr int kW8A8EpiOffset = 4 * kW8A8Stage;
 constexpr int kW8A8EpiWave = 32 * 256;  // 32 output rows of 256 bytes per wave
@@ -67,7 +67,7 @@ constexpr int kStageBf16 = kTileM * 64 * 2;  // 32 KiB
 constexpr int kLdsW8A8 = kW8A8EpiOffset + 4 * kW8A8EpiWave;
 constexpr int kLdsW8A16 = kStages16 * (kStageE4M3 + kStageBf16);
 constexpr int kLdsBytes = kLdsW8A8 > kLdsW8A16 ? kLdsW8A8 : kLdsW8A16;
-static_assert(kLdsBytes >= 4 * 128 * 256, "the W8A16 epilogue stages 128 KiB");
+static_assert(kStageBf16 >= 4 * kW8A8EpiWave, "the W8A16 epilogue stages 8 KiB per wave");
 static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS per workgroup");
 __shared__ __attribute__((aligned(16))) uint8_t lds_mem[kLdsBytes];
 
@@ -135,11 +135,13 @@ __device__ __forceinline__ void wait_vmem_and_barrier() {
 // (p % kChunks) ^ swizzle(r) of logical row r (= P for 128-byte rows,
 // row64(P) for 64-byte rows). voff[j] is that chunk's byte offset inside the
 // tile's resource at K = 0; a stage's K offset travels in the scalar offset.
+// The swizzles depend only on row bits below 5, which j does not change, so
+// a thread copies the same logical chunk of every row it serves (kbyte).
 template <int kChunks>
 struct CopyPlan {
   i32x4 rsrc;
   uint32_t voff[kChunks];
-  int kbyte[kChunks];  // first K byte of the chunk within a stage row
+  int kbyte;  // first K byte of the thread's chunk within a stage row
 
   __device__ __forceinline__ void init(const uint8_t* src, int row0, int rows, int64_t ld_bytes, int tid) {
     const int valid = rows < 256 ? rows : 256;
@@ -150,7 +152,7 @@ struct CopyPlan {
       const int r = kChunks == 4 ? row64(p / kChunks) : p / kChunks;
       const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : swz8(r));
       voff[j] = (uint32_t)(r * ld_bytes) + (uint32_t)c * 16u;
-      kbyte[j] = c * 16;
+      if (j == 0) kbyte = c * 16;
     }
   }
 
@@ -162,12 +164,10 @@ struct CopyPlan {
   // All chunks of the stage starting at byte `k0b`; chunks at or beyond
   // byte `kb` of a row (the K tail) read as zero.
   __device__ __forceinline__ void copy(const uint8_t* lds_tile, int k0b, int kb, uint32_t wave_off) const {
-    const bool tail = k0b + kChunks * 16 > kb;
+    const bool beyond = k0b + kbyte >= kb;
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const uint32_t v = (tail && k0b + kbyte[j] >= kb) ? kOutOfRange : voff[j];
-      dma16(rsrc, v, (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
-    }
+    for (int j = 0; j < kChunks; ++j)
+      dma16(rsrc, beyond ? kOutOfRange : voff[j], (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
   }
 };
 
@@ -240,6 +240,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const GemmGroup& grp,
 // out-of-range offset, so every lane issues the same eight stores.
 __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, uint8_t* stage, const GemmGroup& grp,
                                               __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
+  // The lane-dependent offsets below are cheap; an opaque copy of the lane
+  // index keeps the compiler from holding them in registers across the K loop.
+  asm volatile("" : "+v"(lane));
   const float alpha = grp.alpha;
   const int h = lane >> 5;
   const int m = lane & 31;
@@ -268,17 +271,6 @@ __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, ui
     const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 2u : kOutOfRange;
     __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, 0);
   }
-}
-
-// The whole 128 x 128 wave tile through a 32 KiB per-wave staging area that
-// overlaps the pipeline buffers (hence the workgroup barrier first).
-__device__ __forceinline__ void epilogue_staged(const v16f (&acc)[4][4], const GemmGroup& grp, int M, int m_base,
-                                                int n_base, int lane, int wave) {
-  __syncthreads();
-  uint8_t* stage = lds_mem + wave * (128 * 256);
-  const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, M, m_base);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage + j * 32 * 256, grp, out, n_base, lane);
 }
 
 // ------------------------------------------------------------------ W8A8
@@ -320,9 +312,13 @@ __device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], 
 //             8 MFMAs is then followed by the read of a k-step-0 fragment of
 //             stage s + 1 into (wa, xa) and two copies of stage s + 2 into the
 //             buffer stage s used.
+// In stage 0 of a tile the copies of stage 1 are known to have landed, and
+// the wait skips vmcnt (kWaitVm = false) so that it does not also wait for
+// the previous tile's output stores.
 // The barrier sits mid-stage, after 8 MFMAs that only need registers, and
 // sched_barrier keeps the compiler from regrouping the slots, so copies and
 // reads issue in the shadow of the matrix-core work.
+template <bool kWaitVm>
 __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i (&xa)[4], v8i (&wb)[4], v8i (&xb)[4],
                                            const CopyPlan<8>& pw, const CopyPlan<8>& px, int s, int row_w, int row_x,
                                            int g, uint32_t wave_off) {
@@ -347,7 +343,12 @@ __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i 
   for (int t = 0; t < 16; ++t) {
     const int i = t >> 2, j = t & 3;
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wb[i], xb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-    if (t == 7) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t == 7) {
+      if constexpr (kWaitVm)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     if (t >= 8) {
       const int f = t - 8;
       if (f == 0)
@@ -382,8 +383,9 @@ __device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8>& pw, const C
 // Persistent W8A8 kernel: one workgroup per CU walks the tiles of dispatch
 // slots blockIdx.x, blockIdx.x + gridDim.x, ... After the last LDS read of
 // a tile the first two stages of the next tile are issued, so their latency
-// overlaps the last k-step and the epilogue, which stages its rows through
-// an LDS area of its own.
+// overlaps the last k-step; each wave waits for them before it issues the
+// tile's output stores (which go through an LDS area of its own), so the
+// next tile starts without waiting for those stores to complete.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a8_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -403,13 +405,13 @@ gemm_w8a8_kernel(const GemmArgs a) {
   pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, K, tid);
   px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, K, tid);
   w8a8_first_stages(pw, px, K, KT, wave_off);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   for (;;) {
     const TileCoord cur = tc;
     const GemmGroup& grp = a.g[cur.group];
-    // stages 0 and 1 have landed (this also waits for the stores of the
-    // previous tile's epilogue, issued after them)
-    wait_vmem_and_barrier<0>();
+    // every wave's copies of stages 0 and 1 have landed
+    asm volatile("s_barrier" ::: "memory");
     v8i wa[4], xa[4], wb[4], xb[4];
     w8a8_frags(0, 0, row_w, row_x, g, wa, xa);
     v16f acc[4][4];
@@ -420,7 +422,10 @@ gemm_w8a8_kernel(const GemmArgs a) {
 
     int s = 0;
     // steady state: stage s + 2 exists and is not the last (no K tail)
-    for (; s + 4 <= KT; ++s) w8a8_stage(acc, wa, xa, wb, xb, pw, px, s, row_w, row_x, g, wave_off);
+    if (KT >= 4) {
+      w8a8_stage<false>(acc, wa, xa, wb, xb, pw, px, 0, row_w, row_x, g, wave_off);
+      for (s = 1; s + 4 <= KT; ++s) w8a8_stage<true>(acc, wa, xa, wb, xb, pw, px, s, row_w, row_x, g, wave_off);
+    }
     // the stages before the last: copy only what exists, K tail masked
     for (; s + 1 < KT; ++s) {
       w8a8_frags(s & 1, 1, row_w, row_x, g, wb, xb);
@@ -446,6 +451,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
       w8a8_first_stages(pw, px, K, KT, wave_off);
     }
     w8a8_mma(acc, wb, xb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's stages 0 and 1
     const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
 #pragma unroll
     for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, epi, grp, out, cur.n0 + wn * 128, lane);
@@ -470,87 +476,184 @@ __device__ __forceinline__ v8bf dequant8(uint32_t d0, uint32_t d1) {
 
 __device__ __forceinline__ v8bf as_v8bf(u32x4 c) { return __builtin_bit_cast(v8bf, c); }
 
-// W8A16 pipeline: K stages of 64 elements in three LDS buffers, stage s + 2
-// copied while stage s computes, one vmcnt + barrier per stage.
+constexpr int kW16Copies = 12;          // copies per thread per stage
+constexpr int kW16EpilogueStores = 32;  // buffer stores per thread per tile
+
+// Persistent W8A16 pipeline: K stages of 64 elements; one workgroup per CU
+// walks the tiles of dispatch slots blockIdx.x, blockIdx.x + gridDim.x, ...
+// Stage g (counted over all tiles of the workgroup) sits in LDS buffer g % 3.
+// The copy cursor runs two stages ahead of the matrix cores, across tile
+// boundaries, so the first stages of the next tile are in flight while a
+// tile finishes; past the workgroup's last tile it copies zeros into
+// buffers no one reads. Fragments are double-buffered in registers by half
+// stage (32 K each): set A holds (g, h0), set B (g, h1).
+struct W16Copier {
+  CopyPlan<4> pw;  // E4M3 weight, 64-byte stage rows
+  CopyPlan<8> px;  // bf16 activation, 128-byte stage rows
+  int tile_slot;   // dispatch slot of the tile being copied
+  int k;           // next stage of that tile
+
+  __device__ __forceinline__ void start_tile(const GemmArgs& a, int slot, int tid) {
+    const TileCoord tc = tile_at(a, slot);
+    tile_slot = slot;
+    k = 0;
+    pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
+    px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)a.k * 2, tid);
+  }
+
+  // Copy c of the current stage into buffer `buf`: c < 4 weight chunk c,
+  // else activation chunk c - 4; chunks beyond K read as zero.
+  __device__ __forceinline__ void issue(int c, int buf, int K, uint32_t wave_off) const {
+    if (c < 4) {
+      const int k0b = k * 64;
+      dma16(pw.rsrc, k0b + pw.kbyte >= K ? kOutOfRange : pw.voff[c], (uint32_t)k0b,
+            lds_addr(lds16_w(buf)) + c * kThreads * 16 + wave_off);
+    } else {
+      const int k0b = k * 128;
+      dma16(px.rsrc, k0b + px.kbyte >= 2 * K ? kOutOfRange : px.voff[c - 4], (uint32_t)k0b,
+            lds_addr(lds16_x(buf)) + (c - 4) * kThreads * 16 + wave_off);
+    }
+  }
+
+  __device__ __forceinline__ void advance(const GemmArgs& a, int KT, int tid) {
+    if (++k == KT) {
+      const int next = tile_slot + (int)gridDim.x;
+      if (next < a.total_tiles) {
+        start_tile(a, next, tid);
+      } else {
+        k = 0;
+        pw.rsrc[2] = 0;
+        px.rsrc[2] = 0;
+      }
+    }
+  }
+};
+
+// One half stage of fragments: weight chunk (2h + g) of rows row_w + 32 i
+// (16 E4M3 each) and activation chunks 4h + 2g + e of rows row_x + 32 j
+// (8 bf16 each, x[2 j + e]).
+struct W16Half {
+  u32x4 w[4];
+  u32x4 x[8];
+};
+
+// Per-lane byte offsets of a lane's chunks for half h (e: activation chunk
+// of the pair), inside the weight and activation tiles of a buffer; block
+// i or j adds 2048 (64-byte rows) or 4096 (128-byte rows).
+struct W16Addr {
+  uint32_t w[2], x[2][2];
+  __device__ __forceinline__ void init(int row_w, int row_x, int g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w[h] = row64(row_w) * 64 + ((2 * h + g) ^ swz4(row_w)) * 16;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) x[h][e] = row_x * 128 + ((4 * h + 2 * g + e) ^ swz8(row_x)) * 16;
+    }
+  }
+};
+
+// Read number r (0..11) of half h of buffer b into f.
+__device__ __forceinline__ void w16_read(W16Half& f, int r, int b, int h, const W16Addr& ad) {
+  if (r < 4)
+    f.w[r] = lds_chunk(lds16_w(b), ad.w[h] + r * 2048);
+  else
+    f.x[r - 4] = lds_chunk(lds16_x(b), ad.x[h][(r - 4) & 1] + ((r - 4) >> 1) * 4096);
+}
+
+// Half stage on set f: 32 MFMAs (two k-steps of 16), interleaved with up to
+// one LDS read into set `nf` and one copy per slot as `plan` says.
+__device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W16Half& nf, int nb, int nh,
+                                         const W16Addr& ad, W16Copier& cp, int cbuf, int K, uint32_t wave_off,
+                                         bool second, bool after_stores) {
+  v8bf wf[4];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int e = t >> 4, i = (t >> 2) & 3, j = t & 3;
+    if (j == 0) wf[i] = dequant8(f.w[i][2 * e], f.w[i][2 * e + 1]);
+    const v8bf xv = as_v8bf(f.x[2 * j + e]);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xv, acc[i][j], 0, 0, 0);
+    if (!second) {
+      // first half: the 12 reads of the second half's fragments
+      if ((t & 1) && t < 24) w16_read(nf, t >> 1, nb, nh, ad);
+    } else {
+      if (t == 3) {
+        // the next stage has landed for every wave, and every wave is done
+        // with the buffer the copies below refill
+        // (the previous tile's output stores, issued after the copies of
+        // this tile's stage 1, need not have completed)
+        if (after_stores)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16EpilogueStores) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (t >= 4 && t < 28) {
+        const int q = t - 4;
+        if (q & 1)
+          cp.issue(q >> 1, cbuf, K, wave_off);
+        else
+          w16_read(nf, q >> 1, nb, nh, ad);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a16_kernel(const GemmArgs a) {
-  const TileCoord tc = tile_at(a, blockIdx.x);
-  const GemmGroup& grp = a.g[tc.group];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int K = a.k;
   const int KT = (K + 63) / 64;
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
-  CopyPlan<4> pw;
-  CopyPlan<8> px;
-  pw.init(grp.w, tc.n0, grp.n - tc.n0, K, tid);
-  px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)K * 2, tid);
+  W16Addr ad;
+  ad.init(wn * 128 + (lane & 31), wm * 128 + (lane & 31), lane >> 5);
 
-  v16f acc[4][4];
+  W16Copier cp;
+  cp.start_tile(a, blockIdx.x, tid);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int v = 0; v < 2; ++v) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-
-#pragma unroll
-  for (int s = 0; s < kStages16 - 1; ++s) {
-    if (s < KT) {
-      pw.copy(lds16_w(s), s * 64, K, wave_off);
-      px.copy(lds16_x(s), s * 128, 2 * K, wave_off);
-    }
+    for (int c = 0; c < kW16Copies; ++c) cp.issue(c, v, K, wave_off);
+    cp.advance(a, KT, tid);
   }
+  wait_vmem_and_barrier<kW16Copies>();  // stage 0 has landed
 
-  const int row_w = wn * 128 + (lane & 31);
-  const int row_x = wm * 128 + (lane & 31);
-  const int g = lane >> 5;
+  W16Half fa, fb;
+#pragma unroll
+  for (int r = 0; r < 12; ++r) w16_read(fa, r, 0, 0, ad);
+  int b = 0;  // buffer of the current stage
 
-  for (int kt = 0; kt < KT; ++kt) {
-    // 12 copies per stage per thread
-    if (kt + 1 < KT)
-      wait_vmem_and_barrier<12>();
-    else
-      wait_vmem_and_barrier<0>();
+  for (int tile_slot = blockIdx.x; tile_slot < a.total_tiles; tile_slot += (int)gridDim.x) {
+    const bool first = tile_slot == (int)blockIdx.x;
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-    const int next = kt + kStages16 - 1;
-    if (next < KT) {
-      const int sb = next % kStages16;
-      pw.copy(lds16_w(sb), next * 64, K, wave_off);
-      px.copy(lds16_x(sb), next * 128, 2 * K, wave_off);
+    for (int s = 0; s < KT; ++s) {
+      const int nb = b == 2 ? 0 : b + 1;      // next stage's buffer
+      const int cb = b == 0 ? 2 : b - 1;      // buffer of stage + 2
+      w16_half(acc, fa, fb, b, 1, ad, cp, cb, K, wave_off, false, false);
+      w16_half(acc, fb, fa, nb, 0, ad, cp, cb, K, wave_off, true, s == 0 && !first);
+      cp.advance(a, KT, tid);
+      b = nb;
     }
 
-    const int cb = kt % kStages16;
-    // Two halves of the stage: K [0, 32) and [32, 64). In half h, lane group
-    // g holds K [32h + 16g, 32h + 16g + 16): weight chunk 2h + g (16 E4M3)
-    // and activation chunks 4h + 2g, 4h + 2g + 1 (8 bf16 each); MFMA step
-    // 2h + e uses the e-th 8-element half of each.
+    // Epilogue: rows staged in the activation tile of the last stage's
+    // buffer, which no wave reads once lgkmcnt(0) + barrier have passed.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const TileCoord tc = tile_at(a, tile_slot);
+    const GemmGroup& grp = a.g[tc.group];
+    const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, tc.m0 + wm * 128);
+    uint8_t* stage = lds16_x(b == 0 ? 2 : b - 1) + wave * (32 * 256);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v8bf wf[4][2], xf[4][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = row_w + i * 32;
-        const u32x4 c = lds_chunk(lds16_w(cb), row64(r) * 64 + ((2 * h + g) ^ swz4(r)) * 16);
-        wf[i][0] = dequant8(c[0], c[1]);
-        wf[i][1] = dequant8(c[2], c[3]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = row_x + j * 32;
-        xf[j][0] = as_v8bf(lds_chunk(lds16_x(cb), r * 128 + ((4 * h + 2 * g) ^ swz8(r)) * 16));
-        xf[j][1] = as_v8bf(lds_chunk(lds16_x(cb), r * 128 + ((4 * h + 2 * g + 1) ^ swz8(r)) * 16));
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i][e], xf[j][e], acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, out, tc.n0 + wn * 128, lane);
   }
-
-  epilogue_staged(acc, grp, a.m, tc.m0 + wm * 128, tc.n0 + wn * 128, lane, wave);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Compute units of the current device (256 on MI355X).
@@ -575,7 +678,11 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_w8a16_kernel, dim3((unsigned)a.total_tiles), dim3(kThreads), 0, s, a);
+  static const int cus = cu_count();
+  int grid = cus - cus % kXcds;
+  if (grid <= 0) grid = kXcds;
+  if (grid > a.total_tiles) grid = a.total_tiles;
+  hipLaunchKernelGGL(gemm_w8a16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
