@@ -2,24 +2,28 @@
 
 One step = the shared-QKV projection group in W8A8 mode at its full size:
 x bf16 [16384, 4096] is quantized once to E4M3 with its static input scale
-(fp8lin_quantize_static), then three E4M3 4096 -> 4096 projections with
-distinct weight scales run on it (fp8lin_gemm_w8a8, one call each, HIP
-events around every GEMM). `value` is the GEMM work of the step,
-3 x 2 M N K, over the step's wall time (quantization included), in TFLOP/s.
+(fp8lin_quantize_static), then the three E4M3 4096 -> 4096 projections with
+distinct weight scales run on it in one grouped launch
+(fp8lin_gemm_w8a8_group, HIP events around it). `value` is the GEMM work of
+the step, 3 x 2 M N K, over the step's wall time (quantization included),
+in TFLOP/s.
 
 In the same run, on the same resident inputs:
-  * w8a16     the 16-bit step of the same projections (fp8lin_gemm_w8a16 x3)
-  * rows      every other hot-path call at its workload size: the grouped
-              fp8lin_qkv_shared in both modes, quantize and SwiGLU (GB/s,
+  * w8a16     the 16-bit step of the same projections (fp8lin_qkv_shared in
+              W8A16 mode: one grouped launch, no quantization)
+  * rows      every other hot-path call at its workload size: the same step
+              as three separate fp8lin_gemm_w8a8 calls, fp8lin_qkv_shared in
+              both modes, quantize and SwiGLU (GB/s,
               input/output buffers rotated over > 512 MB so the 256 MB
               last-level cache cannot serve repeats), the gated-MLP GEMMs,
               the 1024- and 8192-row projections, and the step policy
-  * roofline  the W8A8 GEMM kernel against the dense FP8 matrix-core peak
+  * roofline  the grouped W8A8 GEMM launch against the dense FP8 matrix-core
+              peak
   * cpu_baseline  the CPU oracle on a bounded sample of the same step
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --pmc   (a few launches of each kernel and a plain
-                                copy, for rocprofv3 counter runs)
+       python bench.py --pmc   (a few launches of each step kernel and a
+                                plain copy, for rocprofv3 counter runs)
 """
 
 import argparse
@@ -44,7 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 M, K, N = 16384, 4096, 4096
 GEMM_FLOP = 2.0 * M * N * K
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_16384x4096x4096_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_group3_16384x4096x4096_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "w8a16_linear_layers_amd", "csrc", "gemm.hip")
 
 
@@ -76,7 +80,7 @@ def rotating(make, total_bytes, per_set_bytes):
 
 
 def gemm_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if current."""
+    """HBM bytes per grouped GEMM launch from the committed rocprofv3 counter runs, if current."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
@@ -88,7 +92,7 @@ def gemm_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(case, rows=4096, cols=2048):
+def cpu_baseline(case, rows=8192, cols=4096):
     """The oracle's W8A8 step on a bounded sample: `rows` rows x `cols` output columns per projection."""
     from threadpoolctl import threadpool_info
 
@@ -121,16 +125,18 @@ def pmc_mode(dev):
     x = case.x.to(dev)
     qws = [fp8lin.fp8lin_quantize_static(w.to(dev), s) for w, s in zip(case.ws, case.weight_scales)]
     qx = fp8lin.fp8lin_quantize_static(x, case.input_scale)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
     src = torch.ones(256 * 2**20, dtype=torch.uint8, device=dev)  # 256 MiB plain copy
     dst = torch.empty_like(src)
+    sw = case.weight_scales
     for _ in range(3):
         dst.copy_(src)
         fp8lin.fp8lin_quantize_static(x, case.input_scale, out=qx)
-        fp8lin.fp8lin_gemm_w8a8(qx, qws[0], case.input_scale, case.weight_scales[0], out=y)
-        fp8lin.fp8lin_gemm_w8a16(x, qws[0], case.weight_scales[0], out=y)
+        fp8lin.fp8lin_gemm_w8a8_group(qx, qws, case.input_scale, sw, outs=ys)
+        fp8lin.fp8lin_qkv_shared(x, qws, sw, [case.input_scale] * 3, fp8lin.MODE_W8A16, outs=ys)
     torch.cuda.synchronize()
-    log("pmc mode done: 3 x (copy 256 MiB, quantize, gemm_w8a8, gemm_w8a16)")
+    log("pmc mode done: 3 x (copy 256 MiB, quantize, grouped gemm_w8a8, grouped gemm_w8a16), "
+        "3 projections of 16384x4096x4096")
 
 
 def main():
@@ -169,22 +175,20 @@ def main():
 
     def step_w8a8(ev=None):
         fp8lin.fp8lin_quantize_static(x, s_in, out=qx)
-        for i in range(3):
-            if ev is not None:
-                ev[2 * i].record(stream)
-            fp8lin.fp8lin_gemm_w8a8(qx, qws[i], s_in, case.weight_scales[i], out=ys[i])
-            if ev is not None:
-                ev[2 * i + 1].record(stream)
+        if ev is not None:
+            ev[0].record(stream)
+        fp8lin.fp8lin_gemm_w8a8_group(qx, qws, s_in, case.weight_scales, outs=ys)
+        if ev is not None:
+            ev[1].record(stream)
 
     def step_w8a16():
-        for i in range(3):
-            fp8lin.fp8lin_gemm_w8a16(x, qws[i], case.weight_scales[i], out=ys[i])
+        fp8lin.fp8lin_qkv_shared(x, qws, case.weight_scales, [s_in] * 3, fp8lin.MODE_W8A16, outs=ys)
 
     for _ in range(args.warmup):
         step_w8a8()
     torch.cuda.synchronize()
     log("timing %d W8A8 steps" % args.steps)
-    gemm_ev = [events(6) for _ in range(args.steps)]
+    gemm_ev = [events(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -192,7 +196,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    gemm_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for ev in gemm_ev for i in range(3)]
+    gemm_ms = [ev[0].elapsed_time(ev[1]) for ev in gemm_ev]
     gemm_avg_ms = float(np.mean(gemm_ms))
     value = 3 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
 
@@ -206,7 +210,7 @@ def main():
     ms16 = (time.perf_counter() - t0) * 1e3 / args.steps
     tf16 = 3 * GEMM_FLOP / (ms16 * 1e-3) / 1e12
 
-    achieved = GEMM_FLOP / (gemm_avg_ms * 1e-3) / 1e12
+    achieved = 3 * GEMM_FLOP / (gemm_avg_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -237,7 +241,8 @@ def main():
             "dtype": "bf16 activations x E4M3 weights (exact bf16 dequant), fp32 accumulate",
         },
         "roofline": {
-            "kernel": "gemm_w8a8 (v_mfma_f32_32x32x64_f8f6f4), M=16384 N=4096 K=4096",
+            "kernel": "gemm_w8a8 (v_mfma_f32_32x32x64_f8f6f4), one grouped launch of 3 projections, "
+            "each M=16384 N=4096 K=4096",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_FP8_TFLOPS,
@@ -260,6 +265,21 @@ def other_rows(dev, case, x, qws, qx, ys):
     rows = {}
     s_in, sw = case.input_scale, case.weight_scales
     reps = 20
+
+    # the step as three separate GEMM calls (HIP events around each)
+    evs = []
+    for rep in range(reps + 5):
+        fp8lin.fp8lin_quantize_static(x, s_in, out=qx)
+        for i in range(3):
+            e = events(2)
+            e[0].record()
+            fp8lin.fp8lin_gemm_w8a8(qx, qws[i], s_in, sw[i], out=ys[i])
+            e[1].record()
+            if rep >= 5:
+                evs.append(e)
+    torch.cuda.synchronize()
+    t1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    rows["gemm_w8a8_single_launch_16384x4096x4096"] = {"ms": round(t1, 4), "tflops": round(GEMM_FLOP / t1 / 1e9, 2)}
 
     # grouped shared-QKV call, both modes (one quantize + one grouped GEMM launch / one grouped W8A16 launch)
     t8 = timed(lambda: fp8lin.fp8lin_qkv_shared(x, qws, sw, [s_in] * 3, fp8lin.MODE_W8A8, outs=ys, workspace=qx), reps)

@@ -155,6 +155,26 @@ int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* 
                           int64_t K, int64_t ldy, float weight_scale, hipStream_t stream);
 
 /*
+ * The GEMMs of a shared-input projection group on an activation quantized
+ * once ([TRT-17476] "What changed": every projection of the group consumes
+ * the same FP8 tensor, each with its own weight_scale), in one launch:
+ *   y[i][m, n] = bf16_RNE( (sum_k dec(qx[m, k]) * dec(qw[i][n, k]))
+ *                          * (input_scale * weight_scale[i]) )
+ * i.e. fp8lin_gemm_w8a8 for each i with ldy = n_out[i]; the tiles of all
+ * projections share one grid, so the group fills the GPU as one GEMM would.
+ *   qx            device, E4M3 [M, K], contiguous
+ *   nproj         1..4
+ *   qw[i]         device, E4M3 [n_out[i], K]
+ *   n_out[i]      host array: output width of projection i (multiple of 8)
+ *   weight_scale  host array [nproj]; input_scale: the group's one scale
+ *   y[i]          device, bf16 [M, n_out[i]], contiguous
+ *   The host arrays are read during the call only.
+ */
+int32_t fp8lin_gemm_w8a8_group(const void* qx, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
+                               const int64_t n_out[], const float weight_scale[], float input_scale,
+                               void* const y_bf16[], hipStream_t stream);
+
+/*
  * Shared-input projections: Q/K/V (nproj = 3) or gate/up (nproj = 2)
  * ([TRT-17476] "What changed": the group quantizes its shared activation once
  * and hands the same FP8 tensor to every projection, each with its own

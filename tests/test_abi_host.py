@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -183,6 +183,30 @@ def test_gemm_w8a16_refuses_quantized_activation(lib):
     assert lib.fp8lin_gemm_w8a16(args[0], 7, *args[1:]) == fp8lin.EINVAL
     assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_BF16, FAKE, FAKE, 4, 64, 40, 64, 0.001, None) == fp8lin.ELAYOUT
     assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_BF16, FAKE, FAKE, 0, 64, 64, 64, 0.001, None) == fp8lin.OK
+
+
+def grp(lib, n=(64, 64, 64), si=0.01, sw=(0.001, 0.001, 0.001), qx=FAKE, M=4, K=64, nproj=3):
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    k = len(n)
+    return lib.fp8lin_gemm_w8a8_group(
+        qx, M, K, nproj, (vp * k)(*[FAKE] * k), (i64 * k)(*n), (f32 * k)(*sw), si, (vp * k)(*[FAKE] * k), None
+    )
+
+
+def test_gemm_w8a8_group_validation(lib):
+    assert grp(lib, nproj=0) == fp8lin.EINVAL
+    assert grp(lib, nproj=5, n=(64,) * 5, sw=(0.001,) * 5) == fp8lin.EINVAL
+    assert grp(lib, qx=None) == fp8lin.EINVAL
+    assert grp(lib, qx=FAKE + 8) == fp8lin.ELAYOUT
+    assert grp(lib, K=40) == fp8lin.ELAYOUT
+    assert grp(lib, n=(64, 60, 64)) == fp8lin.ELAYOUT
+    assert grp(lib, si=float("inf")) == fp8lin.ESCALE
+    assert grp(lib, sw=(0.001, 0.0, 0.001)) == fp8lin.ESCALE
+    assert grp(lib, si=2.0**-100, sw=(2.0**-100,) * 3) == fp8lin.ESCALE  # alpha underflows
+    assert grp(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
+    assert grp(lib, M=0) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before
 
 
 def qkv(lib, scales_in=(0.01, 0.01, 0.01), n=(64, 64, 64), mode=0, ws=FAKE, nproj=3):

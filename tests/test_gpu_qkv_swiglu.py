@@ -60,6 +60,27 @@ def test_qkv_shared_w8a8(gpu, m, k, n):
         assert torch.equal(y, outs[i])
 
 
+@pytest.mark.parametrize("m,k,ns", [(300, 528, (264, 136, 520)), (16384, 4096, (4096, 4096, 4096)), (77, 64, (8, 24))])
+def test_gemm_w8a8_group(gpu, m, k, ns):
+    """One launch over the projections of a group equals the oracle per projection."""
+    announce("gemm_w8a8_group m=%d k=%d n=%s" % (m, k, ns))
+    case = config3(m=m, k=k, n=max(ns))
+    ws = [w[:n] for w, n in zip(case.ws, ns)]
+    sw = case.weight_scales[: len(ns)]
+    qg = [fp8lin.fp8lin_quantize_static(w.contiguous().to(gpu), s) for w, s in zip(ws, sw)]
+    qx = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    c0 = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
+    outs = fp8lin.fp8lin_gemm_w8a8_group(qx, qg, case.input_scale, sw)
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) - c0 == 1
+    torch.cuda.synchronize()
+    rows = sample_rows(m, 160, 9) if m > 4096 else np.arange(m)
+    qx_ref = linear.quantize_static(f32(case.x)[rows], case.input_scale)
+    for i, (w, s) in enumerate(zip(ws, sw)):
+        assert outs[i].shape == (m, ns[i]) and outs[i].is_contiguous()
+        ref = linear.gemm_w8a8(qx_ref, linear.quantize_static(f32(w.contiguous()), s), case.input_scale, s)
+        assert_gemm_close(f32(outs[i])[rows], ref, "group proj %d" % i)
+
+
 def test_qkv_shared_w8a16_stands_down(gpu):
     announce("qkv_shared w8a16")
     case = config3(m=520, k=1024, n=512)

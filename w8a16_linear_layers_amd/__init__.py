@@ -29,6 +29,7 @@ __all__ = [
     "fp8lin_quantize_static",
     "fp8lin_gemm_w8a8",
     "fp8lin_gemm_w8a16",
+    "fp8lin_gemm_w8a8_group",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_policy_validate",
@@ -55,6 +56,7 @@ EXPORTS = (
     "fp8lin_quantize_static",
     "fp8lin_gemm_w8a8",
     "fp8lin_gemm_w8a16",
+    "fp8lin_gemm_w8a8_group",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_policy_validate",
@@ -106,6 +108,9 @@ def load_library():
     lib.fp8lin_quantize_static.argtypes = [vp, vp, i64, i64, f32, vp]
     lib.fp8lin_gemm_w8a8.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
     lib.fp8lin_gemm_w8a16.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, f32, vp]
+    lib.fp8lin_gemm_w8a8_group.argtypes = [
+        vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32), f32, ctypes.POINTER(vp), vp,
+    ]
     lib.fp8lin_qkv_shared.argtypes = [
         vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32),
         ctypes.POINTER(f32), ctypes.POINTER(vp), vp, i32, vp,
@@ -117,8 +122,9 @@ def load_library():
     lib.fp8lin_strerror.restype = ctypes.c_char_p
     lib.fp8lin_launch_count.argtypes = [i32]
     lib.fp8lin_launch_count.restype = i64
-    for name in EXPORTS[:7]:
-        getattr(lib, name).restype = i32
+    for name in EXPORTS:
+        if name not in ("fp8lin_strerror", "fp8lin_launch_count"):
+            getattr(lib, name).restype = i32
     _LIB = lib
     return lib
 
@@ -202,6 +208,28 @@ def fp8lin_gemm_w8a16(x, qw, weight_scale, out=None, ldy=None, stream=None):
         "fp8lin_gemm_w8a16",
     )
     return out
+
+
+def fp8lin_gemm_w8a8_group(qx, qws, input_scale, weight_scales, outs=None, stream=None):
+    """The projections of a group on one quantized activation, in one launch; returns the bf16 outputs."""
+    if qx.dtype != torch.uint8 or any(w.dtype != torch.uint8 for w in qws):
+        raise TypeError("qx and the weights must hold E4M3 codes as torch.uint8")
+    m, k = _rows(qx)
+    n = len(qws)
+    if outs is None:
+        outs = [torch.empty(tuple(qx.shape[:-1]) + (w.shape[0],), dtype=torch.bfloat16, device=qx.device) for w in qws]
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    c_w = (vp * n)(*[w.data_ptr() for w in qws])
+    c_n = (i64 * n)(*[w.shape[0] for w in qws])
+    c_sw = (f32 * n)(*[float(s) for s in weight_scales])
+    c_y = (vp * n)(*[o.data_ptr() for o in outs])
+    _check(
+        load_library().fp8lin_gemm_w8a8_group(
+            _ptr(qx), m, k, n, c_w, c_n, c_sw, float(input_scale), c_y, _stream(stream)
+        ),
+        "fp8lin_gemm_w8a8_group",
+    )
+    return outs
 
 
 def fp8lin_qkv_shared(x, qws, weight_scales, input_scales, mode, outs=None, workspace=None, stream=None):

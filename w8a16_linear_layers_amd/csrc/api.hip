@@ -182,6 +182,37 @@ int32_t fp8lin_qkv_shared(const void* x_bf16, int64_t M, int64_t K, int32_t npro
   return hip_status(fp8lin::launch_gemm_w8a16(a, stream));
 }
 
+int32_t fp8lin_gemm_w8a8_group(const void* qx, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
+                               const int64_t n_out[], const float weight_scale[], float input_scale,
+                               void* const y_bf16[], hipStream_t stream) {
+  if (qw == nullptr || n_out == nullptr || weight_scale == nullptr || y_bf16 == nullptr) return FP8LIN_EINVAL;
+  if (nproj < 1 || nproj > fp8lin::kMaxGroups) return FP8LIN_EINVAL;
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && qx == nullptr)) return FP8LIN_EINVAL;
+  if (!aligned16(qx)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(input_scale)) return FP8LIN_ESCALE;
+  GemmArgs a{};
+  a.x = qx;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = nproj;
+  for (int i = 0; i < nproj; ++i) {
+    if ((st = check_output(qw[i], y_bf16[i], n_out[i], n_out[i], M)) != FP8LIN_OK) return st;
+    if (!scale_ok(weight_scale[i])) return FP8LIN_ESCALE;
+    a.g[i].w = static_cast<const uint8_t*>(qw[i]);
+    a.g[i].y = y_bf16[i];
+    a.g[i].n = (int32_t)n_out[i];
+    a.g[i].ldy = (int32_t)n_out[i];
+    a.g[i].alpha = input_scale * weight_scale[i];
+    if (!std::isfinite(a.g[i].alpha) || a.g[i].alpha == 0.0f) return FP8LIN_ESCALE;
+  }
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  if (M == 0) return FP8LIN_OK;
+  count_launch(FP8LIN_KERNEL_GEMM_W8A8);
+  return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
+}
+
 int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void* out, int32_t out_dtype, int64_t rows,
                                 int64_t cols, float out_scale, hipStream_t stream) {
   if (out_dtype != FP8LIN_DT_E4M3 && out_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
