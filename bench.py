@@ -16,7 +16,8 @@ In the same run, on the same resident inputs:
               both modes, quantize and SwiGLU (GB/s,
               input/output buffers rotated over > 512 MB so the 256 MB
               last-level cache cannot serve repeats), the gated-MLP GEMMs,
-              the 1024- and 8192-row projections, and the step policy
+              the 1024- and 8192-row projections, the step policy, and the
+              8-step denoising schedule over 4 blocks (config 5)
   * roofline  the grouped W8A8 GEMM launch against the dense FP8 matrix-core
               peak
   * cpu_baseline  the CPU oracle on a bounded sample of the same step
@@ -92,7 +93,7 @@ def gemm_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(case, rows=8192, cols=4096):
+def cpu_baseline(case, rows=16384, cols=4096):
     """The oracle's W8A8 step on a bounded sample: `rows` rows x `cols` output columns per projection."""
     from threadpoolctl import threadpool_info
 
@@ -146,6 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--no-schedule", action="store_true", help="skip the 8-step schedule row")
     ap.add_argument("--pmc", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -254,14 +256,14 @@ def main():
     }
 
     if not args.no_rows:
-        out["rows"] = other_rows(dev, case, x, qws, qx, ys)
+        out["rows"] = other_rows(dev, case, x, qws, qx, ys, schedule_row=not args.no_schedule)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)
 
 
-def other_rows(dev, case, x, qws, qx, ys):
+def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     rows = {}
     s_in, sw = case.input_scale, case.weight_scales
     reps = 20
@@ -368,7 +370,53 @@ def other_rows(dev, case, x, qws, qx, ys):
         fp8lin.fp8lin_step_policy(pol, 0, i % 8, 8)
     rows["step_policy"] = {"us_per_call_incl_python": round((time.perf_counter() - t0) * 100, 3),
                            "trace_8": "".join("8" if t == fp8lin.MODE_W8A8 else "6" for t in trace)}
+    if schedule_row:
+        rows["schedule_cfg5"] = schedule_cfg5(dev, pol)
     return rows
+
+
+def schedule_cfg5(dev, pol):
+    """The 8-step denoising schedule: 4 blocks x 2 CFG passes x 8 steps at 16384 rows, policy first 3 / last 3."""
+    from w8a16_linear_layers_amd import schedule
+    from workloads import config5, config5_step_input
+
+    m, hidden, inter, nblocks, steps = 16384, 4096, 16384, 4, 8
+    log("schedule row: building 4 synthetic blocks (calibration forward on the GPU)")
+    cases = config5(num_blocks=nblocks, hidden=hidden, inter=inter, cal_rows=256, device=dev)
+    q = lambda w, s: fp8lin.fp8lin_quantize_static(w.to(dev), s)  # noqa: E731
+    blocks = [
+        schedule.BlockWeights(
+            [q(w, s) for w, s in zip(c.w_qkv, c.s_qkv)], c.s_qkv, c.s_in_qkv,
+            q(c.w_out, c.s_out), c.s_out, c.s_in_out,
+            q(c.w_gate, c.s_gate), q(c.w_up, c.s_up), c.s_gate, c.s_up, c.s_in_mlp,
+            q(c.w_down, c.s_down), c.s_down, c.s_h,
+        )
+        for c in cases
+    ]
+    del cases
+    buf = schedule.Buffers(m, hidden, inter, dev)
+    log("schedule row: generating the 16 per-pass inputs")
+    inputs = {(st, b): config5_step_input(st, b, m, hidden).to(dev) for st in range(steps) for b in range(2)}
+    run = lambda: schedule.run_schedule(blocks, pol, steps, lambda st, b: inputs[(st, b)], buf)  # noqa: E731
+    run()  # warm-up pass
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    e0.record()
+    trace = run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flop_pass = 2.0 * m * hidden * (4 * hidden + 3 * inter)  # QKV + out + gate/up + down of one block
+    n8 = sum(1 for t in trace if t == fp8lin.MODE_W8A8)
+    flop = flop_pass * nblocks * 2 * steps
+    return {
+        "ms": round(ms, 2),
+        "tflops": round(flop / ms / 1e9, 1),
+        "tflop": round(flop / 1e12, 1),
+        "trace": "".join("8" if t == fp8lin.MODE_W8A8 else "6" for t in trace),
+        "w8a8_steps": n8,
+        "w8a16_steps": steps - n8,
+    }
 
 
 if __name__ == "__main__":
