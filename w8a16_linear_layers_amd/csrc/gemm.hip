@@ -306,16 +306,16 @@ __device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], 
 // 128 bytes in two LDS buffers:
 //   k-step 0: 16 MFMAs, each even one followed by the read of one k-step-1
 //             fragment of stage s into (wb, xb) (order W0, X0..X3, W1..W3).
-//   k-step 1: 16 MFMAs; after the 8th, vmcnt(0) + lgkmcnt(0) + barrier: stage
+//   k-step 1: after its first MFMA, vmcnt(0) + lgkmcnt(0) + barrier: stage
 //             s + 1 (copied during stage s - 1) has landed for every wave,
-//             and no wave reads stage s's buffer any more. Each of the last
-//             8 MFMAs is then followed by the read of a k-step-0 fragment of
-//             stage s + 1 into (wa, xa) and two copies of stage s + 2 into the
-//             buffer stage s used.
+//             and no wave reads stage s's buffer any more. Each MFMA of the
+//             k-step is followed by one copy of stage s + 2 into the buffer
+//             stage s used (16 per thread, so the texture units see an even
+//             stream rather than bursts), each odd one also by the read of a
+//             k-step-0 fragment of stage s + 1 into (wa, xa).
 // In stage 0 of a tile the copies of stage 1 are known to have landed, and
 // the wait skips vmcnt (kWaitVm = false) so that it does not also wait for
 // the previous tile's output stores.
-// The barrier sits mid-stage, after 8 MFMAs that only need registers, and
 // sched_barrier keeps the compiler from regrouping the slots, so copies and
 // reads issue in the shadow of the matrix-core work.
 template <bool kWaitVm>
@@ -343,27 +343,24 @@ __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i 
   for (int t = 0; t < 16; ++t) {
     const int i = t >> 2, j = t & 3;
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wb[i], xb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-    if (t == 7) {
+    if (t == 0) {
       if constexpr (kWaitVm)
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (t >= 8) {
-      const int f = t - 8;
+    if (t < 8)
+      pw.copy_one(lds8_w(cur), k2, t, wave_off);
+    else
+      px.copy_one(lds8_x(cur), k2, t - 8, wave_off);
+    if (t & 1) {
+      const int f = t >> 1;
       if (f == 0)
         wa[0] = frag_w8a8(lds8_w(nxt), row_w, g, 0);
       else if (f < 5)
         xa[f - 1] = frag_w8a8(lds8_x(nxt), row_x + (f - 1) * 32, g, 0);
       else
         wa[f - 4] = frag_w8a8(lds8_w(nxt), row_w + (f - 4) * 32, g, 0);
-      if (f < 4) {
-        pw.copy_one(lds8_w(cur), k2, 2 * f, wave_off);
-        pw.copy_one(lds8_w(cur), k2, 2 * f + 1, wave_off);
-      } else {
-        px.copy_one(lds8_x(cur), k2, 2 * (f - 4), wave_off);
-        px.copy_one(lds8_x(cur), k2, 2 * (f - 4) + 1, wave_off);
-      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
