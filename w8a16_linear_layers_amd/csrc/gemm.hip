@@ -303,21 +303,23 @@ __device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], 
 }
 
 // Steady-state stage s (fragments of its k-step 0 in (wa, xa)); K stages of
-// 128 bytes in two LDS buffers:
-//   k-step 0: 16 MFMAs, each even one followed by the read of one k-step-1
-//             fragment of stage s into (wb, xb) (order W0, X0..X3, W1..W3).
-//   k-step 1: after its first MFMA, vmcnt(0) + lgkmcnt(0) + barrier: stage
-//             s + 1 (copied during stage s - 1) has landed for every wave,
-//             and no wave reads stage s's buffer any more. Each MFMA of the
-//             k-step is followed by one copy of stage s + 2 into the buffer
-//             stage s used (16 per thread, so the texture units see an even
-//             stream rather than bursts), each odd one also by the read of a
-//             k-step-0 fragment of stage s + 1 into (wa, xa).
-// In stage 0 of a tile the copies of stage 1 are known to have landed, and
-// the wait skips vmcnt (kWaitVm = false) so that it does not also wait for
-// the previous tile's output stores.
-// sched_barrier keeps the compiler from regrouping the slots, so copies and
-// reads issue in the shadow of the matrix-core work.
+// 128 bytes in two LDS buffers. Each of the 32 MFMAs is followed by at most
+// one kind of memory work, so the texture path and the LDS see an even
+// stream:
+//   k-step 0, MFMAs 0-7 : read the k-step-1 fragments of stage s into
+//                         (wb, xb), one per MFMA (order W0, X0..X3, W1..W3);
+//   after MFMA 8        : lgkmcnt(0) + barrier: no wave reads stage s's
+//                         buffer any more;
+//   MFMAs 8-15, k-step 1 MFMAs 0-7: one copy of stage s + 2 into that buffer
+//                         each (weight chunks, then activation chunks);
+//   after k-step 1 MFMA 8: vmcnt(16) + barrier: stage s + 1, copied during
+//                         stage s - 1 (older than the 16 copies just issued),
+//                         has landed for every wave;
+//   k-step 1 MFMAs 8-15 : read the k-step-0 fragments of stage s + 1 into
+//                         (wa, xa).
+// In stage 0 of a tile the copies of stage 1 are known to have landed
+// (kWaitVm = false), so that wait need not cover the previous tile's
+// output stores. sched_barrier keeps the compiler from regrouping slots.
 template <bool kWaitVm>
 __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i (&xa)[4], v8i (&wb)[4], v8i (&xb)[4],
                                            const CopyPlan<8>& pw, const CopyPlan<8>& px, int s, int row_w, int row_x,
@@ -328,14 +330,17 @@ __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i 
   for (int t = 0; t < 16; ++t) {
     const int i = t >> 2, j = t & 3;
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[i], xa[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-    if ((t & 1) == 0) {
-      const int f = t >> 1;
+    if (t < 8) {
+      const int f = t;
       if (f == 0)
         wb[0] = frag_w8a8(lds8_w(cur), row_w, g, 1);
       else if (f < 5)
         xb[f - 1] = frag_w8a8(lds8_x(cur), row_x + (f - 1) * 32, g, 1);
       else
         wb[f - 4] = frag_w8a8(lds8_w(cur), row_w + (f - 4) * 32, g, 1);
+    } else {
+      if (t == 8) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage s's buffer is free
+      pw.copy_one(lds8_w(cur), k2, t - 8, wave_off);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -343,18 +348,17 @@ __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i 
   for (int t = 0; t < 16; ++t) {
     const int i = t >> 2, j = t & 3;
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wb[i], xb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-    if (t == 0) {
-      if constexpr (kWaitVm)
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    if (t < 8)
-      pw.copy_one(lds8_w(cur), k2, t, wave_off);
-    else
-      px.copy_one(lds8_x(cur), k2, t - 8, wave_off);
-    if (t & 1) {
-      const int f = t >> 1;
+    if (t < 8) {
+      px.copy_one(lds8_x(cur), k2, t, wave_off);
+    } else {
+      if (t == 8) {
+        // stage s + 1 has landed for every wave (its copies are older than the 16 of stage s + 2)
+        if constexpr (kWaitVm)
+          asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        else
+          asm volatile("s_barrier" ::: "memory");
+      }
+      const int f = t - 8;
       if (f == 0)
         wa[0] = frag_w8a8(lds8_w(nxt), row_w, g, 0);
       else if (f < 5)
