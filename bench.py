@@ -16,6 +16,7 @@ In the same run, on the same resident inputs:
               both modes, quantize and SwiGLU (GB/s,
               input/output buffers rotated over > 512 MB so the 256 MB
               last-level cache cannot serve repeats), the gated-MLP GEMMs,
+              the gate/up + SwiGLU step split and fused,
               the 1024- and 8192-row projections, the step policy, and the
               8-step denoising schedule over 4 blocks (config 5)
   * roofline  the grouped W8A8 GEMM launch against the dense FP8 matrix-core
@@ -41,7 +42,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import w8a16_linear_layers_amd as fp8lin  # noqa: E402
-from workloads import config2, config3, normal_bf16  # noqa: E402
+from workloads import config2, config3, config4, normal_bf16  # noqa: E402
 
 METRIC = "W8A8 FP8 GEMM TFLOP/s (% FP8 MFMA peak) at M=16384,K=N=4096; W8A16 TFLOP/s"
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix-core peak
@@ -347,6 +348,38 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     rows["gate_or_up_8192x16384x4096"] = {"w8a8_tflops": round(f_gu / tg8 / 1e9, 1), "w8a16_tflops": round(f_gu / tg16 / 1e9, 1)}
     rows["down_8192x4096x16384"] = {"w8a8_tflops": round(f_gu / td8 / 1e9, 1), "w8a16_tflops": round(f_gu / td16 / 1e9, 1)}
     del gs, o8, o16, y_gu, y_dn
+
+    # gated MLP gate/up + SwiGLU at config 4 (x [8192, 4096], I = 16384): the split path (one quantize,
+    # one grouped gate/up launch writing two bf16 [8192, 16384] tensors, the two-input SwiGLU reading them)
+    # against the fused launch (one quantize, one GEMM whose epilogue emits the E4M3 h directly)
+    c4 = config4()
+    x4 = c4.x.to(dev)
+    qg4 = fp8lin.fp8lin_quantize_static(c4.w_gate.to(dev), c4.s_gate)
+    qu4 = fp8lin.fp8lin_quantize_static(c4.w_up.to(dev), c4.s_up)
+    qx4 = torch.empty((mi, K), dtype=torch.uint8, device=dev)
+    g4, u4 = (torch.empty((mi, inter), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    h4 = torch.empty((mi, inter), dtype=torch.uint8, device=dev)
+    h4f = torch.empty_like(h4)
+
+    def mlp_split():
+        fp8lin.fp8lin_qkv_shared(x4, [qg4, qu4], [c4.s_gate, c4.s_up], [c4.input_scale] * 2, fp8lin.MODE_W8A8,
+                                 outs=[g4, u4], workspace=qx4)
+        fp8lin.fp8lin_swiglu_2in_quant(g4, u4, c4.s_h, fp8lin.DT_E4M3, out=h4)
+
+    def mlp_fused():
+        fp8lin.fp8lin_quantize_static(x4, c4.input_scale, out=qx4)
+        fp8lin.fp8lin_gate_up_swiglu_w8a8(qx4, qg4, qu4, c4.input_scale, c4.s_gate, c4.s_up, c4.s_h, out=h4f)
+
+    t_split = timed(mlp_split, reps)
+    t_fused = timed(mlp_fused, reps)
+    torch.cuda.synchronize()
+    f_mlp = 2 * f_gu
+    rows["gated_mlp_gate_up_swiglu_8192x4096x16384"] = {
+        "split_ms": round(t_split, 4), "fused_ms": round(t_fused, 4), "speedup": round(t_split / t_fused, 3),
+        "fused_tflops": round(f_mlp / t_fused / 1e9, 1), "split_tflops": round(f_mlp / t_split / 1e9, 1),
+        "fused_equals_split": bool(torch.equal(h4, h4f)),
+    }
+    del x4, qg4, qu4, qx4, g4, u4, h4, h4f, c4
 
     # 4096 -> 4096 projection at 1024 and 8192 rows
     c2 = config2()

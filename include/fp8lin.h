@@ -216,6 +216,30 @@ int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void
                                 int64_t rows, int64_t cols, float out_scale, hipStream_t stream);
 
 /*
+ * Gate/up projections and SwiGLU fused in one GEMM launch (W8A8): the split
+ * gated MLP of [TRT-17476] "What changed" (gate and up on one shared FP8
+ * activation, then silu(G) * U quantized for the down projection) without
+ * the two bf16 [M, I] intermediates. For every element
+ *   g = bf16_RNE( (sum_k dec(qx[m,k]) dec(qw_gate[n,k])) * (input_scale * gate_scale) )
+ *   u = bf16_RNE( (sum_k dec(qx[m,k]) dec(qw_up[n,k]))   * (input_scale * up_scale) )
+ *   h[m, n] = E4M3_RNE(clamp(silu(g) * u / out_scale, +-448))
+ * i.e. exactly fp8lin_gemm_w8a8 for gate and for up followed by
+ * fp8lin_swiglu_2in_quant(E4M3, out_scale) on their outputs; the bf16
+ * rounding of g and u is kept so the result equals that unfused path bit
+ * for bit.
+ *   qx              device, E4M3 [M, K], contiguous (the activation quantized
+ *                   once with input_scale)
+ *   qw_gate, qw_up  device, E4M3 [I, K], contiguous
+ *   h               device, E4M3 [M, I], contiguous
+ *   I               multiple of 16 (else FP8LIN_ELAYOUT), < 2^22
+ *   out_scale       the down projection's static input scale
+ * Launch counted as FP8LIN_KERNEL_GATE_UP_SWIGLU.
+ */
+int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const void* qw_gate, const void* qw_up,
+                                   int64_t I, float input_scale, float gate_scale, float up_scale, float out_scale,
+                                   void* h_e4m3, hipStream_t stream);
+
+/*
  * Fail-closed check of a parsed policy ([TRT-17476] "Denoising-step
  * activation precision": unknown or missing fields, schema_version other than
  * 1 and any other type / index_space / default_mode / overlap are refused).
@@ -246,7 +270,8 @@ enum {
   FP8LIN_KERNEL_GEMM_W8A8 = 1,
   FP8LIN_KERNEL_GEMM_W8A16 = 2,
   FP8LIN_KERNEL_SWIGLU = 3,
-  FP8LIN_KERNEL_KINDS = 4
+  FP8LIN_KERNEL_GATE_UP_SWIGLU = 4,
+  FP8LIN_KERNEL_KINDS = 5
 };
 
 /* Number of kernels of `kind` this process has enqueued through the library

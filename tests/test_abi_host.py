@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -44,7 +44,7 @@ def test_strerror_covers_every_status():
 
 def test_launch_count_rejects_unknown_kind():
     assert fp8lin.fp8lin_launch_count(-1) == -1
-    assert fp8lin.fp8lin_launch_count(4) == -1
+    assert fp8lin.fp8lin_launch_count(5) == -1
     assert fp8lin.fp8lin_launch_count(0) >= 0
 
 
@@ -207,6 +207,29 @@ def test_gemm_w8a8_group_validation(lib):
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
     assert grp(lib, M=0) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before
+
+
+def gus(lib, qx=FAKE, M=4, K=64, wg=FAKE, wu=FAKE, inter=64, si=0.01, sg=0.001, su=0.001, sh=0.02, h=FAKE):
+    return lib.fp8lin_gate_up_swiglu_w8a8(qx, M, K, wg, wu, inter, si, sg, su, sh, h, None)
+
+
+def test_gate_up_swiglu_validation(lib):
+    assert gus(lib, qx=None) == fp8lin.EINVAL
+    assert gus(lib, h=None) == fp8lin.EINVAL
+    assert gus(lib, wu=None) == fp8lin.EINVAL
+    assert gus(lib, inter=0) == fp8lin.EINVAL
+    assert gus(lib, inter=40) == fp8lin.ELAYOUT  # I must be a multiple of 16
+    assert gus(lib, K=40) == fp8lin.ELAYOUT
+    assert gus(lib, wg=FAKE + 8) == fp8lin.ELAYOUT
+    assert gus(lib, h=FAKE + 4) == fp8lin.ELAYOUT
+    assert gus(lib, sh=0.0) == fp8lin.ESCALE
+    assert gus(lib, su=float("nan")) == fp8lin.ESCALE
+    assert gus(lib, si=2.0**-100, sg=2.0**-100) == fp8lin.ESCALE  # alpha underflows
+    assert gus(lib, inter=1 << 22) == fp8lin.EUNSUPPORTED
+    assert gus(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU)
+    assert gus(lib, M=0, qx=None, h=None) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU) == before
 
 
 def qkv(lib, scales_in=(0.01, 0.01, 0.01), n=(64, 64, 64), mode=0, ws=FAKE, nproj=3):

@@ -194,3 +194,47 @@ def test_swiglu_rejects_non_contiguous(gpu):
     g = torch.zeros((64, 32), dtype=torch.bfloat16, device=gpu).t()
     with pytest.raises(ValueError):
         fp8lin.fp8lin_swiglu_2in_quant(g, g, 1.0)
+
+
+# ---------------------------------------------------------------- fused gate/up + SwiGLU
+
+
+@pytest.mark.parametrize(
+    "m,k,inter",
+    [(300, 528, 272), (256, 256, 128), (77, 64, 16), (513, 1040, 400), (8192, 4096, 16384)],
+)
+def test_gate_up_swiglu_fused(gpu, m, k, inter):
+    """One launch equals gemm_w8a8(gate), gemm_w8a8(up), swiglu_2in_quant bit for bit, and the oracle's
+    SwiGLU codes of those bf16 outputs (midpoint cases aside)."""
+    announce("gate_up_swiglu fused m=%d k=%d inter=%d" % (m, k, inter))
+    case = config4(m=m, hidden=k, inter=inter, cal_rows=64)
+    qg = fp8lin.fp8lin_quantize_static(case.w_gate.to(gpu), case.s_gate)
+    qu = fp8lin.fp8lin_quantize_static(case.w_up.to(gpu), case.s_up)
+    qx = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    c0 = [fp8lin.fp8lin_launch_count(i) for i in range(5)]
+    h = fp8lin.fp8lin_gate_up_swiglu_w8a8(qx, qg, qu, case.input_scale, case.s_gate, case.s_up, case.s_h)
+    c1 = [fp8lin.fp8lin_launch_count(i) - c for i, c in enumerate(c0)]
+    assert c1 == [0, 0, 0, 0, 1]  # one launch, no GEMM or SwiGLU kernel of its own
+    g = fp8lin.fp8lin_gemm_w8a8(qx, qg, case.input_scale, case.s_gate)
+    u = fp8lin.fp8lin_gemm_w8a8(qx, qu, case.input_scale, case.s_up)
+    ref = fp8lin.fp8lin_swiglu_2in_quant(g, u, case.s_h, fp8lin.DT_E4M3)
+    torch.cuda.synchronize()
+    assert h.shape == (m, inter) and h.dtype == torch.uint8
+    mism = int((h != ref).sum())
+    assert mism == 0, "%d codes differ from the unfused path" % mism
+    rows = sample_rows(m, 64, 21) if m > 1024 else np.arange(m)
+    near = check_swiglu_codes(g.cpu()[rows], u.cpu()[rows], case.s_h, u8(h)[rows])
+    print("codes at a rounding midpoint: %d" % near)
+
+
+def test_gate_up_swiglu_writes_only_its_output(gpu):
+    announce("gate_up_swiglu guard bytes")
+    case = config4(m=40, hidden=128, inter=48, cal_rows=16)
+    qg = fp8lin.fp8lin_quantize_static(case.w_gate.to(gpu), case.s_gate)
+    qu = fp8lin.fp8lin_quantize_static(case.w_up.to(gpu), case.s_up)
+    qx = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    buf = torch.full((40 * 48 + 256,), 0xA5, dtype=torch.uint8, device=gpu)
+    out = buf[: 40 * 48].view(40, 48)
+    fp8lin.fp8lin_gate_up_swiglu_w8a8(qx, qg, qu, case.input_scale, case.s_gate, case.s_up, case.s_h, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[40 * 48:] == 0xA5)

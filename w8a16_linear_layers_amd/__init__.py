@@ -32,6 +32,7 @@ __all__ = [
     "fp8lin_gemm_w8a8_group",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
+    "fp8lin_gate_up_swiglu_w8a8",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -40,12 +41,13 @@ __all__ = [
     "KERNEL_GEMM_W8A8",
     "KERNEL_GEMM_W8A16",
     "KERNEL_SWIGLU",
+    "KERNEL_GATE_UP_SWIGLU",
 ]
 
 MODE_W8A8, MODE_W8A16 = 0, 1
 DT_BF16, DT_E4M3 = 0, 1
 TOWER_GENERATION, TOWER_REASONER = 0, 1
-KERNEL_QUANTIZE, KERNEL_GEMM_W8A8, KERNEL_GEMM_W8A16, KERNEL_SWIGLU = 0, 1, 2, 3
+KERNEL_QUANTIZE, KERNEL_GEMM_W8A8, KERNEL_GEMM_W8A16, KERNEL_SWIGLU, KERNEL_GATE_UP_SWIGLU = 0, 1, 2, 3, 4
 
 OK, EINVAL, ELAYOUT, EDTYPE, ESCALE, EPOLICY, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
 
@@ -59,6 +61,7 @@ EXPORTS = (
     "fp8lin_gemm_w8a8_group",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
+    "fp8lin_gate_up_swiglu_w8a8",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -116,6 +119,7 @@ def load_library():
         ctypes.POINTER(f32), ctypes.POINTER(vp), vp, i32, vp,
     ]
     lib.fp8lin_swiglu_2in_quant.argtypes = [vp, vp, vp, i32, i64, i64, f32, vp]
+    lib.fp8lin_gate_up_swiglu_w8a8.argtypes = [vp, i64, i64, vp, vp, i64, f32, f32, f32, f32, vp, vp]
     lib.fp8lin_policy_validate.argtypes = [ctypes.POINTER(Policy)]
     lib.fp8lin_step_policy.argtypes = [ctypes.POINTER(Policy), i32, i32, i32, ctypes.POINTER(i32)]
     lib.fp8lin_strerror.argtypes = [i32]
@@ -274,6 +278,27 @@ def fp8lin_swiglu_2in_quant(gate, up, out_scale=1.0, out_dtype=DT_E4M3, out=None
             _ptr(gate), _ptr(up), _ptr(out), int(out_dtype), rows, cols, float(out_scale), _stream(stream)
         ),
         "fp8lin_swiglu_2in_quant",
+    )
+    return out
+
+
+def fp8lin_gate_up_swiglu_w8a8(qx, qw_gate, qw_up, input_scale, gate_scale, up_scale, out_scale, out=None,
+                               stream=None):
+    """h = E4M3(silu(g) * u / out_scale) with g, u the bf16 W8A8 gate/up outputs, in one launch (uint8 codes)."""
+    if qx.dtype != torch.uint8 or qw_gate.dtype != torch.uint8 or qw_up.dtype != torch.uint8:
+        raise TypeError("qx and the weights must hold E4M3 codes as torch.uint8")
+    if qw_gate.shape != qw_up.shape:
+        raise ValueError("gate and up weights must have the same shape")
+    m, k = _rows(qx)
+    inter = qw_gate.shape[0]
+    if out is None:
+        out = torch.empty(tuple(qx.shape[:-1]) + (inter,), dtype=torch.uint8, device=qx.device)
+    _check(
+        load_library().fp8lin_gate_up_swiglu_w8a8(
+            _ptr(qx), m, k, _ptr(qw_gate), _ptr(qw_up), inter, float(input_scale), float(gate_scale),
+            float(up_scale), float(out_scale), _ptr(out), _stream(stream)
+        ),
+        "fp8lin_gate_up_swiglu_w8a8",
     )
     return out
 

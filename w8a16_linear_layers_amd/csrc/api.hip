@@ -213,6 +213,42 @@ int32_t fp8lin_gemm_w8a8_group(const void* qx, int64_t M, int64_t K, int32_t npr
   return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
 }
 
+int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const void* qw_gate, const void* qw_up,
+                                   int64_t I, float input_scale, float gate_scale, float up_scale, float out_scale,
+                                   void* h_e4m3, hipStream_t stream) {
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && (qx == nullptr || h_e4m3 == nullptr))) return FP8LIN_EINVAL;
+  if (qw_gate == nullptr || qw_up == nullptr || I <= 0) return FP8LIN_EINVAL;
+  if (I >= kMaxGemmDim) return FP8LIN_EUNSUPPORTED;
+  if (I % 16 != 0) return FP8LIN_ELAYOUT;
+  if (!aligned16(qx) || !aligned16(qw_gate) || !aligned16(qw_up) || !aligned16(h_e4m3)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(input_scale) || !scale_ok(gate_scale) || !scale_ok(up_scale) || !scale_ok(out_scale))
+    return FP8LIN_ESCALE;
+  const float ag = input_scale * gate_scale, au = input_scale * up_scale;
+  if (!std::isfinite(ag) || ag == 0.0f || !std::isfinite(au) || au == 0.0f) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  GemmArgs a{};
+  a.x = qx;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = 1;
+  a.out_rs = 1.0f / out_scale;
+  a.g[0].w = static_cast<const uint8_t*>(qw_gate);
+  a.g[0].y = h_e4m3;
+  a.g[0].n = (int32_t)I;
+  a.g[0].ldy = (int32_t)I;
+  a.g[0].alpha = ag;
+  a.g[1].w = static_cast<const uint8_t*>(qw_up);
+  a.g[1].n = (int32_t)I;
+  a.g[1].alpha = au;
+  const int64_t tiles = ((M + fp8lin::kTileM - 1) / fp8lin::kTileM) * ((I + fp8lin::kTileN / 2 - 1) / (fp8lin::kTileN / 2));
+  if (tiles >= (int64_t(1) << 31)) return FP8LIN_EUNSUPPORTED;
+  fp8lin::gate_up_plan(a);
+  count_launch(FP8LIN_KERNEL_GATE_UP_SWIGLU);
+  return hip_status(fp8lin::launch_gate_up_swiglu(a, stream));
+}
+
 int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void* out, int32_t out_dtype, int64_t rows,
                                 int64_t cols, float out_scale, hipStream_t stream) {
   if (out_dtype != FP8LIN_DT_E4M3 && out_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;

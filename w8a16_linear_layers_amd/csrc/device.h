@@ -1,5 +1,6 @@
-// Device helpers shared by the elementwise kernels: bf16 unpacking and the
-// float -> OCP E4M3 conversion with saturation and round-to-nearest-even.
+// Device helpers shared by the kernels: bf16 unpacking, the float -> OCP
+// E4M3 conversion with saturation and round-to-nearest-even, the static
+// quantization rule and the SwiGLU element rule.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,6 +86,26 @@ __device__ __forceinline__ uint32_t quant_one_exact(uint32_t bits, float s, floa
 
 __device__ __forceinline__ uint32_t quant_word_exact(uint32_t w, float s, float r, bool exact_ok) {
   return quant_one_exact(w & 0xffffu, s, r, exact_ok) | (quant_one_exact(w >> 16, s, r, exact_ok) << 8);
+}
+
+// SwiGLU element rule ([TRT-17476] "What changed": silu(g) * u in float32
+// from the two bf16 inputs, emitted as E4M3 with the down projection's
+// static input scale). silu(g) * u = g * u / (1 + exp(-g)): expf is the
+// accurate (about 1 ulp) libm exponential, so h stays within a few float32
+// ulp of the exact value for every finite input; a very negative gate gives
+// exp(-g) = inf and h = -0 or 0, a large gate gives g * u. Shared by the
+// two-input SwiGLU kernel and the fused gate/up epilogue, so both produce
+// the same codes from the same bf16 inputs.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = expf(-g);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// E4M3 code of h * rs (rs = 1 / s_h); NaN keeps its sign as S.1111.111.
+__device__ __forceinline__ uint32_t swiglu_code(float h, float rs) {
+  const float t = h * rs;
+  if (__builtin_isnan(t)) return 0x7fu | ((__float_as_uint(t) >> 24) & 0x80u);
+  return e4m3_code(clamp448(t));
 }
 
 }  // namespace fp8lin

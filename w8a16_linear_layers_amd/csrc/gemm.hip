@@ -23,6 +23,7 @@
 //   * Tiles of all groups form one index space, remapped so that the
 //     workgroups dispatched to one XCD (ids congruent mod 8) take a
 //     contiguous run of tiles, rasterized in bands of 8 M-tiles for L2 reuse.
+#include "device.h"
 #include "internal.h"
 
 namespace fp8lin {
@@ -44,8 +45,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -133,32 +132,57 @@ __device__ __forceinline__ void wait_vmem_and_barrier() {
 // chunks per row (8: 128-byte rows, 4: 64-byte rows). Chunk position
 // p = j * 256 + tid of physical row P = p / kChunks holds logical chunk
 // (p % kChunks) ^ swizzle(r) of logical row r (= P for 128-byte rows,
-// row64(P) for 64-byte rows). voff[j] is that chunk's byte offset inside the
-// tile's resource at K = 0; a stage's K offset travels in the scalar offset.
-// The swizzles depend only on row bits below 5, which j does not change, so
-// a thread copies the same logical chunk of every row it serves (kbyte).
+// row64(P) for 64-byte rows). Rows 0-127 and 128-255 come from two buffer
+// resources (the two halves of one matrix, or two matrices such as the gate
+// and up weights), and chunk j lies in the upper half iff j >= kChunks / 2.
+// voff[j] is the chunk's byte offset inside its resource at K = 0; a stage's
+// K offset travels in the scalar offset. The swizzles depend only on row
+// bits below 5, which j does not change, so a thread copies the same
+// logical chunk of every row it serves (kbyte).
 template <int kChunks>
 struct CopyPlan {
-  i32x4 rsrc;
+  i32x4 lo, hi;
   uint32_t voff[kChunks];
   int kbyte;  // first K byte of the thread's chunk within a stage row
 
-  __device__ __forceinline__ void init(const uint8_t* src, int row0, int rows, int64_t ld_bytes, int tid) {
-    const int valid = rows < 256 ? rows : 256;
-    rsrc = make_rsrc(src + (int64_t)row0 * ld_bytes, (uint32_t)(valid * ld_bytes));
+  // Rows [0, 128) from src_lo (rows_lo of them valid), rows [128, 256) from
+  // src_hi (rows_hi valid); rows beyond the valid ones read as zero.
+  __device__ __forceinline__ void init2(const uint8_t* src_lo, int rows_lo, const uint8_t* src_hi, int rows_hi,
+                                        int64_t ld_bytes, int tid) {
+    // readfirstlane: the (uniform) clamps may be computed in vector registers,
+    // and the resources must stay scalar for the copies
+    const int n_lo = __builtin_amdgcn_readfirstlane(max(0, min(rows_lo, 128)));
+    const int n_hi = __builtin_amdgcn_readfirstlane(max(0, min(rows_hi, 128)));
+    lo = make_rsrc(src_lo, (uint32_t)(n_lo * ld_bytes));
+    hi = make_rsrc(src_hi, (uint32_t)(n_hi * ld_bytes));
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
       const int p = j * kThreads + tid;
       const int r = kChunks == 4 ? row64(p / kChunks) : p / kChunks;
       const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : swz8(r));
-      voff[j] = (uint32_t)(r * ld_bytes) + (uint32_t)c * 16u;
+      voff[j] = (uint32_t)((r & 127) * ld_bytes) + (uint32_t)c * 16u;
       if (j == 0) kbyte = c * 16;
     }
   }
 
+  // Rows [row0, row0 + 256) of one matrix with `rows` valid rows from row0.
+  __device__ __forceinline__ void init(const uint8_t* src, int row0, int rows, int64_t ld_bytes, int tid) {
+    const uint8_t* base = src + (int64_t)row0 * ld_bytes;
+    init2(base, rows, base + 128 * ld_bytes, rows - 128, ld_bytes, tid);
+  }
+
+  // One copy of chunk j with offset v (j is a compile-time constant once the
+  // callers' loops are unrolled, so the resource choice folds away).
+  __device__ __forceinline__ void dma(int j, uint32_t v, uint32_t k0b, uint32_t lds) const {
+    if (j < kChunks / 2)
+      dma16(lo, v, k0b, lds);
+    else
+      dma16(hi, v, k0b, lds);
+  }
+
   // Chunk j of the full stage starting at byte `k0b` of each row.
   __device__ __forceinline__ void copy_one(const uint8_t* lds_tile, uint32_t k0b, int j, uint32_t wave_off) const {
-    dma16(rsrc, voff[j], k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+    dma(j, voff[j], k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
   }
 
   // All chunks of the stage starting at byte `k0b`; chunks at or beyond
@@ -167,7 +191,13 @@ struct CopyPlan {
     const bool beyond = k0b + kbyte >= kb;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j)
-      dma16(rsrc, beyond ? kOutOfRange : voff[j], (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+      dma(j, beyond ? kOutOfRange : voff[j], (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+  }
+
+  // Every later copy reads zeros.
+  __device__ __forceinline__ void exhaust() {
+    lo[2] = 0;
+    hi[2] = 0;
   }
 };
 
@@ -185,6 +215,8 @@ struct TileCoord {
 
 // Logical tile of dispatch slot `slot`: slot b runs on XCD b % 8, and each
 // XCD gets a contiguous run of tiles, rasterized in bands of kBandM M-tiles.
+// Tiles are 256 rows of M by kTN columns of N.
+template <int kTN = kTileN>
 __device__ __forceinline__ TileCoord tile_at(const GemmArgs& a, int slot) {
   const int T = a.total_tiles;
   const int xcd = slot % kXcds, idx = slot / kXcds;
@@ -205,7 +237,7 @@ __device__ __forceinline__ TileCoord tile_at(const GemmArgs& a, int slot) {
   TileCoord c;
   c.group = __builtin_amdgcn_readfirstlane(gi);
   c.m0 = __builtin_amdgcn_readfirstlane((first_m + in_band % band_m) * kTileM);
-  c.n0 = __builtin_amdgcn_readfirstlane((in_band / band_m) * kTileN);
+  c.n0 = __builtin_amdgcn_readfirstlane((in_band / band_m) * kTN);
   return c;
 }
 
@@ -381,12 +413,80 @@ __device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8>& pw, const C
   }
 }
 
+// Fused gate/up + SwiGLU epilogue for rows [32 j, 32 j + 32) of the tile.
+// Waves (wm, 0) hold the gate and (wm, 1) the up projection of the same
+// 128 x 128 block of h. Each wave stages bf16(acc * alpha) of its rows in
+// its 8 KiB area (the layout of epilogue_rows) -- the same bf16 values the
+// separate GEMMs would write -- then, after a barrier, wave (wm, wn)
+// combines rows [16 wn, 16 wn + 16) of the pass: silu(g) * u in float32 and
+// its E4M3 code with rs = 1 / s_h (the two-input SwiGLU rule), 16 codes per
+// lane and row, stored through the h resource of rows m_base..+128 (rows
+// past M and columns past I dropped). A second barrier frees the areas.
+__device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, uint8_t* epi, int wm, int wn,
+                                                float alpha, float rs, __amdgpu_buffer_rsrc_t out, int n_base,
+                                                int I, int lane) {
+  asm volatile("" : "+v"(lane));
+  {
+    uint8_t* stage = epi + (wm * 2 + wn) * kW8A8EpiWave;
+    const int h = lane >> 5;
+    const int m = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = i * 4 + t;
+        u32x2 v;
+        v[0] = bf16x2(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
+        v[1] = bf16x2(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
+        *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const uint8_t* ga = epi + (wm * 2) * kW8A8EpiWave;
+  const uint8_t* ua = ga + kW8A8EpiWave;
+  const int cp = lane & 7;  // columns [16 cp, 16 cp + 16) of the block
+  const int col = n_base + 16 * cp;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * wn + 8 * q + (lane >> 3);  // row within the pass
+    u32x4 gv[2], uv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int off = r * 256 + (((2 * cp + e) ^ (r & 15)) * 16);
+      gv[e] = *reinterpret_cast<const u32x4*>(ga + off);
+      uv[e] = *reinterpret_cast<const u32x4*>(ua + off);
+    }
+    u32x4 codes;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x4& gg = gv[w >> 1];
+      const u32x4& uu = uv[w >> 1];
+      const uint32_t g2a = gg[(w & 1) * 2], g2b = gg[(w & 1) * 2 + 1];
+      const uint32_t u2a = uu[(w & 1) * 2], u2b = uu[(w & 1) * 2 + 1];
+      codes[w] = swiglu_code(silu_mul(bf16_lo(g2a), bf16_lo(u2a)), rs) |
+                 (swiglu_code(silu_mul(bf16_hi(g2a), bf16_hi(u2a)), rs) << 8) |
+                 (swiglu_code(silu_mul(bf16_lo(g2b), bf16_lo(u2b)), rs) << 16) |
+                 (swiglu_code(silu_mul(bf16_hi(g2b), bf16_hi(u2b)), rs) << 24);
+    }
+    const uint32_t o = col < I ? (uint32_t)((32 * j + r) * I + col) : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(codes, out, (int)o, 0, 0);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Persistent W8A8 kernel: one workgroup per CU walks the tiles of dispatch
 // slots blockIdx.x, blockIdx.x + gridDim.x, ... After the last LDS read of
 // a tile the first two stages of the next tile are issued, so their latency
 // overlaps the last k-step; each wave waits for them before it issues the
 // tile's output stores (which go through an LDS area of its own), so the
 // next tile starts without waiting for those stores to complete.
+// kSwiGLU: the fused gate/up + SwiGLU form. A tile is 256 rows of M by 128
+// columns of h; weight rows 0-127 of the tile are the gate rows and 128-255
+// the up rows of those columns (a.g[0]: gate, h output, alpha s_in s_gate;
+// a.g[1]: up, alpha s_in s_up; a.out_rs = 1 / s_h), so the accumulators of
+// waves (wm, 0) and (wm, 1) are g and u of the same block.
+template <bool kSwiGLU>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a8_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -400,11 +500,22 @@ gemm_w8a8_kernel(const GemmArgs a) {
   const int g = lane >> 5;
   uint8_t* epi = lds_mem + kW8A8EpiOffset + wave * kW8A8EpiWave;
 
-  int slot = blockIdx.x;
-  TileCoord tc = tile_at(a, slot);
   CopyPlan<8> pw, px;
-  pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, K, tid);
-  px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, K, tid);
+  auto plan_tile = [&](const TileCoord& t) {
+    if constexpr (kSwiGLU) {
+      const int64_t off = (int64_t)t.n0 * K;
+      const int rows = a.g[0].n - t.n0;
+      pw.init2(a.g[0].w + off, rows, a.g[1].w + off, rows, K, tid);
+    } else {
+      pw.init(a.g[t.group].w, t.n0, a.g[t.group].n - t.n0, K, tid);
+    }
+    px.init(static_cast<const uint8_t*>(a.x), t.m0, a.m - t.m0, K, tid);
+  };
+  constexpr int kTN = kSwiGLU ? kTileN / 2 : kTileN;
+
+  int slot = blockIdx.x;
+  TileCoord tc = tile_at<kTN>(a, slot);
+  plan_tile(tc);
   w8a8_first_stages(pw, px, K, KT, wave_off);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -446,16 +557,27 @@ gemm_w8a8_kernel(const GemmArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int next = slot + (int)gridDim.x;
     if (next < a.total_tiles) {
-      tc = tile_at(a, next);
-      pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, K, tid);
-      px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, K, tid);
+      tc = tile_at<kTN>(a, next);
+      plan_tile(tc);
       w8a8_first_stages(pw, px, K, KT, wave_off);
     }
     w8a8_mma(acc, wb, xb);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's stages 0 and 1
-    const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
+    if constexpr (kSwiGLU) {
+      const int I = grp.n;
+      const int m_base = cur.m0 + wm * 128;
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - m_base, 128)));
+      const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<uint8_t*>(grp.y) + (int64_t)min(m_base, a.m) * I, (short)0, rows * I, 0x00020000);
+      const float alpha = wn ? a.g[1].alpha : a.g[0].alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, epi, grp, out, cur.n0 + wn * 128, lane);
+      for (int j = 0; j < 4; ++j)
+        epilogue_swiglu(acc, j, lds_mem + kW8A8EpiOffset, wm, wn, alpha, a.out_rs, out, cur.n0, I, lane);
+    } else {
+      const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, epi, grp, out, cur.n0 + wn * 128, lane);
+    }
     if (next >= a.total_tiles) break;
     slot = next;
   }
@@ -507,11 +629,11 @@ struct W16Copier {
   __device__ __forceinline__ void issue(int c, int buf, int K, uint32_t wave_off) const {
     if (c < 4) {
       const int k0b = k * 64;
-      dma16(pw.rsrc, k0b + pw.kbyte >= K ? kOutOfRange : pw.voff[c], (uint32_t)k0b,
+      pw.dma(c, k0b + pw.kbyte >= K ? kOutOfRange : pw.voff[c], (uint32_t)k0b,
             lds_addr(lds16_w(buf)) + c * kThreads * 16 + wave_off);
     } else {
       const int k0b = k * 128;
-      dma16(px.rsrc, k0b + px.kbyte >= 2 * K ? kOutOfRange : px.voff[c - 4], (uint32_t)k0b,
+      px.dma(c - 4, k0b + px.kbyte >= 2 * K ? kOutOfRange : px.voff[c - 4], (uint32_t)k0b,
             lds_addr(lds16_x(buf)) + (c - 4) * kThreads * 16 + wave_off);
     }
   }
@@ -523,8 +645,8 @@ struct W16Copier {
         start_tile(a, next, tid);
       } else {
         k = 0;
-        pw.rsrc[2] = 0;
-        px.rsrc[2] = 0;
+        pw.exhaust();
+        px.exhaust();
       }
     }
   }
@@ -674,7 +796,23 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL(gemm_w8a8_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(gemm_w8a8_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+void gate_up_plan(GemmArgs& a) {
+  a.tiles_m = (a.m + kTileM - 1) / kTileM;
+  a.g[0].tiles_n = (a.g[0].n + kTileN / 2 - 1) / (kTileN / 2);
+  a.g[0].tile_begin = 0;
+  a.total_tiles = a.tiles_m * a.g[0].tiles_n;
+}
+
+hipError_t launch_gate_up_swiglu(const GemmArgs& a, hipStream_t s) {
+  static const int cus = cu_count();
+  int grid = cus - cus % kXcds;
+  if (grid <= 0) grid = kXcds;
+  if (grid > a.total_tiles) grid = a.total_tiles;
+  hipLaunchKernelGGL(gemm_w8a8_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

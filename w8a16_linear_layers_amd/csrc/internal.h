@@ -33,16 +33,21 @@ struct GemmArgs {
   int32_t tiles_m;
   int32_t ngroups;
   int32_t total_tiles;
-  int32_t pad_;
+  float out_rs;   // fused gate/up + SwiGLU: 1 / s_h (the down projection's input scale)
   GemmGroup g[kMaxGroups];
 };
 
 // Fills tile_begin / tiles_n / tiles_m / total_tiles from m, n of each group.
 void gemm_plan(GemmArgs& a);
 
+// Tile plan of the fused gate/up + SwiGLU GEMM (ngroups = 1; g[0] = gate with
+// the h output, n = I; g[1] = up): tiles of 256 rows by 128 columns of h.
+void gate_up_plan(GemmArgs& a);
+
 hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipStream_t s);
 hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gate_up_swiglu(const GemmArgs& a, hipStream_t s);
 hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, int64_t n, float scale,
                          hipStream_t s);
 

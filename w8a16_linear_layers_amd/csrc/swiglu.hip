@@ -17,21 +17,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;
 
-// silu(g) * u = g * u / (1 + exp(-g)) in float32. expf is the accurate
-// (about 1 ulp) libm exponential, so h stays within a few float32 ulp of
-// the exact value for every finite input; a very negative gate gives
-// exp(-g) = inf and h = -0 or 0, a large gate gives g * u.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = expf(-g);
-  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-__device__ __forceinline__ uint32_t code_of(float h, float rs) {
-  const float t = h * rs;
-  if (__builtin_isnan(t)) return 0x7fu | ((__float_as_uint(t) >> 24) & 0x80u);
-  return e4m3_code(clamp448(t));
-}
-
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   const __bf16 lo = (__bf16)a;
   const __bf16 hi = (__bf16)b;
@@ -48,8 +33,10 @@ __device__ __forceinline__ void swiglu8(const u32x4 gv, const u32x4 uv, void* ou
   }
   if constexpr (kFp8Out) {
     u32x2 o;
-    o.x = code_of(h[0], rs) | (code_of(h[1], rs) << 8) | (code_of(h[2], rs) << 16) | (code_of(h[3], rs) << 24);
-    o.y = code_of(h[4], rs) | (code_of(h[5], rs) << 8) | (code_of(h[6], rs) << 16) | (code_of(h[7], rs) << 24);
+    o.x = swiglu_code(h[0], rs) | (swiglu_code(h[1], rs) << 8) | (swiglu_code(h[2], rs) << 16) |
+          (swiglu_code(h[3], rs) << 24);
+    o.y = swiglu_code(h[4], rs) | (swiglu_code(h[5], rs) << 8) | (swiglu_code(h[6], rs) << 16) |
+          (swiglu_code(h[7], rs) << 24);
     __builtin_nontemporal_store(o, static_cast<u32x2*>(out) + i);
   } else {
     u32x4 o;
