@@ -683,8 +683,17 @@ __device__ __forceinline__ void w16_read(W16Half& f, int r, int b, int h, const 
     f.x[r - 4] = lds_chunk(lds16_x(b), ad.x[h][(r - 4) & 1] + ((r - 4) >> 1) * 4096);
 }
 
-// Half stage on set f: 32 MFMAs (two k-steps of 16), interleaved with up to
-// one LDS read into set `nf` and one copy per slot as `plan` says.
+// Half stage on set f: 32 MFMAs (two k-steps of 16), each followed by at
+// most one memory operation:
+//   first half : the 12 reads of the second half's fragments (set nf) and
+//                copies 0-5 of stage g + 2. Its buffer held stage g - 1,
+//                which every wave finished reading before the previous
+//                stage's barrier (lgkmcnt(0) precedes it).
+//   second half: after MFMA 3, vmcnt + lgkmcnt(0) + barrier: stage g + 1 has
+//                landed for every wave (only the 6 copies just issued, and
+//                after a tile change the previous tile's 32 output stores,
+//                are younger than its copies); then the 12 reads of the
+//                next stage's first-half fragments and copies 6-11.
 __device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W16Half& nf, int nb, int nh,
                                          const W16Addr& ad, W16Copier& cp, int cbuf, int K, uint32_t wave_off,
                                          bool second, bool after_stores) {
@@ -696,27 +705,18 @@ __device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W1
     const v8bf xv = as_v8bf(f.x[2 * j + e]);
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xv, acc[i][j], 0, 0, 0);
     if (!second) {
-      // first half: the 12 reads of the second half's fragments
       if ((t & 1) && t < 24) w16_read(nf, t >> 1, nb, nh, ad);
+      if (t >= 4 && t <= 24 && (t & 3) == 0) cp.issue((t >> 2) - 1, cbuf, K, wave_off);
     } else {
       if (t == 3) {
-        // the next stage has landed for every wave, and every wave is done
-        // with the buffer the copies below refill
-        // (the previous tile's output stores, issued after the copies of
-        // this tile's stage 1, need not have completed)
         if (after_stores)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16EpilogueStores) : "memory");
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2 + kW16EpilogueStores) : "memory");
         else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2) : "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      if (t >= 4 && t < 28) {
-        const int q = t - 4;
-        if (q & 1)
-          cp.issue(q >> 1, cbuf, K, wave_off);
-        else
-          w16_read(nf, q >> 1, nb, nh, ad);
-      }
+      if (t >= 4 && t < 28 && (t & 1) == 0) w16_read(nf, (t - 4) >> 1, nb, nh, ad);
+      if (t >= 5 && t <= 25 && (t & 3) == 1) cp.issue(6 + ((t - 5) >> 2), cbuf, K, wave_off);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
