@@ -73,7 +73,7 @@ hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipSt
   const int64_t nvec = n / 8;
   const int64_t per_block = kThreads * kUnroll;
   int64_t blocks = (nvec + per_block - 1) / per_block;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 65536) blocks = 65536;  // one chunk per workgroup up to 2^26 vectors
   const float r = 1.0f / scale;  // correctly rounded on the host
   int e = 0;
   const bool pow2 = std::frexp(scale, &e) == 0.5f;  // scale = 2^(e-1), and 1/scale is normal

@@ -77,7 +77,7 @@ hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, 
   const int64_t nvec = n / 8;
   const int64_t per_block = kThreads * kUnroll;
   int64_t blocks = (nvec + per_block - 1) / per_block;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > 65536) blocks = 65536;  // one chunk per workgroup up to 2^25 vectors
   const float rs = fp8_out ? 1.0f / scale : 1.0f;
   if (fp8_out) {
     hipLaunchKernelGGL(swiglu_2in_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
