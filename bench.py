@@ -439,12 +439,20 @@ def schedule_cfg5(dev, pol):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    # the same schedule with the fused gate/up + SwiGLU launch on its W8A8 steps
+    e2, e3 = events(2)
+    e2.record()
+    schedule.run_schedule(blocks, pol, steps, lambda st, b: inputs[(st, b)], buf, fused_mlp=True)
+    e3.record()
+    torch.cuda.synchronize()
+    ms_fused = e2.elapsed_time(e3)
     flop_pass = 2.0 * m * hidden * (4 * hidden + 3 * inter)  # QKV + out + gate/up + down of one block
     n8 = sum(1 for t in trace if t == fp8lin.MODE_W8A8)
     flop = flop_pass * nblocks * 2 * steps
     return {
         "ms": round(ms, 2),
         "tflops": round(flop / ms / 1e9, 1),
+        "ms_fused_mlp": round(ms_fused, 2),
         "tflop": round(flop / 1e12, 1),
         "trace": "".join("8" if t == fp8lin.MODE_W8A8 else "6" for t in trace),
         "w8a8_steps": n8,

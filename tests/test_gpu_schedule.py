@@ -101,3 +101,18 @@ def test_block_stack_end_to_end(gpu, setup, mode):
     rel = np.sqrt(np.mean((y - ref) ** 2) / np.mean(ref**2))
     print("%s end-to-end relative rms error vs oracle chain: %.3e" % (mode, rel))
     assert rel < (5e-2 if mode == "W8A8" else 1e-2)
+
+
+def test_fused_mlp_block_stack_equals_split(gpu, setup):
+    """W8A8 blocks with the fused gate/up + SwiGLU launch give the split path's output bit for bit."""
+    announce("block stack fused MLP")
+    _, blocks, buf = setup
+    x = config5_step_input(5, 1, M, HIDDEN).to(gpu)
+    y_split = schedule.stack_forward(blocks, x, fp8lin.MODE_W8A8, buf).clone()
+    c0 = [fp8lin.fp8lin_launch_count(i) for i in range(5)]
+    y_fused = schedule.stack_forward(blocks, x, fp8lin.MODE_W8A8, buf, fused_mlp=True)
+    c1 = [fp8lin.fp8lin_launch_count(i) - c for i, c in enumerate(c0)]
+    torch.cuda.synchronize()
+    assert torch.equal(y_split, y_fused)
+    # per block: 3 quantizations (QKV group, out-proj input, MLP input), 3 GEMMs, 1 fused launch
+    assert c1 == [3 * BLOCKS, 3 * BLOCKS, 0, 0, BLOCKS]

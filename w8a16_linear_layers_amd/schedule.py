@@ -27,6 +27,7 @@ from . import (
     MODE_W8A8,
     MODE_W8A16,
     TOWER_GENERATION,
+    fp8lin_gate_up_swiglu_w8a8,
     fp8lin_gemm_w8a8,
     fp8lin_gemm_w8a16,
     fp8lin_qkv_shared,
@@ -84,17 +85,26 @@ class Buffers:
         self.out = [torch.empty((m, d), dtype=bf, device=dev) for _ in range(2)]
 
 
-def block_forward(w: BlockWeights, x: torch.Tensor, mode: int, buf: Buffers, out: torch.Tensor):
-    """One block in `mode`; writes the block output into `out` (bf16 [m, hidden])."""
+def block_forward(w: BlockWeights, x: torch.Tensor, mode: int, buf: Buffers, out: torch.Tensor, fused_mlp=False):
+    """One block in `mode`; writes the block output into `out` (bf16 [m, hidden]).
+
+    fused_mlp (W8A8 steps): gate/up and the SwiGLU run as one fused launch
+    (fp8lin_gate_up_swiglu_w8a8) on the once-quantized MLP input; the codes
+    equal the split path's bit for bit.
+    """
     m, d = x.shape
     xq = buf.xq.view(-1)[: m * d].view(m, d)
     if mode == MODE_W8A8:
         fp8lin_qkv_shared(x, w.qkv, w.s_qkv, [w.s_in_qkv] * 3, MODE_W8A8, outs=[buf.q, buf.k, buf.v], workspace=xq)
         fp8lin_quantize_static(buf.v, w.s_in_out, out=xq)
         fp8lin_gemm_w8a8(xq, w.out, w.s_in_out, w.s_out, out=buf.o)
-        fp8lin_qkv_shared(buf.o, [w.gate, w.up], [w.s_gate, w.s_up], [w.s_in_mlp] * 2, MODE_W8A8,
-                          outs=[buf.g, buf.u], workspace=xq)
-        fp8lin_swiglu_2in_quant(buf.g, buf.u, w.s_h, DT_E4M3, out=buf.h8)
+        if fused_mlp:
+            fp8lin_quantize_static(buf.o, w.s_in_mlp, out=xq)
+            fp8lin_gate_up_swiglu_w8a8(xq, w.gate, w.up, w.s_in_mlp, w.s_gate, w.s_up, w.s_h, out=buf.h8)
+        else:
+            fp8lin_qkv_shared(buf.o, [w.gate, w.up], [w.s_gate, w.s_up], [w.s_in_mlp] * 2, MODE_W8A8,
+                              outs=[buf.g, buf.u], workspace=xq)
+            fp8lin_swiglu_2in_quant(buf.g, buf.u, w.s_h, DT_E4M3, out=buf.h8)
         fp8lin_gemm_w8a8(buf.h8, w.down, w.s_h, w.s_down, out=out)
     elif mode == MODE_W8A16:
         fp8lin_qkv_shared(x, w.qkv, w.s_qkv, [w.s_in_qkv] * 3, MODE_W8A16, outs=[buf.q, buf.k, buf.v])
@@ -108,15 +118,15 @@ def block_forward(w: BlockWeights, x: torch.Tensor, mode: int, buf: Buffers, out
     return out
 
 
-def stack_forward(blocks: List[BlockWeights], x: torch.Tensor, mode: int, buf: Buffers):
+def stack_forward(blocks: List[BlockWeights], x: torch.Tensor, mode: int, buf: Buffers, fused_mlp=False):
     """All blocks in one mode; returns the buffer holding the last output."""
     h = x
     for b, w in enumerate(blocks):
-        h = block_forward(w, h, mode, buf, buf.out[b % 2])
+        h = block_forward(w, h, mode, buf, buf.out[b % 2], fused_mlp)
     return h
 
 
-def run_schedule(blocks, policy, num_steps, step_inputs, buf, branches=2):
+def run_schedule(blocks, policy, num_steps, step_inputs, buf, branches=2, fused_mlp=False):
     """Run `num_steps` denoising steps of `branches` CFG passes each.
 
     step_inputs(step, branch) returns the bf16 input of that pass. Returns
@@ -127,5 +137,5 @@ def run_schedule(blocks, policy, num_steps, step_inputs, buf, branches=2):
         mode = fp8lin_step_policy(policy, TOWER_GENERATION, step, num_steps)
         trace.append(mode)
         for branch in range(branches):
-            stack_forward(blocks, step_inputs(step, branch), mode, buf)
+            stack_forward(blocks, step_inputs(step, branch), mode, buf, fused_mlp)
     return trace
