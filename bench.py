@@ -370,16 +370,32 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
         fp8lin.fp8lin_quantize_static(x4, c4.input_scale, out=qx4)
         fp8lin.fp8lin_gate_up_swiglu_w8a8(qx4, qg4, qu4, c4.input_scale, c4.s_gate, c4.s_up, c4.s_h, out=h4f)
 
+    h16s = torch.empty((mi, inter), dtype=torch.bfloat16, device=dev)
+    h16f = torch.empty_like(h16s)
+
+    def mlp16_split():
+        fp8lin.fp8lin_qkv_shared(x4, [qg4, qu4], [c4.s_gate, c4.s_up], [c4.input_scale] * 2, fp8lin.MODE_W8A16,
+                                 outs=[g4, u4])
+        fp8lin.fp8lin_swiglu_2in_quant(g4, u4, 1.0, fp8lin.DT_BF16, out=h16s)
+
+    def mlp16_fused():
+        fp8lin.fp8lin_gate_up_swiglu_w8a16(x4, qg4, qu4, c4.s_gate, c4.s_up, out=h16f)
+
     t_split = timed(mlp_split, reps)
     t_fused = timed(mlp_fused, reps)
+    t16_split = timed(mlp16_split, reps)
+    t16_fused = timed(mlp16_fused, reps)
     torch.cuda.synchronize()
     f_mlp = 2 * f_gu
     rows["gated_mlp_gate_up_swiglu_8192x4096x16384"] = {
         "split_ms": round(t_split, 4), "fused_ms": round(t_fused, 4), "speedup": round(t_split / t_fused, 3),
         "fused_tflops": round(f_mlp / t_fused / 1e9, 1), "split_tflops": round(f_mlp / t_split / 1e9, 1),
         "fused_equals_split": bool(torch.equal(h4, h4f)),
+        "w8a16_split_ms": round(t16_split, 4), "w8a16_fused_ms": round(t16_fused, 4),
+        "w8a16_speedup": round(t16_split / t16_fused, 3),
+        "w8a16_fused_equals_split": bool(torch.equal(h16s.view(torch.int16), h16f.view(torch.int16))),
     }
-    del x4, qg4, qu4, qx4, g4, u4, h4, h4f, c4
+    del x4, qg4, qu4, qx4, g4, u4, h4, h4f, h16s, h16f, c4
 
     # 4096 -> 4096 projection at 1024 and 8192 rows
     c2 = config2()

@@ -240,6 +240,25 @@ int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const v
                                    void* h_e4m3, hipStream_t stream);
 
 /*
+ * The same fusion for 16-bit steps (W8A16): gate and up from a bf16
+ * activation and the resident E4M3 weights ([TRT-17476] "Denoising-step
+ * activation precision"), then the two-input SwiGLU with a bf16 output:
+ *   g = bf16_RNE( gate_scale * sum_k x[m,k] dec(qw_gate[n,k]) )
+ *   u = bf16_RNE( up_scale   * sum_k x[m,k] dec(qw_up[n,k]) )
+ *   h[m, n] = bf16_RNE( silu(g) * u )
+ * i.e. exactly fp8lin_gemm_w8a16 for gate and for up followed by
+ * fp8lin_swiglu_2in_quant(FP8LIN_DT_BF16) on their outputs, bit for bit.
+ *   x_dtype  must be FP8LIN_DT_BF16 (FP8LIN_DT_E4M3 -> FP8LIN_EDTYPE)
+ *   x        device, bf16 [M, K], contiguous
+ *   qw_gate, qw_up  device, E4M3 [I, K], contiguous
+ *   h        device, bf16 [M, I], contiguous; I multiple of 16, < 2^22
+ * Launch counted as FP8LIN_KERNEL_GATE_UP_SWIGLU.
+ */
+int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t M, int64_t K, const void* qw_gate,
+                                    const void* qw_up, int64_t I, float gate_scale, float up_scale, void* h_bf16,
+                                    hipStream_t stream);
+
+/*
  * Fail-closed check of a parsed policy ([TRT-17476] "Denoising-step
  * activation precision": unknown or missing fields, schema_version other than
  * 1 and any other type / index_space / default_mode / overlap are refused).

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -229,6 +229,25 @@ def test_gate_up_swiglu_validation(lib):
     assert gus(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU)
     assert gus(lib, M=0, qx=None, h=None) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU) == before
+
+
+def gus16(lib, x=FAKE, dt=0, M=4, K=64, wg=FAKE, wu=FAKE, inter=64, sg=0.001, su=0.001, h=FAKE):
+    return lib.fp8lin_gate_up_swiglu_w8a16(x, dt, M, K, wg, wu, inter, sg, su, h, None)
+
+
+def test_gate_up_swiglu_w8a16_validation(lib):
+    assert gus16(lib, dt=fp8lin.DT_E4M3) == fp8lin.EDTYPE  # the 16-bit step refuses FP8 activations
+    assert gus16(lib, dt=7) == fp8lin.EINVAL
+    assert gus16(lib, x=None) == fp8lin.EINVAL
+    assert gus16(lib, wg=None) == fp8lin.EINVAL
+    assert gus16(lib, inter=24) == fp8lin.ELAYOUT
+    assert gus16(lib, K=40) == fp8lin.ELAYOUT
+    assert gus16(lib, h=FAKE + 2) == fp8lin.ELAYOUT
+    assert gus16(lib, sg=float("inf")) == fp8lin.ESCALE
+    assert gus16(lib, inter=1 << 22) == fp8lin.EUNSUPPORTED
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU)
+    assert gus16(lib, M=0, x=None, h=None) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU) == before
 
 

@@ -238,3 +238,38 @@ def test_gate_up_swiglu_writes_only_its_output(gpu):
     fp8lin.fp8lin_gate_up_swiglu_w8a8(qx, qg, qu, case.input_scale, case.s_gate, case.s_up, case.s_h, out=out)
     torch.cuda.synchronize()
     assert torch.all(buf[40 * 48:] == 0xA5)
+
+
+@pytest.mark.parametrize("m,k,inter", [(300, 528, 272), (77, 64, 16), (513, 1040, 400), (8192, 4096, 16384)])
+def test_gate_up_swiglu_fused_w8a16(gpu, m, k, inter):
+    """16-bit step: one launch equals gemm_w8a16(gate), gemm_w8a16(up), swiglu_2in_quant(bf16) bit for bit,
+    and is within the bf16 rounding of the oracle's SwiGLU of those outputs."""
+    announce("gate_up_swiglu fused w8a16 m=%d k=%d inter=%d" % (m, k, inter))
+    case = config4(m=m, hidden=k, inter=inter, cal_rows=64)
+    qg = fp8lin.fp8lin_quantize_static(case.w_gate.to(gpu), case.s_gate)
+    qu = fp8lin.fp8lin_quantize_static(case.w_up.to(gpu), case.s_up)
+    x = case.x.to(gpu)
+    c0 = [fp8lin.fp8lin_launch_count(i) for i in range(5)]
+    h = fp8lin.fp8lin_gate_up_swiglu_w8a16(x, qg, qu, case.s_gate, case.s_up)
+    c1 = [fp8lin.fp8lin_launch_count(i) - c for i, c in enumerate(c0)]
+    assert c1 == [0, 0, 0, 0, 1]
+    g = fp8lin.fp8lin_gemm_w8a16(x, qg, case.s_gate)
+    u = fp8lin.fp8lin_gemm_w8a16(x, qu, case.s_up)
+    ref = fp8lin.fp8lin_swiglu_2in_quant(g, u, 1.0, fp8lin.DT_BF16)
+    torch.cuda.synchronize()
+    assert h.shape == (m, inter) and h.dtype == torch.bfloat16
+    mism = int((h.view(torch.int16) != ref.view(torch.int16)).sum())
+    assert mism == 0, "%d values differ from the unfused path" % mism
+    rows = sample_rows(m, 64, 23) if m > 1024 else np.arange(m)
+    gr = f32(g.cpu()[rows]).astype(np.float64)
+    ur = f32(u.cpu()[rows]).astype(np.float64)
+    exact = swiglu.swiglu_2in(gr, ur)
+    got = f32(h.cpu()[rows]).astype(np.float64)
+    assert np.all(np.abs(got - exact) <= obf16.ulp(exact))
+
+
+def test_gate_up_swiglu_w8a16_refuses_fp8_activation(gpu):
+    qw = torch.zeros((16, 64), dtype=torch.uint8, device=gpu)
+    with pytest.raises(fp8lin.Fp8LinError) as e:
+        fp8lin.fp8lin_gate_up_swiglu_w8a16(torch.zeros((4, 64), dtype=torch.uint8, device=gpu), qw, qw, 1.0, 1.0)
+    assert e.value.status == fp8lin.EDTYPE

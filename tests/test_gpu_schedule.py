@@ -103,16 +103,21 @@ def test_block_stack_end_to_end(gpu, setup, mode):
     assert rel < (5e-2 if mode == "W8A8" else 1e-2)
 
 
-def test_fused_mlp_block_stack_equals_split(gpu, setup):
-    """W8A8 blocks with the fused gate/up + SwiGLU launch give the split path's output bit for bit."""
-    announce("block stack fused MLP")
+@pytest.mark.parametrize("mode", ["W8A8", "W8A16"])
+def test_fused_mlp_block_stack_equals_split(gpu, setup, mode):
+    """Blocks with the fused gate/up + SwiGLU launch give the split path's output bit for bit."""
+    announce("block stack fused MLP %s" % mode)
     _, blocks, buf = setup
+    md = fp8lin.MODE_W8A8 if mode == "W8A8" else fp8lin.MODE_W8A16
     x = config5_step_input(5, 1, M, HIDDEN).to(gpu)
-    y_split = schedule.stack_forward(blocks, x, fp8lin.MODE_W8A8, buf).clone()
+    y_split = schedule.stack_forward(blocks, x, md, buf).clone()
     c0 = [fp8lin.fp8lin_launch_count(i) for i in range(5)]
-    y_fused = schedule.stack_forward(blocks, x, fp8lin.MODE_W8A8, buf, fused_mlp=True)
+    y_fused = schedule.stack_forward(blocks, x, md, buf, fused_mlp=True)
     c1 = [fp8lin.fp8lin_launch_count(i) - c for i, c in enumerate(c0)]
     torch.cuda.synchronize()
     assert torch.equal(y_split, y_fused)
-    # per block: 3 quantizations (QKV group, out-proj input, MLP input), 3 GEMMs, 1 fused launch
-    assert c1 == [3 * BLOCKS, 3 * BLOCKS, 0, 0, BLOCKS]
+    if mode == "W8A8":
+        # per block: 3 quantizations (QKV group, out-proj input, MLP input), 3 GEMMs, 1 fused launch
+        assert c1 == [3 * BLOCKS, 3 * BLOCKS, 0, 0, BLOCKS]
+    else:
+        assert c1 == [0, 0, 3 * BLOCKS, 0, BLOCKS]

@@ -33,6 +33,7 @@ __all__ = [
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_gate_up_swiglu_w8a8",
+    "fp8lin_gate_up_swiglu_w8a16",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -62,6 +63,7 @@ EXPORTS = (
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_gate_up_swiglu_w8a8",
+    "fp8lin_gate_up_swiglu_w8a16",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -120,6 +122,7 @@ def load_library():
     ]
     lib.fp8lin_swiglu_2in_quant.argtypes = [vp, vp, vp, i32, i64, i64, f32, vp]
     lib.fp8lin_gate_up_swiglu_w8a8.argtypes = [vp, i64, i64, vp, vp, i64, f32, f32, f32, f32, vp, vp]
+    lib.fp8lin_gate_up_swiglu_w8a16.argtypes = [vp, i32, i64, i64, vp, vp, i64, f32, f32, vp, vp]
     lib.fp8lin_policy_validate.argtypes = [ctypes.POINTER(Policy)]
     lib.fp8lin_step_policy.argtypes = [ctypes.POINTER(Policy), i32, i32, i32, ctypes.POINTER(i32)]
     lib.fp8lin_strerror.argtypes = [i32]
@@ -299,6 +302,29 @@ def fp8lin_gate_up_swiglu_w8a8(qx, qw_gate, qw_up, input_scale, gate_scale, up_s
             float(up_scale), float(out_scale), _ptr(out), _stream(stream)
         ),
         "fp8lin_gate_up_swiglu_w8a8",
+    )
+    return out
+
+
+def fp8lin_gate_up_swiglu_w8a16(x, qw_gate, qw_up, gate_scale, up_scale, out=None, stream=None):
+    """h = bf16(silu(g) * u) with g, u the bf16 W8A16 gate/up outputs, in one launch (FP8 input refused)."""
+    dtype = DT_E4M3 if x.dtype in (torch.uint8, torch.float8_e4m3fn) else DT_BF16
+    if dtype == DT_BF16 and x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if qw_gate.dtype != torch.uint8 or qw_up.dtype != torch.uint8:
+        raise TypeError("the weights must hold E4M3 codes as torch.uint8")
+    if qw_gate.shape != qw_up.shape:
+        raise ValueError("gate and up weights must have the same shape")
+    m, k = _rows(x)
+    inter = qw_gate.shape[0]
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (inter,), dtype=torch.bfloat16, device=x.device)
+    _check(
+        load_library().fp8lin_gate_up_swiglu_w8a16(
+            _ptr(x), dtype, m, k, _ptr(qw_gate), _ptr(qw_up), inter, float(gate_scale), float(up_scale), _ptr(out),
+            _stream(stream)
+        ),
+        "fp8lin_gate_up_swiglu_w8a16",
     )
     return out
 

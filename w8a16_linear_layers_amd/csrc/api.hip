@@ -246,7 +246,42 @@ int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const v
   if (tiles >= (int64_t(1) << 31)) return FP8LIN_EUNSUPPORTED;
   fp8lin::gate_up_plan(a);
   count_launch(FP8LIN_KERNEL_GATE_UP_SWIGLU);
-  return hip_status(fp8lin::launch_gate_up_swiglu(a, stream));
+  return hip_status(fp8lin::launch_gate_up_swiglu(a, false, stream));
+}
+
+int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t M, int64_t K, const void* qw_gate,
+                                    const void* qw_up, int64_t I, float gate_scale, float up_scale, void* h_bf16,
+                                    hipStream_t stream) {
+  if (x_dtype == FP8LIN_DT_E4M3) return FP8LIN_EDTYPE;
+  if (x_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && (x_bf16 == nullptr || h_bf16 == nullptr))) return FP8LIN_EINVAL;
+  if (qw_gate == nullptr || qw_up == nullptr || I <= 0) return FP8LIN_EINVAL;
+  if (I >= kMaxGemmDim) return FP8LIN_EUNSUPPORTED;
+  if (I % 16 != 0) return FP8LIN_ELAYOUT;
+  if (!aligned16(x_bf16) || !aligned16(qw_gate) || !aligned16(qw_up) || !aligned16(h_bf16)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(gate_scale) || !scale_ok(up_scale)) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  GemmArgs a{};
+  a.x = x_bf16;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = 1;
+  a.out_rs = 1.0f;
+  a.g[0].w = static_cast<const uint8_t*>(qw_gate);
+  a.g[0].y = h_bf16;
+  a.g[0].n = (int32_t)I;
+  a.g[0].ldy = (int32_t)I;
+  a.g[0].alpha = gate_scale;
+  a.g[1].w = static_cast<const uint8_t*>(qw_up);
+  a.g[1].n = (int32_t)I;
+  a.g[1].alpha = up_scale;
+  const int64_t tiles = ((M + fp8lin::kTileM - 1) / fp8lin::kTileM) * ((I + fp8lin::kTileN / 2 - 1) / (fp8lin::kTileN / 2));
+  if (tiles >= (int64_t(1) << 31)) return FP8LIN_EUNSUPPORTED;
+  fp8lin::gate_up_plan(a);
+  count_launch(FP8LIN_KERNEL_GATE_UP_SWIGLU);
+  return hip_status(fp8lin::launch_gate_up_swiglu(a, true, stream));
 }
 
 int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void* out, int32_t out_dtype, int64_t rows,

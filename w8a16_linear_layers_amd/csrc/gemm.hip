@@ -416,12 +416,14 @@ __device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8>& pw, const C
 // Fused gate/up + SwiGLU epilogue for rows [32 j, 32 j + 32) of the tile.
 // Waves (wm, 0) hold the gate and (wm, 1) the up projection of the same
 // 128 x 128 block of h. Each wave stages bf16(acc * alpha) of its rows in
-// its 8 KiB area (the layout of epilogue_rows) -- the same bf16 values the
-// separate GEMMs would write -- then, after a barrier, wave (wm, wn)
-// combines rows [16 wn, 16 wn + 16) of the pass: silu(g) * u in float32 and
-// its E4M3 code with rs = 1 / s_h (the two-input SwiGLU rule), 16 codes per
-// lane and row, stored through the h resource of rows m_base..+128 (rows
-// past M and columns past I dropped). A second barrier frees the areas.
+// its 8 KiB area `epi + wave * 8 KiB` (the layout of epilogue_rows) -- the
+// same bf16 values the separate GEMMs would write -- then, after a barrier,
+// wave (wm, wn) combines rows [16 wn, 16 wn + 16) of the pass: silu(g) * u
+// in float32 (the two-input SwiGLU rule) and either its E4M3 code with
+// rs = 1 / s_h (kFp8Out) or its bf16 rounding, 16 columns per lane and row,
+// stored through the h resource of rows m_base..+128 (rows past M and
+// columns past I dropped). A second barrier frees the areas.
+template <bool kFp8Out>
 __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, uint8_t* epi, int wm, int wn,
                                                 float alpha, float rs, __amdgpu_buffer_rsrc_t out, int n_base,
                                                 int I, int lane) {
@@ -447,6 +449,7 @@ __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, 
   const uint8_t* ua = ga + kW8A8EpiWave;
   const int cp = lane & 7;  // columns [16 cp, 16 cp + 16) of the block
   const int col = n_base + 16 * cp;
+  constexpr int kBytes = kFp8Out ? 1 : 2;  // per h element
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = 16 * wn + 8 * q + (lane >> 3);  // row within the pass
@@ -457,22 +460,41 @@ __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, 
       gv[e] = *reinterpret_cast<const u32x4*>(ga + off);
       uv[e] = *reinterpret_cast<const u32x4*>(ua + off);
     }
-    u32x4 codes;
+    float hv[16];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x4& gg = gv[w >> 1];
-      const u32x4& uu = uv[w >> 1];
-      const uint32_t g2a = gg[(w & 1) * 2], g2b = gg[(w & 1) * 2 + 1];
-      const uint32_t u2a = uu[(w & 1) * 2], u2b = uu[(w & 1) * 2 + 1];
-      codes[w] = swiglu_code(silu_mul(bf16_lo(g2a), bf16_lo(u2a)), rs) |
-                 (swiglu_code(silu_mul(bf16_hi(g2a), bf16_hi(u2a)), rs) << 8) |
-                 (swiglu_code(silu_mul(bf16_lo(g2b), bf16_lo(u2b)), rs) << 16) |
-                 (swiglu_code(silu_mul(bf16_hi(g2b), bf16_hi(u2b)), rs) << 24);
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t gw = gv[w >> 2][w & 3], uw = uv[w >> 2][w & 3];
+      hv[2 * w] = silu_mul(bf16_lo(gw), bf16_lo(uw));
+      hv[2 * w + 1] = silu_mul(bf16_hi(gw), bf16_hi(uw));
     }
-    const uint32_t o = col < I ? (uint32_t)((32 * j + r) * I + col) : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b128(codes, out, (int)o, 0, 0);
+    const uint32_t o = col < I ? (uint32_t)(((32 * j + r) * I + col) * kBytes) : kOutOfRange;
+    if constexpr (kFp8Out) {
+      u32x4 codes;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        codes[w] = swiglu_code(hv[4 * w], rs) | (swiglu_code(hv[4 * w + 1], rs) << 8) |
+                   (swiglu_code(hv[4 * w + 2], rs) << 16) | (swiglu_code(hv[4 * w + 3], rs) << 24);
+      __builtin_amdgcn_raw_buffer_store_b128(codes, out, (int)o, 0, 0);
+    } else {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lo[w] = bf16x2(hv[2 * w], hv[2 * w + 1]);
+        hi[w] = bf16x2(hv[8 + 2 * w], hv[8 + 2 * w + 1]);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(lo, out, (int)o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(hi, out, (int)(o + 16u), 0, 0);
+    }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Output resource of the fused h: rows [m_base, min(M, m_base + 128)) of an
+// [M, I] tensor of `bytes`-byte elements.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(void* h, int M, int m_base, int I, int bytes) {
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(M - m_base, 128)));
+  return __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(h) + (int64_t)min(m_base, M) * I * bytes, (short)0,
+                                           rows * I * bytes, 0x00020000);
 }
 
 // Persistent W8A8 kernel: one workgroup per CU walks the tiles of dispatch
@@ -565,14 +587,11 @@ gemm_w8a8_kernel(const GemmArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's stages 0 and 1
     if constexpr (kSwiGLU) {
       const int I = grp.n;
-      const int m_base = cur.m0 + wm * 128;
-      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - m_base, 128)));
-      const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
-          static_cast<uint8_t*>(grp.y) + (int64_t)min(m_base, a.m) * I, (short)0, rows * I, 0x00020000);
+      const __amdgpu_buffer_rsrc_t out = h_rsrc(grp.y, a.m, cur.m0 + wm * 128, I, 1);
       const float alpha = wn ? a.g[1].alpha : a.g[0].alpha;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        epilogue_swiglu(acc, j, lds_mem + kW8A8EpiOffset, wm, wn, alpha, a.out_rs, out, cur.n0, I, lane);
+        epilogue_swiglu<true>(acc, j, lds_mem + kW8A8EpiOffset, wm, wn, alpha, a.out_rs, out, cur.n0, I, lane);
     } else {
       const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
 #pragma unroll
@@ -610,6 +629,9 @@ constexpr int kW16EpilogueStores = 32;  // buffer stores per thread per tile
 // tile finishes; past the workgroup's last tile it copies zeros into
 // buffers no one reads. Fragments are double-buffered in registers by half
 // stage (32 K each): set A holds (g, h0), set B (g, h1).
+// kSwiGLU: tiles of 128 columns whose weight rows 0-127 are gate and
+// 128-255 up rows (a.g[0], a.g[1]), as in the fused W8A8 kernel.
+template <bool kSwiGLU>
 struct W16Copier {
   CopyPlan<4> pw;  // E4M3 weight, 64-byte stage rows
   CopyPlan<8> px;  // bf16 activation, 128-byte stage rows
@@ -617,10 +639,16 @@ struct W16Copier {
   int k;           // next stage of that tile
 
   __device__ __forceinline__ void start_tile(const GemmArgs& a, int slot, int tid) {
-    const TileCoord tc = tile_at(a, slot);
+    const TileCoord tc = tile_at<kSwiGLU ? kTileN / 2 : kTileN>(a, slot);
     tile_slot = slot;
     k = 0;
-    pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
+    if constexpr (kSwiGLU) {
+      const int64_t off = (int64_t)tc.n0 * a.k;
+      const int rows = a.g[0].n - tc.n0;
+      pw.init2(a.g[0].w + off, rows, a.g[1].w + off, rows, a.k, tid);
+    } else {
+      pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
+    }
     px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)a.k * 2, tid);
   }
 
@@ -694,8 +722,9 @@ __device__ __forceinline__ void w16_read(W16Half& f, int r, int b, int h, const 
 //                after a tile change the previous tile's 32 output stores,
 //                are younger than its copies); then the 12 reads of the
 //                next stage's first-half fragments and copies 6-11.
+template <class Copier>
 __device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W16Half& nf, int nb, int nh,
-                                         const W16Addr& ad, W16Copier& cp, int cbuf, int K, uint32_t wave_off,
+                                         const W16Addr& ad, Copier& cp, int cbuf, int K, uint32_t wave_off,
                                          bool second, bool after_stores) {
   v8bf wf[4];
 #pragma unroll
@@ -723,6 +752,10 @@ __device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W1
 }
 
 
+// kSwiGLU: the fused gate/up + SwiGLU form with a bf16 h (the 16-bit step's
+// split MLP), tiles and weight rows as in the fused W8A8 kernel; a.g[0]:
+// gate, h output, alpha s_gate; a.g[1]: up, alpha s_up.
+template <bool kSwiGLU>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a16_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -734,7 +767,7 @@ gemm_w8a16_kernel(const GemmArgs a) {
   W16Addr ad;
   ad.init(wn * 128 + (lane & 31), wm * 128 + (lane & 31), lane >> 5);
 
-  W16Copier cp;
+  W16Copier<kSwiGLU> cp;
   cp.start_tile(a, blockIdx.x, tid);
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -769,12 +802,22 @@ gemm_w8a16_kernel(const GemmArgs a) {
     // Epilogue: rows staged in the activation tile of the last stage's
     // buffer, which no wave reads once lgkmcnt(0) + barrier have passed.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const TileCoord tc = tile_at(a, tile_slot);
-    const GemmGroup& grp = a.g[tc.group];
-    const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, tc.m0 + wm * 128);
-    uint8_t* stage = lds16_x(b == 0 ? 2 : b - 1) + wave * (32 * 256);
+    uint8_t* area = lds16_x(b == 0 ? 2 : b - 1);
+    if constexpr (kSwiGLU) {
+      const TileCoord tc = tile_at<kTileN / 2>(a, tile_slot);
+      const int I = a.g[0].n;
+      const __amdgpu_buffer_rsrc_t out = h_rsrc(a.g[0].y, a.m, tc.m0 + wm * 128, I, 2);
+      const float alpha = wn ? a.g[1].alpha : a.g[0].alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, out, tc.n0 + wn * 128, lane);
+      for (int j = 0; j < 4; ++j) epilogue_swiglu<false>(acc, j, area, wm, wn, alpha, 1.0f, out, tc.n0, I, lane);
+    } else {
+      const TileCoord tc = tile_at(a, tile_slot);
+      const GemmGroup& grp = a.g[tc.group];
+      const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, tc.m0 + wm * 128);
+      uint8_t* stage = area + wave * (32 * 256);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, out, tc.n0 + wn * 128, lane);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -807,12 +850,15 @@ void gate_up_plan(GemmArgs& a) {
   a.total_tiles = a.tiles_m * a.g[0].tiles_n;
 }
 
-hipError_t launch_gate_up_swiglu(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, hipStream_t s) {
   static const int cus = cu_count();
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL(gemm_w8a8_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if (w8a16)
+    hipLaunchKernelGGL(gemm_w8a16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemm_w8a8_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -821,7 +867,7 @@ hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s) {
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL(gemm_w8a16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(gemm_w8a16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

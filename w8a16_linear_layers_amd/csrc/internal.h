@@ -47,7 +47,8 @@ void gate_up_plan(GemmArgs& a);
 hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipStream_t s);
 hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s);
-hipError_t launch_gate_up_swiglu(const GemmArgs& a, hipStream_t s);
+// Fused gate/up + SwiGLU: W8A8 (E4M3 h, a.out_rs) or W8A16 (bf16 h).
+hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, hipStream_t s);
 hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, int64_t n, float scale,
                          hipStream_t s);
 

@@ -28,6 +28,7 @@ from . import (
     MODE_W8A16,
     TOWER_GENERATION,
     fp8lin_gate_up_swiglu_w8a8,
+    fp8lin_gate_up_swiglu_w8a16,
     fp8lin_gemm_w8a8,
     fp8lin_gemm_w8a16,
     fp8lin_qkv_shared,
@@ -88,9 +89,10 @@ class Buffers:
 def block_forward(w: BlockWeights, x: torch.Tensor, mode: int, buf: Buffers, out: torch.Tensor, fused_mlp=False):
     """One block in `mode`; writes the block output into `out` (bf16 [m, hidden]).
 
-    fused_mlp (W8A8 steps): gate/up and the SwiGLU run as one fused launch
-    (fp8lin_gate_up_swiglu_w8a8) on the once-quantized MLP input; the codes
-    equal the split path's bit for bit.
+    fused_mlp: gate/up and the SwiGLU run as one fused launch
+    (fp8lin_gate_up_swiglu_w8a8 on the once-quantized MLP input on W8A8
+    steps, fp8lin_gate_up_swiglu_w8a16 on 16-bit steps); the output equals
+    the split path's bit for bit.
     """
     m, d = x.shape
     xq = buf.xq.view(-1)[: m * d].view(m, d)
@@ -109,9 +111,12 @@ def block_forward(w: BlockWeights, x: torch.Tensor, mode: int, buf: Buffers, out
     elif mode == MODE_W8A16:
         fp8lin_qkv_shared(x, w.qkv, w.s_qkv, [w.s_in_qkv] * 3, MODE_W8A16, outs=[buf.q, buf.k, buf.v])
         fp8lin_gemm_w8a16(buf.v, w.out, w.s_out, out=buf.o)
-        fp8lin_qkv_shared(buf.o, [w.gate, w.up], [w.s_gate, w.s_up], [w.s_in_mlp] * 2, MODE_W8A16,
-                          outs=[buf.g, buf.u])
-        fp8lin_swiglu_2in_quant(buf.g, buf.u, 1.0, DT_BF16, out=buf.h16)
+        if fused_mlp:
+            fp8lin_gate_up_swiglu_w8a16(buf.o, w.gate, w.up, w.s_gate, w.s_up, out=buf.h16)
+        else:
+            fp8lin_qkv_shared(buf.o, [w.gate, w.up], [w.s_gate, w.s_up], [w.s_in_mlp] * 2, MODE_W8A16,
+                              outs=[buf.g, buf.u])
+            fp8lin_swiglu_2in_quant(buf.g, buf.u, 1.0, DT_BF16, out=buf.h16)
         fp8lin_gemm_w8a16(buf.h16, w.down, w.s_down, out=out)
     else:
         raise ValueError("mode must be MODE_W8A8 or MODE_W8A16")
