@@ -28,6 +28,7 @@ Modules:
   bf16      -- bfloat16 bit conversion and round-to-nearest-even
   linear    -- static activation quantization, W8A8 and W8A16 GEMMs,
                shared-QKV, and the fused max-scale re-quantization identity
+  dynamic   -- dynamic per-tensor quantization: the scale from a runtime amax
   swiglu    -- two-input SwiGLU with E4M3 or bf16 output
   policy    -- diffusion_step_policy validation and per-step mode selection
 
