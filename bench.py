@@ -17,7 +17,8 @@ In the same run, on the same resident inputs:
               input/output buffers rotated over > 512 MB so the 256 MB
               last-level cache cannot serve repeats), the gated-MLP GEMMs,
               the gate/up + SwiGLU step split and fused,
-              the 1024- and 8192-row projections, the step policy, and the
+              the 1024- and 8192-row projections, the dynamic-FP8 form of the
+              step, the step policy, and the
               8-step denoising schedule over 4 blocks (config 5)
   * roofline  the grouped W8A8 GEMM launch against the dense FP8 matrix-core
               peak
@@ -289,6 +290,25 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     t16 = timed(lambda: fp8lin.fp8lin_qkv_shared(x, qws, sw, [s_in] * 3, fp8lin.MODE_W8A16, outs=ys), reps)
     rows["qkv_shared_w8a8"] = {"ms": round(t8, 4), "tflops": round(3 * GEMM_FLOP / t8 / 1e9, 2)}
     rows["qkv_shared_w8a16"] = {"ms": round(t16, 4), "tflops": round(3 * GEMM_FLOP / t16 / 1e9, 2)}
+
+    # dynamic per-tensor FP8 on the same activation: amax pass + quantize with the device scale, then the
+    # three projections reading that scale from device memory
+    s_dev = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_dev = torch.empty(1, dtype=torch.int32, device=dev)
+    t_qd = timed(lambda: fp8lin.fp8lin_quantize_dynamic(x, out=qx, scale=s_dev, workspace=ws_dev), reps)
+    t_qs = timed(lambda: fp8lin.fp8lin_quantize_static(x, s_in, out=qx), reps)
+
+    def step_dynamic():
+        fp8lin.fp8lin_quantize_dynamic(x, out=qx, scale=s_dev, workspace=ws_dev)
+        for i in range(3):
+            fp8lin.fp8lin_gemm_w8a8_dev_scale(qx, qws[i], s_dev, sw[i], out=ys[i])
+
+    t_dyn = timed(step_dynamic, reps)
+    rows["dynamic_fp8_qkv_16384x4096"] = {
+        "quantize_dynamic_ms": round(t_qd, 4), "quantize_static_ms": round(t_qs, 4),
+        "amax_pass_gbps": round(2 * M * K / max(t_qd - t_qs, 1e-6) / 1e6, 1),
+        "step_ms": round(t_dyn, 4), "step_tflops": round(3 * GEMM_FLOP / t_dyn / 1e9, 2),
+    }
 
     # quantize at [16384, 4096]: 2 bytes in + 1 byte out per element, buffers rotated over > 512 MB
     n = M * K

@@ -259,6 +259,39 @@ int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t
                                     hipStream_t stream);
 
 /*
+ * Dynamic per-tensor activation quantization: the scale comes from the
+ * tensor itself at run time instead of a calibrated checkpoint value (the
+ * dynamically quantized FP8 path the pages keep beside the static one,
+ * [TRT-17476] "What changed", "Test Coverage"). Two passes over x:
+ *   amax = max |x| over the finite elements (NaN and +-Inf excluded)
+ *   s    = max( fl32(amax) / 448, 2^-126 )     (float32, IEEE division; the
+ *          max-calibration rule behind the printed amax of [DF-15170] "Logs")
+ *   q    = the fp8lin_quantize_static codes of x with input scale s
+ * and s is stored to *scale_out on the device (for fp8lin_gemm_w8a8_dev_scale);
+ * the host never reads it, so there is no synchronization.
+ *   x, q       device, as for fp8lin_quantize_static (cols multiple of 16)
+ *   scale_out  device, one float (written)
+ *   amax_ws    device, one 32-bit word of scratch (cleared and overwritten
+ *              on the stream; calls sharing it must not overlap)
+ * rows or cols == 0: nothing is launched and *scale_out is left as it was.
+ * Launches counted as FP8LIN_KERNEL_AMAX and FP8LIN_KERNEL_QUANTIZE.
+ */
+int32_t fp8lin_quantize_dynamic(const void* x_bf16, void* q_e4m3, int64_t rows, int64_t cols, float* scale_out,
+                                uint32_t* amax_ws, hipStream_t stream);
+
+/*
+ * fp8lin_gemm_w8a8 with the input scale read from device memory (the scale
+ * fp8lin_quantize_dynamic stored): alpha = weight_scale * (*input_scale_dev),
+ * the same float product as the static call's, so the results agree bit for
+ * bit with fp8lin_gemm_w8a8 given that scale on the host. *input_scale_dev
+ * must be a positive normal float (it is not validated on the host).
+ *   input_scale_dev  device, one float, 4-byte aligned
+ */
+int32_t fp8lin_gemm_w8a8_dev_scale(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+                                   int64_t ldy, const float* input_scale_dev, float weight_scale,
+                                   hipStream_t stream);
+
+/*
  * Fail-closed check of a parsed policy ([TRT-17476] "Denoising-step
  * activation precision": unknown or missing fields, schema_version other than
  * 1 and any other type / index_space / default_mode / overlap are refused).
@@ -290,7 +323,8 @@ enum {
   FP8LIN_KERNEL_GEMM_W8A16 = 2,
   FP8LIN_KERNEL_SWIGLU = 3,
   FP8LIN_KERNEL_GATE_UP_SWIGLU = 4,
-  FP8LIN_KERNEL_KINDS = 5
+  FP8LIN_KERNEL_AMAX = 5,
+  FP8LIN_KERNEL_KINDS = 6
 };
 
 /* Number of kernels of `kind` this process has enqueued through the library

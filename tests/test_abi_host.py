@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -44,7 +44,7 @@ def test_strerror_covers_every_status():
 
 def test_launch_count_rejects_unknown_kind():
     assert fp8lin.fp8lin_launch_count(-1) == -1
-    assert fp8lin.fp8lin_launch_count(5) == -1
+    assert fp8lin.fp8lin_launch_count(6) == -1
     assert fp8lin.fp8lin_launch_count(0) >= 0
 
 
@@ -249,6 +249,34 @@ def test_gate_up_swiglu_w8a16_validation(lib):
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU)
     assert gus16(lib, M=0, x=None, h=None) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU) == before
+
+
+def qdyn(lib, x=FAKE, q=FAKE, rows=4, cols=64, scale=FAKE, ws=FAKE):
+    return lib.fp8lin_quantize_dynamic(x, q, rows, cols, scale, ws, None)
+
+
+def test_quantize_dynamic_validation(lib):
+    assert qdyn(lib, x=None) == fp8lin.EINVAL
+    assert qdyn(lib, scale=None) == fp8lin.EINVAL
+    assert qdyn(lib, ws=None) == fp8lin.EINVAL
+    assert qdyn(lib, cols=24) == fp8lin.ELAYOUT
+    assert qdyn(lib, scale=FAKE + 2) == fp8lin.ELAYOUT
+    assert qdyn(lib, ws=FAKE + 1) == fp8lin.ELAYOUT
+    assert qdyn(lib, cols=1 << 24) == fp8lin.EUNSUPPORTED
+    before = [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_AMAX, fp8lin.KERNEL_QUANTIZE)]
+    assert qdyn(lib, rows=0, x=None, q=None, scale=None, ws=None) == fp8lin.OK  # empty: nothing launched
+    assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_AMAX, fp8lin.KERNEL_QUANTIZE)] == before
+
+
+def test_gemm_dev_scale_validation(lib):
+    def g(qx=FAKE, qw=FAKE, y=FAKE, M=4, N=64, K=64, ldy=64, sd=FAKE, sw=0.001):
+        return lib.fp8lin_gemm_w8a8_dev_scale(qx, qw, y, M, N, K, ldy, sd, sw, None)
+
+    assert g(sd=None) == fp8lin.EINVAL
+    assert g(sd=FAKE + 2) == fp8lin.ELAYOUT
+    assert g(K=40) == fp8lin.ELAYOUT
+    assert g(sw=float("nan")) == fp8lin.ESCALE
+    assert g(M=0) == fp8lin.OK
 
 
 def qkv(lib, scales_in=(0.01, 0.01, 0.01), n=(64, 64, 64), mode=0, ws=FAKE, nproj=3):

@@ -34,6 +34,8 @@ __all__ = [
     "fp8lin_swiglu_2in_quant",
     "fp8lin_gate_up_swiglu_w8a8",
     "fp8lin_gate_up_swiglu_w8a16",
+    "fp8lin_quantize_dynamic",
+    "fp8lin_gemm_w8a8_dev_scale",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -43,12 +45,13 @@ __all__ = [
     "KERNEL_GEMM_W8A16",
     "KERNEL_SWIGLU",
     "KERNEL_GATE_UP_SWIGLU",
+    "KERNEL_AMAX",
 ]
 
 MODE_W8A8, MODE_W8A16 = 0, 1
 DT_BF16, DT_E4M3 = 0, 1
 TOWER_GENERATION, TOWER_REASONER = 0, 1
-KERNEL_QUANTIZE, KERNEL_GEMM_W8A8, KERNEL_GEMM_W8A16, KERNEL_SWIGLU, KERNEL_GATE_UP_SWIGLU = 0, 1, 2, 3, 4
+KERNEL_QUANTIZE, KERNEL_GEMM_W8A8, KERNEL_GEMM_W8A16, KERNEL_SWIGLU, KERNEL_GATE_UP_SWIGLU, KERNEL_AMAX = range(6)
 
 OK, EINVAL, ELAYOUT, EDTYPE, ESCALE, EPOLICY, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
 
@@ -64,6 +67,8 @@ EXPORTS = (
     "fp8lin_swiglu_2in_quant",
     "fp8lin_gate_up_swiglu_w8a8",
     "fp8lin_gate_up_swiglu_w8a16",
+    "fp8lin_quantize_dynamic",
+    "fp8lin_gemm_w8a8_dev_scale",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -123,6 +128,8 @@ def load_library():
     lib.fp8lin_swiglu_2in_quant.argtypes = [vp, vp, vp, i32, i64, i64, f32, vp]
     lib.fp8lin_gate_up_swiglu_w8a8.argtypes = [vp, i64, i64, vp, vp, i64, f32, f32, f32, f32, vp, vp]
     lib.fp8lin_gate_up_swiglu_w8a16.argtypes = [vp, i32, i64, i64, vp, vp, i64, f32, f32, vp, vp]
+    lib.fp8lin_quantize_dynamic.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.fp8lin_gemm_w8a8_dev_scale.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, f32, vp]
     lib.fp8lin_policy_validate.argtypes = [ctypes.POINTER(Policy)]
     lib.fp8lin_step_policy.argtypes = [ctypes.POINTER(Policy), i32, i32, i32, ctypes.POINTER(i32)]
     lib.fp8lin_strerror.argtypes = [i32]
@@ -325,6 +332,43 @@ def fp8lin_gate_up_swiglu_w8a16(x, qw_gate, qw_up, gate_scale, up_scale, out=Non
             _stream(stream)
         ),
         "fp8lin_gate_up_swiglu_w8a16",
+    )
+    return out
+
+
+def fp8lin_quantize_dynamic(x, out=None, scale=None, workspace=None, stream=None):
+    """(codes, scale): E4M3 codes of bf16 x with its own runtime scale; `scale` is a 1-element float32 device tensor."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    rows, cols = _rows(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check(
+        load_library().fp8lin_quantize_dynamic(_ptr(x), _ptr(out), rows, cols, _ptr(scale), _ptr(workspace),
+                                               _stream(stream)),
+        "fp8lin_quantize_dynamic",
+    )
+    return out, scale
+
+
+def fp8lin_gemm_w8a8_dev_scale(qx, qw, input_scale_dev, weight_scale, out=None, ldy=None, stream=None):
+    """fp8lin_gemm_w8a8 with the input scale taken from a 1-element float32 device tensor."""
+    if qx.dtype != torch.uint8 or qw.dtype != torch.uint8:
+        raise TypeError("qx and qw must hold E4M3 codes as torch.uint8")
+    if input_scale_dev.dtype != torch.float32 or input_scale_dev.numel() < 1:
+        raise TypeError("input_scale_dev must be a float32 device tensor")
+    m, k = _rows(qx)
+    n = qw.shape[0]
+    out, ldy = _gemm_out(qx.shape[:-1], n, qx.device, out, ldy)
+    _check(
+        load_library().fp8lin_gemm_w8a8_dev_scale(
+            _ptr(qx), _ptr(qw), _ptr(out), m, n, k, ldy, _ptr(input_scale_dev), float(weight_scale), _stream(stream)
+        ),
+        "fp8lin_gemm_w8a8_dev_scale",
     )
     return out
 

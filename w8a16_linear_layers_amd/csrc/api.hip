@@ -79,6 +79,46 @@ int32_t fp8lin_quantize_static(const void* x_bf16, void* q_e4m3, int64_t rows, i
   return hip_status(fp8lin::launch_quantize(x_bf16, q_e4m3, rows * cols, input_scale, stream));
 }
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int32_t fp8lin_quantize_dynamic(const void* x_bf16, void* q_e4m3, int64_t rows, int64_t cols, float* scale_out,
+                                uint32_t* amax_ws, hipStream_t stream) {
+  int32_t st = check_matrix(rows, cols);
+  if (st != FP8LIN_OK) return st;
+  if (rows == 0 || cols == 0) return FP8LIN_OK;  // empty: nothing launched, scale_out untouched
+  if (x_bf16 == nullptr || q_e4m3 == nullptr || scale_out == nullptr || amax_ws == nullptr) return FP8LIN_EINVAL;
+  if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned4(scale_out) || !aligned4(amax_ws)) return FP8LIN_ELAYOUT;
+  count_launch(FP8LIN_KERNEL_AMAX);
+  count_launch(FP8LIN_KERNEL_QUANTIZE);
+  return hip_status(fp8lin::launch_quantize_dynamic(x_bf16, q_e4m3, rows * cols, amax_ws, scale_out, stream));
+}
+
+int32_t fp8lin_gemm_w8a8_dev_scale(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+                                   int64_t ldy, const float* input_scale_dev, float weight_scale,
+                                   hipStream_t stream) {
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && qx == nullptr) || input_scale_dev == nullptr) return FP8LIN_EINVAL;
+  if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
+  if (!aligned16(qx) || !aligned4(input_scale_dev)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(weight_scale)) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  GemmArgs a{};
+  a.x = qx;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = 1;
+  a.in_scale_dev = input_scale_dev;
+  a.g[0].w = static_cast<const uint8_t*>(qw);
+  a.g[0].y = y_bf16;
+  a.g[0].n = (int32_t)N;
+  a.g[0].ldy = (int32_t)ldy;
+  a.g[0].alpha = weight_scale;
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  count_launch(FP8LIN_KERNEL_GEMM_W8A8);
+  return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
+}
+
 int32_t fp8lin_gemm_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K, int64_t ldy,
                          float input_scale, float weight_scale, hipStream_t stream) {
   int32_t st = check_gemm_matrix(M, K);

@@ -271,11 +271,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const GemmGroup& grp,
 // bf16) through the wave's 8 KiB staging area. Columns at or beyond N get an
 // out-of-range offset, so every lane issues the same eight stores.
 __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, uint8_t* stage, const GemmGroup& grp,
-                                              __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
+                                              float alpha, __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
   // The lane-dependent offsets below are cheap; an opaque copy of the lane
   // index keeps the compiler from holding them in registers across the K loop.
   asm volatile("" : "+v"(lane));
-  const float alpha = grp.alpha;
   const int h = lane >> 5;
   const int m = lane & 31;
 #pragma unroll
@@ -521,6 +520,9 @@ gemm_w8a8_kernel(const GemmArgs a) {
   const int row_x = wm * 128 + (lane & 31);
   const int g = lane >> 5;
   uint8_t* epi = lds_mem + kW8A8EpiOffset + wave * kW8A8EpiWave;
+  // dynamic quantization: the input scale is read from device memory and
+  // multiplies the host's weight_scale (the same float product as s_in * s_w)
+  const float alpha_mul = a.in_scale_dev != nullptr ? *a.in_scale_dev : 1.0f;
 
   CopyPlan<8> pw, px;
   auto plan_tile = [&](const TileCoord& t) {
@@ -595,7 +597,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
     } else {
       const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, epi, grp, out, cur.n0 + wn * 128, lane);
+      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, epi, grp, grp.alpha * alpha_mul, out, cur.n0 + wn * 128, lane);
     }
     if (next >= a.total_tiles) break;
     slot = next;
@@ -816,7 +818,7 @@ gemm_w8a16_kernel(const GemmArgs a) {
       const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, tc.m0 + wm * 128);
       uint8_t* stage = area + wave * (32 * 256);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, out, tc.n0 + wn * 128, lane);
+      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, grp.alpha, out, tc.n0 + wn * 128, lane);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

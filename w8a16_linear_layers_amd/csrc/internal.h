@@ -35,6 +35,7 @@ struct GemmArgs {
   int32_t total_tiles;
   float out_rs;   // fused gate/up + SwiGLU: 1 / s_h (the down projection's input scale)
   GemmGroup g[kMaxGroups];
+  const float* in_scale_dev;  // W8A8 with a device input scale: alpha = g.alpha * *in_scale_dev
 };
 
 // Fills tile_begin / tiles_n / tiles_m / total_tiles from m, n of each group.
@@ -45,6 +46,10 @@ void gemm_plan(GemmArgs& a);
 void gate_up_plan(GemmArgs& a);
 
 hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipStream_t s);
+// Dynamic: clears amax_ws, reduces the finite amax of x into it, then
+// quantizes with s = max(fl32(amax) / 448, 2^-126) and stores s to scale_out.
+hipError_t launch_quantize_dynamic(const void* x, void* q, int64_t n, uint32_t* amax_ws, float* scale_out,
+                                   hipStream_t s);
 hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s);
 // Fused gate/up + SwiGLU: W8A8 (E4M3 h, a.out_rs) or W8A16 (bf16 h).
