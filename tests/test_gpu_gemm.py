@@ -165,3 +165,29 @@ def test_w8a16_refuses_fp8_activation(gpu):
     with pytest.raises(fp8lin.Fp8LinError) as e:
         fp8lin.fp8lin_gemm_w8a16(q, qw, 1.0)
     assert e.value.status == fp8lin.EDTYPE
+
+
+@pytest.mark.parametrize("kind", ["w8a8", "w8a16", "gate_up_w8a8", "gate_up_w8a16"])
+def test_repeated_launches_are_bit_identical(gpu, kind):
+    """Several tiles per workgroup (persistent kernels): every launch gives the same bits. A wave that
+    reuses LDS another wave still reads (tile changes, staging areas) would show up as run-to-run
+    differences."""
+    announce("repeatability %s" % kind)
+    m, k, n = 8192, 4096, 4096
+    x = normal_bf16((m, k), 0.35, 61).to(gpu)
+    qw = random_e4m3_codes((n, k), 62).to(gpu)
+    qw2 = random_e4m3_codes((n, k), 63).to(gpu)
+    qx = fp8lin.fp8lin_quantize_static(x, 0.35 * 4 / 448)
+    if kind == "w8a8":
+        run = lambda: fp8lin.fp8lin_gemm_w8a8(qx, qw, 0.35 * 4 / 448, 1e-3)  # noqa: E731
+    elif kind == "w8a16":
+        run = lambda: fp8lin.fp8lin_gemm_w8a16(x, qw, 1e-3)  # noqa: E731
+    elif kind == "gate_up_w8a8":
+        run = lambda: fp8lin.fp8lin_gate_up_swiglu_w8a8(qx, qw, qw2, 0.35 * 4 / 448, 1e-3, 1e-3, 0.05)  # noqa: E731
+    else:
+        run = lambda: fp8lin.fp8lin_gate_up_swiglu_w8a16(x, qw, qw2, 1e-3, 1e-3)  # noqa: E731
+    first = run()
+    for _ in range(4):
+        again = run()
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.uint8), again.view(torch.uint8))

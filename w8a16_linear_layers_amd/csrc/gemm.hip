@@ -819,6 +819,9 @@ gemm_w8a16_kernel(const GemmArgs a) {
       uint8_t* stage = area + wave * (32 * 256);
 #pragma unroll
       for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, grp.alpha, out, tc.n0 + wn * 128, lane);
+      // the next stage's first copies refill this buffer: every wave must be
+      // done reading its staged rows first
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
