@@ -26,10 +26,12 @@ Sources (web pages; cited by title and section):
 Modules:
   e4m3      -- OCP E4M3 ("FN") decode / saturating round-to-nearest-even encode
   bf16      -- bfloat16 bit conversion and round-to-nearest-even
+  f16       -- IEEE binary16 decode and round-to-nearest-even
   linear    -- static activation quantization, W8A8 and W8A16 GEMMs,
-               shared-QKV, and the fused max-scale re-quantization identity
+               shared-QKV, the fused max-scale re-quantization identity,
+               and the float32-accumulation bound of W8A16 outputs
   dynamic   -- dynamic per-tensor quantization: the scale from a runtime amax
-  swiglu    -- two-input SwiGLU with E4M3 or bf16 output
+  swiglu    -- two-input SwiGLU with E4M3, bf16 or fp16 output
   policy    -- diffusion_step_policy validation and per-step mode selection
 
 Parity pins: every function is pinned by tests in ``tests/test_oracle_*.py``
@@ -39,4 +41,4 @@ E4M3 path near rounding midpoints is pinned only up to the documented
 near-tie rule (see ``swiglu``).
 """
 
-from . import bf16, e4m3, linear, policy, swiglu  # noqa: F401
+from . import bf16, dynamic, e4m3, f16, linear, policy, swiglu  # noqa: F401

@@ -60,10 +60,45 @@ def gemm_w8a16(x, qw, weight_scale):
     s_w * dec(qW) to the activation dtype before the GEMM ([DF-14664]
     "Behavior": dequant + F.linear); the exact product is used here, which
     that path approximates within the GEMM tolerance.
+
+    The activation may be bf16, fp16 or float32 ([DF-14664] "Tests" lists an
+    FP32 W8A16 case): the definition is the same, taken on the values.
     """
     xf = np.asarray(x, dtype=np.float64)
     b = e4m3.decode(qw)
     return (xf @ b.T) * float(np.float32(weight_scale))
+
+
+def f32_ulp(v):
+    """Spacing of float32 values at |v| (float64), floored at 2**-149."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(v)
+    e = np.where(v > 0, e, -1000)  # zero: the subnormal quantum
+    return np.ldexp(1.0, np.maximum(e - 24, -149))
+
+
+def gemm_w8a16_bound(x, qw, weight_scale, n_terms, out_ulp):
+    """Largest |y - y_ref| of a W8A16 product accumulated in float32.
+
+    The arithmetic bound for y = round_out(fl32(s_w * A)), where A is a
+    float32 sum, in any order, of n_terms exact products whose true sum is
+    sum_k x dec(qW): |A - sum| <= gamma * S with S = sum_k |x dec(qW)| and
+    gamma = n u / (1 - n u), u = 2**-24 (the standard bound for recursive or
+    blocked summation); the scale multiply adds a relative u, and rounding
+    to the output format at most one ulp of the output (out_ulp) at the
+    largest magnitude the value can take. For 16-bit activations each
+    product is exact in float32 and n_terms = K; a float32 activation split
+    into three bf16 pieces gives 3 K exact products.
+    """
+    u = 2.0**-24
+    n = float(n_terms)
+    gamma = n * u / (1.0 - n * u)
+    s_w = float(np.float32(weight_scale))
+    xa = np.abs(np.asarray(x, dtype=np.float64))
+    S = (xa @ np.abs(e4m3.decode(qw)).T) * s_w
+    y_ref = gemm_w8a16(x, qw, weight_scale)
+    acc_err = gamma * (1.0 + u) * S + u * np.abs(y_ref)
+    return acc_err + out_ulp(np.abs(y_ref) + acc_err)
 
 
 def qkv_shared(x, qws, input_scales, weight_scales, mode):

@@ -17,12 +17,16 @@ Readings (the pages are silent):
     rounding midpoint, both neighbouring codes are accepted
     (``near_midpoint``). Outside that band the codes must be identical.
   * bf16 output: within one bf16 ulp of bf16_rne(h).
+  * FP16 inputs ([TRT-17476] "Test Coverage" runs the fused SwiGLU on BF16
+    and FP16 shapes): the same float64 h from the half-precision values;
+    FP8 output as above, FP16 output within one binary16 ulp of
+    f16_rne(h), which overflows to an infinity from 65520 up.
 Parity beyond these closed forms is unpinned: the pages print no values.
 """
 
 import numpy as np
 
-from . import bf16, e4m3
+from . import bf16, e4m3, f16
 
 NEAR_TIE_REL = 2.0**-20
 
@@ -48,6 +52,11 @@ def swiglu_2in_quant(g, u, out_scale):
 def swiglu_2in_bf16(g, u):
     """bf16_rne(silu(g) * u) as float64 values."""
     return bf16.round_rne(swiglu_2in(g, u))
+
+
+def swiglu_2in_f16(g, u):
+    """f16_rne(silu(g) * u) as float64 values (FP16 in, FP16 out)."""
+    return f16.round_rne(swiglu_2in(g, u))
 
 
 def near_midpoint(t, rel=NEAR_TIE_REL):
