@@ -353,6 +353,45 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     rows["swiglu_bf16_8192x16384"] = {"ms": round(ts16, 4), "gbps": round(6 * n2 / ts16 / 1e6, 1),
                                       "pct_hbm_peak": round(100 * 6 * n2 / ts16 / 1e6 / PEAK_HBM_GBPS, 2)}
 
+    # the same SwiGLU from binary16 gate/up (E4M3 or binary16 out)
+    gh = [(g.half(), u.half()) for g, u in gs]
+    o16h = torch.empty((mi, inter), dtype=torch.float16, device=dev)
+    it[0] = 0
+
+    def swh8():
+        i = it[0] % len(gh)
+        it[0] += 1
+        fp8lin.fp8lin_swiglu_2in(gh[i][0], gh[i][1], 2.1 / 448, fp8lin.DT_E4M3, out=o8[i])
+
+    def swh16():
+        i = it[0] % len(gh)
+        it[0] += 1
+        fp8lin.fp8lin_swiglu_2in(gh[i][0], gh[i][1], 1.0, fp8lin.DT_F16, out=o16h)
+
+    th8 = timed(swh8, 20)
+    th16 = timed(swh16, 20)
+    rows["swiglu_f16_in_8192x16384"] = {
+        "fp8_out_ms": round(th8, 4), "fp8_out_gbps": round(5 * n2 / th8 / 1e6, 1),
+        "f16_out_ms": round(th16, 4), "f16_out_gbps": round(6 * n2 / th16 / 1e6, 1),
+    }
+    del gh, o16h
+
+    # W8A16 with binary16 and float32 activations at the headline shape
+    x16 = x.half()
+    y16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    t_h = timed(lambda: fp8lin.fp8lin_gemm_w8a16(x16, qws[0], sw[0], out=y16), reps)
+    del x16, y16
+    x32 = x.float()
+    y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws32 = torch.empty(fp8lin.fp8lin_w8a16_f32_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    t_f = timed(lambda: fp8lin.fp8lin_gemm_w8a16_f32(x32, qws[0], sw[0], out=y32, workspace=ws32), reps)
+    rows["w8a16_activation_dtypes_16384x4096x4096"] = {
+        "f16_ms": round(t_h, 4), "f16_tflops": round(GEMM_FLOP / t_h / 1e9, 1),
+        "f32_ms": round(t_f, 4), "f32_tflops": round(GEMM_FLOP / t_f / 1e9, 1),
+        "f32_note": "split into three bf16 pieces (4 B in, 6 B out per value) + bf16 MFMA over 3K",
+    }
+    del x32, y32, ws32
+
     # gated-MLP GEMMs (gate/up 4096 -> 16384 on 8192 rows; down 16384 -> 4096) in both modes
     g_in = gs[0][0][:, :K].contiguous()  # any [8192, 4096] bf16 activation
     w_gu = torch.randint(0, 0x7E, (inter, K), dtype=torch.uint8, device=dev)

@@ -66,7 +66,8 @@ typedef enum {
 
 typedef enum { FP8LIN_MODE_W8A8 = 0, FP8LIN_MODE_W8A16 = 1 } fp8lin_mode;
 
-typedef enum { FP8LIN_DT_BF16 = 0, FP8LIN_DT_E4M3 = 1 } fp8lin_dtype;
+/* Element formats: bf16, OCP E4M3, IEEE binary16, IEEE binary32. */
+typedef enum { FP8LIN_DT_BF16 = 0, FP8LIN_DT_E4M3 = 1, FP8LIN_DT_F16 = 2, FP8LIN_DT_F32 = 3 } fp8lin_dtype;
 
 typedef enum { FP8LIN_TOWER_GENERATION = 0, FP8LIN_TOWER_REASONER = 1 } fp8lin_tower;
 
@@ -141,18 +142,50 @@ int32_t fp8lin_gemm_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M
  * ([TRT-17476] "Denoising-step activation precision": the resident FP8
  * weight is dequantized with its own weight_scale, input_scale is unused, no
  * dequantized weight copy is kept; [DF-14664] "Behavior"):
- *   y[m, n] = bf16_RNE( weight_scale * sum_k x[m, k] * dec(qw[n, k]) )
- * Weight tiles are staged in LDS as E4M3 and converted exactly to bf16 on
- * the way to the bf16 matrix cores; no bf16 weight is written to memory.
- *   x_dtype  must be FP8LIN_DT_BF16; an already-quantized activation
- *            (FP8LIN_DT_E4M3) is refused with FP8LIN_EDTYPE, as the pages'
- *            16-bit path refuses one.
- *   x   device, bf16 [M, K], contiguous
+ *   y[m, n] = RNE( weight_scale * sum_k x[m, k] * dec(qw[n, k]) )
+ * in the activation's 16-bit format. Weight tiles are staged in LDS as
+ * E4M3 and converted exactly to bf16 (or binary16) on the way to the
+ * matching matrix cores; no dequantized weight is written to memory.
+ *   x_dtype  FP8LIN_DT_BF16 or FP8LIN_DT_F16 (the pages' 16-bit activation
+ *            dtypes); an already-quantized activation (FP8LIN_DT_E4M3) is
+ *            refused with FP8LIN_EDTYPE, as the pages' 16-bit path refuses
+ *            one, and so is FP8LIN_DT_F32 (it needs the workspace of
+ *            fp8lin_gemm_w8a16_f32)
+ *   x   device, [M, K] of x_dtype, contiguous
  *   qw  device, E4M3 [N, K], contiguous
- *   y   device, bf16 [M, ldy]
+ *   y   device, [M, ldy] of x_dtype (binary16 overflows to an infinity)
  */
 int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,
                           int64_t K, int64_t ldy, float weight_scale, hipStream_t stream);
+
+/*
+ * W8A16 with a float32 activation ([DF-14664] "Tests" lists this case: the
+ * weight is dequantized to the activation's dtype and the product is taken
+ * in float32):
+ *   y[m, n] = fl32( weight_scale * A ),  A = sum_k x[m, k] * dec(qw[n, k])
+ * accumulated in float32. A first kernel splits every x value exactly into
+ * three bf16 pieces (hi + mid + lo = x; exact for |x| >= 2^-110, and
+ * non-finite values stay whole in hi) into the workspace, then the bf16
+ * W8A16 kernel takes 3 K exact products per output and writes float32.
+ * |y - exact| <= (3 K u / (1 - 3 K u)) * weight_scale * sum_k |x dec(qw)|
+ * plus two float32 roundings, u = 2^-24.
+ *   x          device, float32 [M, K], contiguous
+ *   qw         device, E4M3 [N, K], contiguous
+ *   y          device, float32 [M, ldy]
+ *   workspace  device, at least fp8lin_w8a16_f32_workspace_bytes(M, K)
+ *              bytes, 16-byte aligned; overwritten (caller-owned scratch;
+ *              two calls in flight on different streams need two)
+ *   K          multiple of 16, < 2^20 (else FP8LIN_EUNSUPPORTED)
+ * Launches counted as FP8LIN_KERNEL_SPLIT and FP8LIN_KERNEL_GEMM_W8A16.
+ */
+int32_t fp8lin_gemm_w8a16_f32(const void* x_f32, const void* qw, void* y_f32, int64_t M, int64_t N, int64_t K,
+                              int64_t ldy, float weight_scale, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Workspace bytes fp8lin_gemm_w8a16_f32 needs: M * 3 * 64 * ceil(K / 64) * 2
+ * (three bf16 pieces per value, each row padded to 64 values); -1 for
+ * sizes the call refuses. Host only. */
+int64_t fp8lin_w8a16_f32_workspace_bytes(int64_t M, int64_t K);
 
 /*
  * The GEMMs of a shared-input projection group on an activation quantized
@@ -216,6 +249,20 @@ int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void
                                 int64_t rows, int64_t cols, float out_scale, hipStream_t stream);
 
 /*
+ * The same two-input SwiGLU for either 16-bit input format ([TRT-17476]
+ * "What changed": the split SwiGLU runs on BF16 and FP16 shapes):
+ *   in_dtype   FP8LIN_DT_BF16 or FP8LIN_DT_F16 (else FP8LIN_EDTYPE)
+ *   out_dtype  FP8LIN_DT_E4M3 (codes as above) or in_dtype (RNE of h in
+ *              the input's format; binary16 overflows to an infinity);
+ *              another format -> FP8LIN_EDTYPE
+ *   gate, up   device, [rows, cols] of in_dtype, contiguous
+ * With in_dtype = FP8LIN_DT_BF16 it is fp8lin_swiglu_2in_quant. Unknown
+ * format values -> FP8LIN_EINVAL.
+ */
+int32_t fp8lin_swiglu_2in(const void* gate, const void* up, int32_t in_dtype, void* out, int32_t out_dtype,
+                          int64_t rows, int64_t cols, float out_scale, hipStream_t stream);
+
+/*
  * Gate/up projections and SwiGLU fused in one GEMM launch (W8A8): the split
  * gated MLP of [TRT-17476] "What changed" (gate and up on one shared FP8
  * activation, then silu(G) * U quantized for the down projection) without
@@ -248,10 +295,13 @@ int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const v
  *   h[m, n] = bf16_RNE( silu(g) * u )
  * i.e. exactly fp8lin_gemm_w8a16 for gate and for up followed by
  * fp8lin_swiglu_2in_quant(FP8LIN_DT_BF16) on their outputs, bit for bit.
- *   x_dtype  must be FP8LIN_DT_BF16 (FP8LIN_DT_E4M3 -> FP8LIN_EDTYPE)
- *   x        device, bf16 [M, K], contiguous
+ * With a binary16 activation every bf16 above is binary16 (the chain
+ * fp8lin_gemm_w8a16 + fp8lin_swiglu_2in in FP8LIN_DT_F16).
+ *   x_dtype  FP8LIN_DT_BF16 or FP8LIN_DT_F16 (FP8LIN_DT_E4M3 and
+ *            FP8LIN_DT_F32 -> FP8LIN_EDTYPE)
+ *   x        device, [M, K] of x_dtype, contiguous
  *   qw_gate, qw_up  device, E4M3 [I, K], contiguous
- *   h        device, bf16 [M, I], contiguous; I multiple of 16, < 2^22
+ *   h        device, [M, I] of x_dtype, contiguous; I multiple of 16, < 2^22
  * Launch counted as FP8LIN_KERNEL_GATE_UP_SWIGLU.
  */
 int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t M, int64_t K, const void* qw_gate,
@@ -324,7 +374,8 @@ enum {
   FP8LIN_KERNEL_SWIGLU = 3,
   FP8LIN_KERNEL_GATE_UP_SWIGLU = 4,
   FP8LIN_KERNEL_AMAX = 5,
-  FP8LIN_KERNEL_KINDS = 6
+  FP8LIN_KERNEL_SPLIT = 6, /* float32 activation -> three bf16 pieces */
+  FP8LIN_KERNEL_KINDS = 7
 };
 
 /* Number of kernels of `kind` this process has enqueued through the library

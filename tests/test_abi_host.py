@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -44,7 +44,7 @@ def test_strerror_covers_every_status():
 
 def test_launch_count_rejects_unknown_kind():
     assert fp8lin.fp8lin_launch_count(-1) == -1
-    assert fp8lin.fp8lin_launch_count(6) == -1
+    assert fp8lin.fp8lin_launch_count(7) == -1
     assert fp8lin.fp8lin_launch_count(0) >= 0
 
 
@@ -183,6 +183,35 @@ def test_gemm_w8a16_refuses_quantized_activation(lib):
     assert lib.fp8lin_gemm_w8a16(args[0], 7, *args[1:]) == fp8lin.EINVAL
     assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_BF16, FAKE, FAKE, 4, 64, 40, 64, 0.001, None) == fp8lin.ELAYOUT
     assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_BF16, FAKE, FAKE, 0, 64, 64, 64, 0.001, None) == fp8lin.OK
+    # float32 needs the workspace entry point; binary16 is accepted
+    assert lib.fp8lin_gemm_w8a16(args[0], fp8lin.DT_F32, *args[1:]) == fp8lin.EDTYPE
+    assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_F16, FAKE, FAKE, 0, 64, 64, 64, 0.001, None) == fp8lin.OK
+    assert lib.fp8lin_gemm_w8a16(FAKE, fp8lin.DT_F16, FAKE, FAKE, 4, 64, 40, 64, 0.001, None) == fp8lin.ELAYOUT
+
+
+def g16f32(lib, x=FAKE, w=FAKE, y=FAKE, M=4, N=64, K=64, ldy=64, sw=0.001, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.fp8lin_w8a16_f32_workspace_bytes(M, K)
+    return lib.fp8lin_gemm_w8a16_f32(x, w, y, M, N, K, ldy, sw, ws, wsb, None)
+
+
+def test_gemm_w8a16_f32_validation(lib):
+    ws = lib.fp8lin_w8a16_f32_workspace_bytes
+    assert ws(4, 64) == 4 * 3 * 64 * 2
+    assert ws(4, 80) == 4 * 3 * 128 * 2  # rows padded to 64 values
+    assert ws(0, 64) == 0
+    assert ws(-1, 64) == -1 and ws(4, 1 << 20) == -1
+    assert g16f32(lib, wsb=4 * 3 * 64 * 2 - 1) == fp8lin.EINVAL
+    assert g16f32(lib, ws=None) == fp8lin.EINVAL
+    assert g16f32(lib, ws=FAKE + 8) == fp8lin.ELAYOUT
+    assert g16f32(lib, x=FAKE + 4) == fp8lin.ELAYOUT
+    assert g16f32(lib, K=40) == fp8lin.ELAYOUT
+    assert g16f32(lib, K=1 << 20) == fp8lin.EUNSUPPORTED
+    assert g16f32(lib, ldy=32) == fp8lin.ELAYOUT
+    assert g16f32(lib, sw=0.0) == fp8lin.ESCALE
+    before = [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_SPLIT, fp8lin.KERNEL_GEMM_W8A16)]
+    assert g16f32(lib, M=0, x=None, y=None, ws=None, wsb=0) == fp8lin.OK
+    assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_SPLIT, fp8lin.KERNEL_GEMM_W8A16)] == before
 
 
 def grp(lib, n=(64, 64, 64), si=0.01, sw=(0.001, 0.001, 0.001), qx=FAKE, M=4, K=64, nproj=3):
@@ -239,6 +268,8 @@ def gus16(lib, x=FAKE, dt=0, M=4, K=64, wg=FAKE, wu=FAKE, inter=64, sg=0.001, su
 def test_gate_up_swiglu_w8a16_validation(lib):
     assert gus16(lib, dt=fp8lin.DT_E4M3) == fp8lin.EDTYPE  # the 16-bit step refuses FP8 activations
     assert gus16(lib, dt=7) == fp8lin.EINVAL
+    assert gus16(lib, dt=fp8lin.DT_F32) == fp8lin.EDTYPE
+    assert gus16(lib, dt=fp8lin.DT_F16, inter=24) == fp8lin.ELAYOUT  # binary16 passes the dtype check
     assert gus16(lib, x=None) == fp8lin.EINVAL
     assert gus16(lib, wg=None) == fp8lin.EINVAL
     assert gus16(lib, inter=24) == fp8lin.ELAYOUT
@@ -306,3 +337,19 @@ def test_swiglu_validation(lib):
     assert f(FAKE, FAKE + 2, FAKE, fp8lin.DT_E4M3, 4, 64, 0.1, None) == fp8lin.ELAYOUT
     assert f(FAKE, FAKE, FAKE, fp8lin.DT_E4M3, 4, 64, 0.0, None) == fp8lin.ESCALE
     assert f(FAKE, FAKE, FAKE, fp8lin.DT_BF16, 0, 64, 0.0, None) == fp8lin.OK  # scale unused for bf16
+
+
+def test_swiglu_2in_validation(lib):
+    f = lib.fp8lin_swiglu_2in
+    BF, F16, E4, F32 = fp8lin.DT_BF16, fp8lin.DT_F16, fp8lin.DT_E4M3, fp8lin.DT_F32
+    assert f(FAKE, FAKE, 9, FAKE, E4, 4, 64, 0.1, None) == fp8lin.EINVAL
+    assert f(FAKE, FAKE, F16, FAKE, 9, 4, 64, 0.1, None) == fp8lin.EINVAL
+    assert f(FAKE, FAKE, E4, FAKE, E4, 4, 64, 0.1, None) == fp8lin.EDTYPE
+    assert f(FAKE, FAKE, F32, FAKE, F32, 4, 64, 0.1, None) == fp8lin.EDTYPE
+    assert f(FAKE, FAKE, F16, FAKE, BF, 4, 64, 0.1, None) == fp8lin.EDTYPE  # 16-bit out = in format
+    assert f(FAKE, FAKE, BF, FAKE, F16, 4, 64, 0.1, None) == fp8lin.EDTYPE
+    assert f(FAKE, FAKE, F16, FAKE, E4, 4, 40, 0.1, None) == fp8lin.ELAYOUT
+    assert f(FAKE, FAKE, F16, FAKE, E4, 4, 64, 0.0, None) == fp8lin.ESCALE
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_SWIGLU)
+    assert f(None, None, F16, None, F16, 0, 64, 0.0, None) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_SWIGLU) == before

@@ -22,6 +22,8 @@ __all__ = [
     "MODE_W8A16",
     "DT_BF16",
     "DT_E4M3",
+    "DT_F16",
+    "DT_F32",
     "TOWER_GENERATION",
     "TOWER_REASONER",
     "Policy",
@@ -29,9 +31,12 @@ __all__ = [
     "fp8lin_quantize_static",
     "fp8lin_gemm_w8a8",
     "fp8lin_gemm_w8a16",
+    "fp8lin_gemm_w8a16_f32",
+    "fp8lin_w8a16_f32_workspace_bytes",
     "fp8lin_gemm_w8a8_group",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
+    "fp8lin_swiglu_2in",
     "fp8lin_gate_up_swiglu_w8a8",
     "fp8lin_gate_up_swiglu_w8a16",
     "fp8lin_quantize_dynamic",
@@ -46,12 +51,31 @@ __all__ = [
     "KERNEL_SWIGLU",
     "KERNEL_GATE_UP_SWIGLU",
     "KERNEL_AMAX",
+    "KERNEL_SPLIT",
 ]
 
 MODE_W8A8, MODE_W8A16 = 0, 1
-DT_BF16, DT_E4M3 = 0, 1
+DT_BF16, DT_E4M3, DT_F16, DT_F32 = 0, 1, 2, 3
 TOWER_GENERATION, TOWER_REASONER = 0, 1
-KERNEL_QUANTIZE, KERNEL_GEMM_W8A8, KERNEL_GEMM_W8A16, KERNEL_SWIGLU, KERNEL_GATE_UP_SWIGLU, KERNEL_AMAX = range(6)
+(
+    KERNEL_QUANTIZE,
+    KERNEL_GEMM_W8A8,
+    KERNEL_GEMM_W8A16,
+    KERNEL_SWIGLU,
+    KERNEL_GATE_UP_SWIGLU,
+    KERNEL_AMAX,
+    KERNEL_SPLIT,
+) = range(7)
+
+# torch dtype -> fp8lin_dtype (E4M3 codes travel as uint8 or float8_e4m3fn)
+_DT_OF = {
+    torch.bfloat16: DT_BF16,
+    torch.float16: DT_F16,
+    torch.float32: DT_F32,
+    torch.uint8: DT_E4M3,
+    torch.float8_e4m3fn: DT_E4M3,
+}
+_TORCH_OF = {DT_BF16: torch.bfloat16, DT_F16: torch.float16, DT_F32: torch.float32, DT_E4M3: torch.uint8}
 
 OK, EINVAL, ELAYOUT, EDTYPE, ESCALE, EPOLICY, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
 
@@ -62,9 +86,12 @@ EXPORTS = (
     "fp8lin_quantize_static",
     "fp8lin_gemm_w8a8",
     "fp8lin_gemm_w8a16",
+    "fp8lin_gemm_w8a16_f32",
+    "fp8lin_w8a16_f32_workspace_bytes",
     "fp8lin_gemm_w8a8_group",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
+    "fp8lin_swiglu_2in",
     "fp8lin_gate_up_swiglu_w8a8",
     "fp8lin_gate_up_swiglu_w8a16",
     "fp8lin_quantize_dynamic",
@@ -118,6 +145,10 @@ def load_library():
     lib.fp8lin_quantize_static.argtypes = [vp, vp, i64, i64, f32, vp]
     lib.fp8lin_gemm_w8a8.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
     lib.fp8lin_gemm_w8a16.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, f32, vp]
+    lib.fp8lin_gemm_w8a16_f32.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, vp, i64, vp]
+    lib.fp8lin_w8a16_f32_workspace_bytes.argtypes = [i64, i64]
+    lib.fp8lin_w8a16_f32_workspace_bytes.restype = i64
+    lib.fp8lin_swiglu_2in.argtypes = [vp, vp, i32, vp, i32, i64, i64, f32, vp]
     lib.fp8lin_gemm_w8a8_group.argtypes = [
         vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32), f32, ctypes.POINTER(vp), vp,
     ]
@@ -137,7 +168,7 @@ def load_library():
     lib.fp8lin_launch_count.argtypes = [i32]
     lib.fp8lin_launch_count.restype = i64
     for name in EXPORTS:
-        if name not in ("fp8lin_strerror", "fp8lin_launch_count"):
+        if name not in ("fp8lin_strerror", "fp8lin_launch_count", "fp8lin_w8a16_f32_workspace_bytes"):
             getattr(lib, name).restype = i32
     _LIB = lib
     return lib
@@ -182,9 +213,9 @@ def fp8lin_quantize_static(x, input_scale, out=None, stream=None):
     return out
 
 
-def _gemm_out(m_shape, n, device, out, ldy):
+def _gemm_out(m_shape, n, device, out, ldy, dtype=torch.bfloat16):
     if out is None:
-        out = torch.empty(tuple(m_shape) + (n,), dtype=torch.bfloat16, device=device)
+        out = torch.empty(tuple(m_shape) + (n,), dtype=dtype, device=device)
         ldy = n
     elif ldy is None:
         ldy = out.stride(-2) if out.dim() >= 2 else n
@@ -208,18 +239,46 @@ def fp8lin_gemm_w8a8(qx, qw, input_scale, weight_scale, out=None, ldy=None, stre
 
 
 def fp8lin_gemm_w8a16(x, qw, weight_scale, out=None, ldy=None, stream=None):
-    """y = (x dec(qw)^T) * s_w in bf16; x [..., K] bf16 (FP8 input is refused)."""
-    dtype = DT_E4M3 if x.dtype in (torch.uint8, torch.float8_e4m3fn) else DT_BF16
-    if dtype == DT_BF16 and x.dtype != torch.bfloat16:
-        raise TypeError("x must be bfloat16")
+    """y = (x dec(qw)^T) * s_w in x's 16-bit dtype; x [..., K] bf16 or fp16.
+
+    FP8 and float32 activations are passed on as such and refused by the
+    library (float32 takes fp8lin_gemm_w8a16_f32)."""
+    if x.dtype not in _DT_OF:
+        raise TypeError("x must be bfloat16 or float16")
+    dtype = _DT_OF[x.dtype]
     m, k = _rows(x)
     n = qw.shape[0]
-    out, ldy = _gemm_out(x.shape[:-1], n, x.device, out, ldy)
+    out, ldy = _gemm_out(x.shape[:-1], n, x.device, out, ldy, x.dtype if dtype in (DT_BF16, DT_F16) else torch.bfloat16)
     _check(
         load_library().fp8lin_gemm_w8a16(
             _ptr(x), dtype, _ptr(qw), _ptr(out), m, n, k, ldy, float(weight_scale), _stream(stream)
         ),
         "fp8lin_gemm_w8a16",
+    )
+    return out
+
+
+def fp8lin_w8a16_f32_workspace_bytes(m, k):
+    """Bytes of the workspace fp8lin_gemm_w8a16_f32 needs for an [m, k] activation."""
+    return int(load_library().fp8lin_w8a16_f32_workspace_bytes(int(m), int(k)))
+
+
+def fp8lin_gemm_w8a16_f32(x, qw, weight_scale, out=None, ldy=None, workspace=None, stream=None):
+    """y = (x dec(qw)^T) * s_w in float32 from a float32 x [..., K] (exact products, float32 sums)."""
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    m, k = _rows(x)
+    n = qw.shape[0]
+    out, ldy = _gemm_out(x.shape[:-1], n, x.device, out, ldy, torch.float32)
+    need = fp8lin_w8a16_f32_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(
+        load_library().fp8lin_gemm_w8a16_f32(
+            _ptr(x), _ptr(qw), _ptr(out), m, n, k, ldy, float(weight_scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)
+        ),
+        "fp8lin_gemm_w8a16_f32",
     )
     return out
 
@@ -292,6 +351,27 @@ def fp8lin_swiglu_2in_quant(gate, up, out_scale=1.0, out_dtype=DT_E4M3, out=None
     return out
 
 
+def fp8lin_swiglu_2in(gate, up, out_scale=1.0, out_dtype=DT_E4M3, out=None, stream=None):
+    """silu(gate) * up from bf16 or fp16 inputs, as E4M3 codes (uint8) or in the input's dtype."""
+    if gate.dtype != up.dtype or gate.dtype not in _DT_OF:
+        raise TypeError("gate and up must share a supported dtype")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    if not (gate.is_contiguous() and up.is_contiguous()):
+        raise ValueError("gate and up must be contiguous")
+    rows, cols = _rows(gate)
+    if out is None:
+        out = torch.empty(gate.shape, dtype=_TORCH_OF.get(int(out_dtype), torch.uint8), device=gate.device)
+    _check(
+        load_library().fp8lin_swiglu_2in(
+            _ptr(gate), _ptr(up), _DT_OF[gate.dtype], _ptr(out), int(out_dtype), rows, cols, float(out_scale),
+            _stream(stream)
+        ),
+        "fp8lin_swiglu_2in",
+    )
+    return out
+
+
 def fp8lin_gate_up_swiglu_w8a8(qx, qw_gate, qw_up, input_scale, gate_scale, up_scale, out_scale, out=None,
                                stream=None):
     """h = E4M3(silu(g) * u / out_scale) with g, u the bf16 W8A8 gate/up outputs, in one launch (uint8 codes)."""
@@ -314,10 +394,10 @@ def fp8lin_gate_up_swiglu_w8a8(qx, qw_gate, qw_up, input_scale, gate_scale, up_s
 
 
 def fp8lin_gate_up_swiglu_w8a16(x, qw_gate, qw_up, gate_scale, up_scale, out=None, stream=None):
-    """h = bf16(silu(g) * u) with g, u the bf16 W8A16 gate/up outputs, in one launch (FP8 input refused)."""
-    dtype = DT_E4M3 if x.dtype in (torch.uint8, torch.float8_e4m3fn) else DT_BF16
-    if dtype == DT_BF16 and x.dtype != torch.bfloat16:
-        raise TypeError("x must be bfloat16")
+    """h = silu(g) * u with g, u the W8A16 gate/up outputs, in one launch, in x's 16-bit dtype (FP8 refused)."""
+    if x.dtype not in _DT_OF:
+        raise TypeError("x must be bfloat16 or float16")
+    dtype = _DT_OF[x.dtype]
     if qw_gate.dtype != torch.uint8 or qw_up.dtype != torch.uint8:
         raise TypeError("the weights must hold E4M3 codes as torch.uint8")
     if qw_gate.shape != qw_up.shape:
@@ -325,7 +405,8 @@ def fp8lin_gate_up_swiglu_w8a16(x, qw_gate, qw_up, gate_scale, up_scale, out=Non
     m, k = _rows(x)
     inter = qw_gate.shape[0]
     if out is None:
-        out = torch.empty(tuple(x.shape[:-1]) + (inter,), dtype=torch.bfloat16, device=x.device)
+        odt = x.dtype if dtype in (DT_BF16, DT_F16) else torch.bfloat16
+        out = torch.empty(tuple(x.shape[:-1]) + (inter,), dtype=odt, device=x.device)
     _check(
         load_library().fp8lin_gate_up_swiglu_w8a16(
             _ptr(x), dtype, m, k, _ptr(qw_gate), _ptr(qw_up), inter, float(gate_scale), float(up_scale), _ptr(out),

@@ -23,6 +23,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 // rows of a bf16 activation (2 K bytes each) and 128 output rows (2 ldy bytes
 // each) must stay below the 2^31 out-of-range offset.
 constexpr int64_t kMaxGemmDim = int64_t(1) << 22;
+// The three-piece float32 activation has 3 * 64 * ceil(K / 64) bf16 values
+// per row; 256 such rows must stay below the same 2^31 offset.
+constexpr int64_t kMaxF32K = int64_t(1) << 20;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -147,8 +150,9 @@ int32_t fp8lin_gemm_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M
 
 int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,
                           int64_t K, int64_t ldy, float weight_scale, hipStream_t stream) {
-  if (x_dtype == FP8LIN_DT_E4M3) return FP8LIN_EDTYPE;
-  if (x_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
+  // FP8 activations are refused; float32 ones take fp8lin_gemm_w8a16_f32
+  if (x_dtype == FP8LIN_DT_E4M3 || x_dtype == FP8LIN_DT_F32) return FP8LIN_EDTYPE;
+  if (x_dtype != FP8LIN_DT_BF16 && x_dtype != FP8LIN_DT_F16) return FP8LIN_EINVAL;
   int32_t st = check_gemm_matrix(M, K);
   if (st != FP8LIN_OK) return st;
   if (K == 0 || (M > 0 && x == nullptr)) return FP8LIN_EINVAL;
@@ -168,7 +172,44 @@ int32_t fp8lin_gemm_w8a16(const void* x, int32_t x_dtype, const void* qw, void* 
   a.g[0].alpha = weight_scale;
   if ((st = finish_plan(a)) != FP8LIN_OK) return st;
   count_launch(FP8LIN_KERNEL_GEMM_W8A16);
-  return hip_status(fp8lin::launch_gemm_w8a16(a, stream));
+  return hip_status(
+      fp8lin::launch_gemm_w8a16(a, x_dtype == FP8LIN_DT_F16 ? fp8lin::kW16F16 : fp8lin::kW16Bf16, stream));
+}
+
+int64_t fp8lin_w8a16_f32_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || K >= kMaxF32K || M > kMaxRows) return -1;
+  return M * 3 * ((K + 63) / 64 * 64) * 2;
+}
+
+int32_t fp8lin_gemm_w8a16_f32(const void* x_f32, const void* qw, void* y_f32, int64_t M, int64_t N, int64_t K,
+                              int64_t ldy, float weight_scale, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K >= kMaxF32K) return FP8LIN_EUNSUPPORTED;
+  if (K == 0 || (M > 0 && (x_f32 == nullptr || workspace == nullptr))) return FP8LIN_EINVAL;
+  if ((st = check_output(qw, y_f32, N, ldy, M)) != FP8LIN_OK) return st;
+  if (!aligned16(x_f32) || !aligned16(workspace)) return FP8LIN_ELAYOUT;
+  if (!scale_ok(weight_scale)) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  if (workspace_bytes < fp8lin_w8a16_f32_workspace_bytes(M, K)) return FP8LIN_EINVAL;
+  GemmArgs a{};
+  a.x = workspace;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.xk = (int32_t)(3 * ((K + 63) / 64 * 64));
+  a.ngroups = 1;
+  a.g[0].w = static_cast<const uint8_t*>(qw);
+  a.g[0].y = y_f32;
+  a.g[0].n = (int32_t)N;
+  a.g[0].ldy = (int32_t)ldy;
+  a.g[0].alpha = weight_scale;
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  count_launch(FP8LIN_KERNEL_SPLIT);
+  count_launch(FP8LIN_KERNEL_GEMM_W8A16);
+  hipError_t e = fp8lin::launch_split3(static_cast<const float*>(x_f32), workspace, M, K, stream);
+  if (e != hipSuccess) return FP8LIN_EHIP;
+  return hip_status(fp8lin::launch_gemm_w8a16(a, fp8lin::kW16F32, stream));
 }
 
 int32_t fp8lin_qkv_shared(const void* x_bf16, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
@@ -219,7 +260,7 @@ int32_t fp8lin_qkv_shared(const void* x_bf16, int64_t M, int64_t K, int32_t npro
     return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
   }
   count_launch(FP8LIN_KERNEL_GEMM_W8A16);
-  return hip_status(fp8lin::launch_gemm_w8a16(a, stream));
+  return hip_status(fp8lin::launch_gemm_w8a16(a, fp8lin::kW16Bf16, stream));
 }
 
 int32_t fp8lin_gemm_w8a8_group(const void* qx, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
@@ -286,14 +327,14 @@ int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const v
   if (tiles >= (int64_t(1) << 31)) return FP8LIN_EUNSUPPORTED;
   fp8lin::gate_up_plan(a);
   count_launch(FP8LIN_KERNEL_GATE_UP_SWIGLU);
-  return hip_status(fp8lin::launch_gate_up_swiglu(a, false, stream));
+  return hip_status(fp8lin::launch_gate_up_swiglu(a, false, false, stream));
 }
 
 int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t M, int64_t K, const void* qw_gate,
                                     const void* qw_up, int64_t I, float gate_scale, float up_scale, void* h_bf16,
                                     hipStream_t stream) {
-  if (x_dtype == FP8LIN_DT_E4M3) return FP8LIN_EDTYPE;
-  if (x_dtype != FP8LIN_DT_BF16) return FP8LIN_EINVAL;
+  if (x_dtype == FP8LIN_DT_E4M3 || x_dtype == FP8LIN_DT_F32) return FP8LIN_EDTYPE;
+  if (x_dtype != FP8LIN_DT_BF16 && x_dtype != FP8LIN_DT_F16) return FP8LIN_EINVAL;
   int32_t st = check_gemm_matrix(M, K);
   if (st != FP8LIN_OK) return st;
   if (K == 0 || (M > 0 && (x_bf16 == nullptr || h_bf16 == nullptr))) return FP8LIN_EINVAL;
@@ -321,7 +362,7 @@ int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t
   if (tiles >= (int64_t(1) << 31)) return FP8LIN_EUNSUPPORTED;
   fp8lin::gate_up_plan(a);
   count_launch(FP8LIN_KERNEL_GATE_UP_SWIGLU);
-  return hip_status(fp8lin::launch_gate_up_swiglu(a, true, stream));
+  return hip_status(fp8lin::launch_gate_up_swiglu(a, true, x_dtype == FP8LIN_DT_F16, stream));
 }
 
 int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void* out, int32_t out_dtype, int64_t rows,
@@ -335,7 +376,27 @@ int32_t fp8lin_swiglu_2in_quant(const void* gate_bf16, const void* up_bf16, void
   if (gate_bf16 == nullptr || up_bf16 == nullptr || out == nullptr) return FP8LIN_EINVAL;
   if (!aligned16(gate_bf16) || !aligned16(up_bf16) || !aligned16(out)) return FP8LIN_ELAYOUT;
   count_launch(FP8LIN_KERNEL_SWIGLU);
-  return hip_status(fp8lin::launch_swiglu(gate_bf16, up_bf16, out, fp8_out, rows * cols, out_scale, stream));
+  return hip_status(fp8lin::launch_swiglu(gate_bf16, up_bf16, out, false, fp8_out, rows * cols, out_scale, stream));
+}
+
+int32_t fp8lin_swiglu_2in(const void* gate, const void* up, int32_t in_dtype, void* out, int32_t out_dtype,
+                          int64_t rows, int64_t cols, float out_scale, hipStream_t stream) {
+  const auto known = [](int32_t d) {
+    return d == FP8LIN_DT_BF16 || d == FP8LIN_DT_E4M3 || d == FP8LIN_DT_F16 || d == FP8LIN_DT_F32;
+  };
+  if (!known(in_dtype) || !known(out_dtype)) return FP8LIN_EINVAL;
+  if (in_dtype != FP8LIN_DT_BF16 && in_dtype != FP8LIN_DT_F16) return FP8LIN_EDTYPE;
+  if (out_dtype != FP8LIN_DT_E4M3 && out_dtype != in_dtype) return FP8LIN_EDTYPE;
+  int32_t st = check_matrix(rows, cols);
+  if (st != FP8LIN_OK) return st;
+  const bool fp8_out = out_dtype == FP8LIN_DT_E4M3;
+  if (fp8_out && !scale_ok(out_scale)) return FP8LIN_ESCALE;
+  if (rows == 0 || cols == 0) return FP8LIN_OK;  // empty: pointers may be NULL
+  if (gate == nullptr || up == nullptr || out == nullptr) return FP8LIN_EINVAL;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(out)) return FP8LIN_ELAYOUT;
+  count_launch(FP8LIN_KERNEL_SWIGLU);
+  return hip_status(
+      fp8lin::launch_swiglu(gate, up, out, in_dtype == FP8LIN_DT_F16, fp8_out, rows * cols, out_scale, stream));
 }
 
 int32_t fp8lin_policy_validate(const fp8lin_policy* p) {

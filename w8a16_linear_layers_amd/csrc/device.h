@@ -14,6 +14,30 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// 16-bit activation formats: kF16 = false is bf16, true is IEEE binary16.
+// Unpacking is exact; packing rounds to nearest even (binary16 overflows to
+// an infinity, as the conversion instruction does by default).
+template <bool kF16>
+__device__ __forceinline__ float h16_lo(uint32_t w) {
+  if constexpr (kF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  else return bf16_lo(w);
+}
+template <bool kF16>
+__device__ __forceinline__ float h16_hi(uint32_t w) {
+  if constexpr (kF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else return bf16_hi(w);
+}
+template <bool kF16>
+__device__ __forceinline__ uint32_t h16x2(float a, float b) {
+  if constexpr (kF16) {
+    const _Float16 lo = (_Float16)a, hi = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  } else {
+    const __bf16 lo = (__bf16)a, hi = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+}
+
 // Saturate to the finite E4M3 range; +-Inf become +-448.
 __device__ __forceinline__ float clamp448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
 

@@ -23,12 +23,15 @@
 //   * Tiles of all groups form one index space, remapped so that the
 //     workgroups dispatched to one XCD (ids congruent mod 8) take a
 //     contiguous run of tiles, rasterized in bands of 8 M-tiles for L2 reuse.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
 namespace fp8lin {
 
 void gemm_plan(GemmArgs& a) {
+  if (a.xk == 0) a.xk = a.k;
   a.tiles_m = (a.m + kTileM - 1) / kTileM;
   int32_t t = 0;
   for (int i = 0; i < a.ngroups; ++i) {
@@ -45,6 +48,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -243,10 +248,7 @@ __device__ __forceinline__ TileCoord tile_at(const GemmArgs& a, int slot) {
 
 // ------------------------------------------------------------------ epilogues
 
-__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
-  const __bf16 lo = (__bf16)a, hi = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) { return h16x2<false>(a, b); }
 
 // acc[i][j] holds D[n][m] of the 32 x 32 block (n-block i, m-block j):
 // lane l, register v -> m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4,
@@ -259,17 +261,21 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
 
 // Output resource of a wave's 128 x 128 tile: rows [m_base, min(M, m_base +
 // 128)) of y, so stores to rows beyond M fall outside it and are dropped.
+// Rows m_base..+128 of a group's output of kBytes-byte elements.
+template <int kBytes = 2>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const GemmGroup& grp, int M, int m_base) {
   // readfirstlane keeps the (uniform) count scalar: a clamp may be computed
   // in a vector register, and a resource in vector registers costs a loop
   const int rows = __builtin_amdgcn_readfirstlane(max(0, min(M - m_base, 128)));
-  uint16_t* base = static_cast<uint16_t*>(grp.y) + (int64_t)min(m_base, M) * grp.ldy;
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * grp.ldy * 2, 0x00020000);
+  uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(m_base, M) * grp.ldy * kBytes;
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * grp.ldy * kBytes, 0x00020000);
 }
 
 // Rows [32 j, 32 j + 32) of the wave's tile (scaled by alpha, rounded to
-// bf16) through the wave's 8 KiB staging area. Columns at or beyond N get an
-// out-of-range offset, so every lane issues the same eight stores.
+// bf16, or to binary16 with kF16) through the wave's 8 KiB staging area.
+// Columns at or beyond N get an out-of-range offset, so every lane issues
+// the same eight stores.
+template <bool kF16 = false>
 __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, uint8_t* stage, const GemmGroup& grp,
                                               float alpha, __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
   // The lane-dependent offsets below are cheap; an opaque copy of the lane
@@ -283,8 +289,8 @@ __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, ui
     for (int t = 0; t < 4; ++t) {
       const int c = i * 4 + t;  // 16-byte chunk of n = 32 i + 8 t + 4 h
       u32x2 v;
-      v[0] = bf16x2(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
-      v[1] = bf16x2(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
+      v[0] = h16x2<kF16>(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
+      v[1] = h16x2<kF16>(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
       *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
     }
   }
@@ -300,6 +306,44 @@ __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, ui
   for (int q = 0; q < 8; ++q) {
     const int ml = 32 * j + q * 4 + (lane >> 4);
     const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, 0);
+  }
+}
+
+// Float32 form of epilogue_rows: columns [64 hf, 64 hf + 64) of rows
+// [32 j, 32 j + 32), scaled by alpha, through the same 8 KiB area (two calls
+// per row block; one wave's LDS operations complete in order, so a call's
+// staging writes follow the previous call's reads).
+__device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j, int hf, uint8_t* stage,
+                                                  const GemmGroup& grp, float alpha, __amdgpu_buffer_rsrc_t out,
+                                                  int n_base, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int h = lane >> 5;
+  const int m = lane & 31;
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = ii * 8 + t * 2 + h;  // 16-byte chunk of n = 64 hf + 32 ii + 8 t + 4 h
+      const int i = 2 * hf + ii;
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(acc[i][j][4 * t + e] * alpha);
+      *reinterpret_cast<u32x4*>(stage + m * 256 + ((c ^ (m & 15)) * 16)) = v;
+    }
+  }
+  const int c = lane & 15;
+  const int n = n_base + 64 * hf + c * 4;
+  u32x4 v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int ml = q * 4 + (lane >> 4);
+    v[q] = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) * 16));
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int ml = 32 * j + q * 4 + (lane >> 4);
+    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 4u : kOutOfRange;
     __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, 0);
   }
 }
@@ -421,8 +465,10 @@ __device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8>& pw, const C
 // in float32 (the two-input SwiGLU rule) and either its E4M3 code with
 // rs = 1 / s_h (kFp8Out) or its bf16 rounding, 16 columns per lane and row,
 // stored through the h resource of rows m_base..+128 (rows past M and
-// columns past I dropped). A second barrier frees the areas.
-template <bool kFp8Out>
+// columns past I dropped). A second barrier frees the areas. With kF16 the
+// staged values and a 16-bit h are binary16 instead of bf16 (the fp16
+// activation form of the separate GEMMs and SwiGLU).
+template <bool kFp8Out, bool kF16 = false>
 __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, uint8_t* epi, int wm, int wn,
                                                 float alpha, float rs, __amdgpu_buffer_rsrc_t out, int n_base,
                                                 int I, int lane) {
@@ -437,8 +483,8 @@ __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, 
       for (int t = 0; t < 4; ++t) {
         const int c = i * 4 + t;
         u32x2 v;
-        v[0] = bf16x2(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
-        v[1] = bf16x2(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
+        v[0] = h16x2<kF16>(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
+        v[1] = h16x2<kF16>(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
         *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
       }
     }
@@ -463,8 +509,8 @@ __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, 
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const uint32_t gw = gv[w >> 2][w & 3], uw = uv[w >> 2][w & 3];
-      hv[2 * w] = silu_mul(bf16_lo(gw), bf16_lo(uw));
-      hv[2 * w + 1] = silu_mul(bf16_hi(gw), bf16_hi(uw));
+      hv[2 * w] = silu_mul(h16_lo<kF16>(gw), h16_lo<kF16>(uw));
+      hv[2 * w + 1] = silu_mul(h16_hi<kF16>(gw), h16_hi<kF16>(uw));
     }
     const uint32_t o = col < I ? (uint32_t)(((32 * j + r) * I + col) * kBytes) : kOutOfRange;
     if constexpr (kFp8Out) {
@@ -478,8 +524,8 @@ __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, 
       u32x4 lo, hi;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        lo[w] = bf16x2(hv[2 * w], hv[2 * w + 1]);
-        hi[w] = bf16x2(hv[8 + 2 * w], hv[8 + 2 * w + 1]);
+        lo[w] = h16x2<kF16>(hv[2 * w], hv[2 * w + 1]);
+        hi[w] = h16x2<kF16>(hv[8 + 2 * w], hv[8 + 2 * w + 1]);
       }
       __builtin_amdgcn_raw_buffer_store_b128(lo, out, (int)o, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(hi, out, (int)(o + 16u), 0, 0);
@@ -606,22 +652,57 @@ gemm_w8a8_kernel(const GemmArgs a) {
 
 // ------------------------------------------------------------------ W8A16
 
-// Eight exact E4M3 -> bf16 conversions of one dword pair.
-__device__ __forceinline__ v8bf dequant8(uint32_t d0, uint32_t d1) {
-  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
-  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
-  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
-  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
-  v8bf v;
-  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
-  v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
-  return v;
+// Activation and output forms of the W8A16 kernel.
+enum W16Form : int {
+  kFormBf16 = kW16Bf16,  // bf16 activation and output, bf16 MFMA
+  kFormF16 = kW16F16,    // binary16 activation and output, fp16 MFMA
+  kFormF32 = kW16F32,    // float32 activation as three bf16 pieces per
+                         // 64-element block (hi, mid, lo: 3 K exact
+                         // products), float32 output
+};
+
+// The MFMA operand format: binary16 for kFormF16, else bf16.
+template <int kForm>
+using W16Op = typename std::conditional<kForm == kFormF16, v8h, v8bf>::type;
+
+// Eight exact E4M3 -> bf16 (or binary16) conversions of one dword pair;
+// every E4M3 value is representable in both formats.
+template <int kForm>
+__device__ __forceinline__ W16Op<kForm> dequant8(uint32_t d0, uint32_t d1) {
+  if constexpr (kForm == kFormF16) {
+    const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false);
+    const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true);
+    const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false);
+    const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true);
+    v8h v;
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+    return v;
+  } else {
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+    v8bf v;
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+    return v;
+  }
 }
 
-__device__ __forceinline__ v8bf as_v8bf(u32x4 c) { return __builtin_bit_cast(v8bf, c); }
+template <int kForm>
+__device__ __forceinline__ v16f w16_mfma(W16Op<kForm> w, u32x4 x, v16f acc) {
+  if constexpr (kForm == kFormF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(w, __builtin_bit_cast(v8h, x), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, __builtin_bit_cast(v8bf, x), acc, 0, 0, 0);
+}
 
-constexpr int kW16Copies = 12;          // copies per thread per stage
-constexpr int kW16EpilogueStores = 32;  // buffer stores per thread per tile
+constexpr int kW16Copies = 12;  // copies per thread per stage
+// Buffer stores per thread per tile: per 32-row block 8 (16-bit output),
+// 16 (float32) or 4 (the fused SwiGLU's 16-bit h).
+template <bool kSwiGLU, int kForm>
+constexpr int kW16EpilogueStores = kSwiGLU ? 16 : (kForm == kFormF32 ? 64 : 32);
 
 // Persistent W8A16 pipeline: K stages of 64 elements; one workgroup per CU
 // walks the tiles of dispatch slots blockIdx.x, blockIdx.x + gridDim.x, ...
@@ -633,7 +714,9 @@ constexpr int kW16EpilogueStores = 32;  // buffer stores per thread per tile
 // stage (32 K each): set A holds (g, h0), set B (g, h1).
 // kSwiGLU: tiles of 128 columns whose weight rows 0-127 are gate and
 // 128-255 up rows (a.g[0], a.g[1]), as in the fused W8A8 kernel.
-template <bool kSwiGLU>
+// kForm == kFormF32: the activation is the three-piece bf16 form, 3 stages
+// per 64-element weight block (stage k reads weight block k / 3).
+template <bool kSwiGLU, int kForm>
 struct W16Copier {
   CopyPlan<4> pw;  // E4M3 weight, 64-byte stage rows
   CopyPlan<8> px;  // bf16 activation, 128-byte stage rows
@@ -651,19 +734,20 @@ struct W16Copier {
     } else {
       pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
     }
-    px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)a.k * 2, tid);
+    px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)a.xk * 2, tid);
   }
 
   // Copy c of the current stage into buffer `buf`: c < 4 weight chunk c,
-  // else activation chunk c - 4; chunks beyond K read as zero.
-  __device__ __forceinline__ void issue(int c, int buf, int K, uint32_t wave_off) const {
+  // else activation chunk c - 4; weight chunks beyond K and activation
+  // chunks beyond XK (the activation row length) read as zero.
+  __device__ __forceinline__ void issue(int c, int buf, int K, int XK, uint32_t wave_off) const {
     if (c < 4) {
-      const int k0b = k * 64;
+      const int k0b = (kForm == kFormF32 ? k / 3 : k) * 64;
       pw.dma(c, k0b + pw.kbyte >= K ? kOutOfRange : pw.voff[c], (uint32_t)k0b,
             lds_addr(lds16_w(buf)) + c * kThreads * 16 + wave_off);
     } else {
       const int k0b = k * 128;
-      px.dma(c - 4, k0b + px.kbyte >= 2 * K ? kOutOfRange : px.voff[c - 4], (uint32_t)k0b,
+      px.dma(c - 4, k0b + px.kbyte >= 2 * XK ? kOutOfRange : px.voff[c - 4], (uint32_t)k0b,
             lds_addr(lds16_x(buf)) + (c - 4) * kThreads * 16 + wave_off);
     }
   }
@@ -724,57 +808,66 @@ __device__ __forceinline__ void w16_read(W16Half& f, int r, int b, int h, const 
 //                after a tile change the previous tile's 32 output stores,
 //                are younger than its copies); then the 12 reads of the
 //                next stage's first-half fragments and copies 6-11.
-template <class Copier>
+// vmcnt encodes at most 63: a larger count waits for some of the younger
+// stores too, which is still correct.
+template <bool kSwiGLU, int kForm>
+constexpr int kW16AfterStoresWait = kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm> < 63
+                                        ? kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm>
+                                        : 63;
+
+template <bool kSwiGLU, int kForm, class Copier>
 __device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W16Half& nf, int nb, int nh,
-                                         const W16Addr& ad, Copier& cp, int cbuf, int K, uint32_t wave_off,
+                                         const W16Addr& ad, Copier& cp, int cbuf, int K, int XK, uint32_t wave_off,
                                          bool second, bool after_stores) {
-  v8bf wf[4];
+  W16Op<kForm> wf[4];
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
     const int e = t >> 4, i = (t >> 2) & 3, j = t & 3;
-    if (j == 0) wf[i] = dequant8(f.w[i][2 * e], f.w[i][2 * e + 1]);
-    const v8bf xv = as_v8bf(f.x[2 * j + e]);
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xv, acc[i][j], 0, 0, 0);
+    if (j == 0) wf[i] = dequant8<kForm>(f.w[i][2 * e], f.w[i][2 * e + 1]);
+    acc[i][j] = w16_mfma<kForm>(wf[i], f.x[2 * j + e], acc[i][j]);
     if (!second) {
       if ((t & 1) && t < 24) w16_read(nf, t >> 1, nb, nh, ad);
-      if (t >= 4 && t <= 24 && (t & 3) == 0) cp.issue((t >> 2) - 1, cbuf, K, wave_off);
+      if (t >= 4 && t <= 24 && (t & 3) == 0) cp.issue((t >> 2) - 1, cbuf, K, XK, wave_off);
     } else {
       if (t == 3) {
         if (after_stores)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2 + kW16EpilogueStores) : "memory");
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16AfterStoresWait<kSwiGLU, kForm>) : "memory");
         else
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2) : "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
       if (t >= 4 && t < 28 && (t & 1) == 0) w16_read(nf, (t - 4) >> 1, nb, nh, ad);
-      if (t >= 5 && t <= 25 && (t & 3) == 1) cp.issue(6 + ((t - 5) >> 2), cbuf, K, wave_off);
+      if (t >= 5 && t <= 25 && (t & 3) == 1) cp.issue(6 + ((t - 5) >> 2), cbuf, K, XK, wave_off);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 
-// kSwiGLU: the fused gate/up + SwiGLU form with a bf16 h (the 16-bit step's
-// split MLP), tiles and weight rows as in the fused W8A8 kernel; a.g[0]:
-// gate, h output, alpha s_gate; a.g[1]: up, alpha s_up.
-template <bool kSwiGLU>
+// kSwiGLU: the fused gate/up + SwiGLU form with a 16-bit h (the 16-bit
+// step's split MLP), tiles and weight rows as in the fused W8A8 kernel;
+// a.g[0]: gate, h output, alpha s_gate; a.g[1]: up, alpha s_up.
+// kForm: bf16, binary16 or (not with kSwiGLU) the float32 three-piece form,
+// whose activation rows hold a.xk = 3 * 64 * ceil(K / 64) bf16 values.
+template <bool kSwiGLU, int kForm>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a16_kernel(const GemmArgs a) {
+  static_assert(!(kSwiGLU && kForm == kFormF32), "the fused SwiGLU form has a 16-bit h");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.k;
-  const int KT = (K + 63) / 64;
+  const int K = a.k, XK = a.xk;
+  const int KT = (XK + 63) / 64;  // stages: 64 activation values each
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
   W16Addr ad;
   ad.init(wn * 128 + (lane & 31), wm * 128 + (lane & 31), lane >> 5);
 
-  W16Copier<kSwiGLU> cp;
+  W16Copier<kSwiGLU, kForm> cp;
   cp.start_tile(a, blockIdx.x, tid);
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
 #pragma unroll
-    for (int c = 0; c < kW16Copies; ++c) cp.issue(c, v, K, wave_off);
+    for (int c = 0; c < kW16Copies; ++c) cp.issue(c, v, K, XK, wave_off);
     cp.advance(a, KT, tid);
   }
   wait_vmem_and_barrier<kW16Copies>();  // stage 0 has landed
@@ -795,8 +888,8 @@ gemm_w8a16_kernel(const GemmArgs a) {
     for (int s = 0; s < KT; ++s) {
       const int nb = b == 2 ? 0 : b + 1;      // next stage's buffer
       const int cb = b == 0 ? 2 : b - 1;      // buffer of stage + 2
-      w16_half(acc, fa, fb, b, 1, ad, cp, cb, K, wave_off, false, false);
-      w16_half(acc, fb, fa, nb, 0, ad, cp, cb, K, wave_off, true, s == 0 && !first);
+      w16_half<kSwiGLU, kForm>(acc, fa, fb, b, 1, ad, cp, cb, K, XK, wave_off, false, false);
+      w16_half<kSwiGLU, kForm>(acc, fb, fa, nb, 0, ad, cp, cb, K, XK, wave_off, true, s == 0 && !first);
       cp.advance(a, KT, tid);
       b = nb;
     }
@@ -811,14 +904,25 @@ gemm_w8a16_kernel(const GemmArgs a) {
       const __amdgpu_buffer_rsrc_t out = h_rsrc(a.g[0].y, a.m, tc.m0 + wm * 128, I, 2);
       const float alpha = wn ? a.g[1].alpha : a.g[0].alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) epilogue_swiglu<false>(acc, j, area, wm, wn, alpha, 1.0f, out, tc.n0, I, lane);
+      for (int j = 0; j < 4; ++j)
+        epilogue_swiglu<false, kForm == kFormF16>(acc, j, area, wm, wn, alpha, 1.0f, out, tc.n0, I, lane);
     } else {
       const TileCoord tc = tile_at(a, tile_slot);
       const GemmGroup& grp = a.g[tc.group];
-      const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, tc.m0 + wm * 128);
       uint8_t* stage = area + wave * (32 * 256);
+      if constexpr (kForm == kFormF32) {
+        const __amdgpu_buffer_rsrc_t out = out_rsrc<4>(grp, a.m, tc.m0 + wm * 128);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, stage, grp, grp.alpha, out, tc.n0 + wn * 128, lane);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            epilogue_rows_f32(acc, j, hf, stage, grp, grp.alpha, out, tc.n0 + wn * 128, lane);
+      } else {
+        const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, tc.m0 + wm * 128);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          epilogue_rows<kForm == kFormF16>(acc, j, stage, grp, grp.alpha, out, tc.n0 + wn * 128, lane);
+      }
       // the next stage's first copies refill this buffer: every wave must be
       // done reading its staged rows first
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -849,30 +953,34 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
 }
 
 void gate_up_plan(GemmArgs& a) {
+  if (a.xk == 0) a.xk = a.k;
   a.tiles_m = (a.m + kTileM - 1) / kTileM;
   a.g[0].tiles_n = (a.g[0].n + kTileN / 2 - 1) / (kTileN / 2);
   a.g[0].tile_begin = 0;
   a.total_tiles = a.tiles_m * a.g[0].tiles_n;
 }
 
-hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, hipStream_t s) {
+hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, bool f16, hipStream_t s) {
   static const int cus = cu_count();
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  if (w8a16)
-    hipLaunchKernelGGL(gemm_w8a16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_w8a8_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  auto kernel = !w8a16 ? gemm_w8a8_kernel<true>
+                : f16  ? gemm_w8a16_kernel<true, kFormF16>
+                       : gemm_w8a16_kernel<true, kFormBf16>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s) {
   static const int cus = cu_count();
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL(gemm_w8a16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  auto kernel = form == kW16F16   ? gemm_w8a16_kernel<false, kFormF16>
+                : form == kW16F32 ? gemm_w8a16_kernel<false, kFormF32>
+                                  : gemm_w8a16_kernel<false, kFormBf16>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

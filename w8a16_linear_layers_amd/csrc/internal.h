@@ -27,9 +27,11 @@ struct GemmGroup {
 };
 
 struct GemmArgs {
-  const void* x;  // E4M3 [m, k] (W8A8) or bf16 [m, k] (W8A16)
+  const void* x;  // E4M3 [m, k] (W8A8) or 16-bit [m, xk] (W8A16)
   int32_t m;
   int32_t k;
+  int32_t xk;     // W8A16 activation row length: k, or 3 * 64 * ceil(k / 64) for
+                  // the three-piece float32 form (0: set to k by the plans)
   int32_t tiles_m;
   int32_t ngroups;
   int32_t total_tiles;
@@ -51,10 +53,15 @@ hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipSt
 hipError_t launch_quantize_dynamic(const void* x, void* q, int64_t n, uint32_t* amax_ws, float* scale_out,
                                    hipStream_t s);
 hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
-hipError_t launch_gemm_w8a16(const GemmArgs& a, hipStream_t s);
-// Fused gate/up + SwiGLU: W8A8 (E4M3 h, a.out_rs) or W8A16 (bf16 h).
-hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, hipStream_t s);
-hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, int64_t n, float scale,
+// W8A16 activation forms: bf16, binary16, float32 as three bf16 pieces
+constexpr int kW16Bf16 = 0, kW16F16 = 1, kW16F32 = 2;
+hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s);
+// x [rows, k] float32 -> x3 [rows, 3 * 64 * ceil(k / 64)] bf16 pieces
+hipError_t launch_split3(const float* x, void* x3, int64_t rows, int64_t k, hipStream_t s);
+// Fused gate/up + SwiGLU: W8A8 (E4M3 h, a.out_rs) or W8A16 (bf16 h, or
+// binary16 h from a binary16 activation with f16).
+hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, bool f16, hipStream_t s);
+hipError_t launch_swiglu(const void* g, const void* u, void* out, bool f16, bool fp8_out, int64_t n, float scale,
                          hipStream_t s);
 
 }  // namespace fp8lin

@@ -1,6 +1,6 @@
-// Two-input SwiGLU: h = silu(gate) * up from two separate bf16 tensors,
-// emitted as E4M3 codes (scaled by the down projection's static input
-// scale) or as bf16 on 16-bit steps.
+// Two-input SwiGLU: h = silu(gate) * up from two separate 16-bit tensors
+// (bf16 or fp16), emitted as E4M3 codes (scaled by the down projection's
+// static input scale) or in the input's format on 16-bit steps.
 //
 // [TRT-17476] "What changed": the split gated MLP feeds SiLU(G) * U from
 // two tensors straight into an FP8 output, avoiding the concatenated
@@ -17,19 +17,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;
 
-__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
-  const __bf16 lo = (__bf16)a;
-  const __bf16 hi = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
-
-template <bool kFp8Out>
+template <bool kF16, bool kFp8Out>
 __device__ __forceinline__ void swiglu8(const u32x4 gv, const u32x4 uv, void* out, int64_t i, float rs) {
   float h[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    h[2 * e] = silu_mul(bf16_lo(gv[e]), bf16_lo(uv[e]));
-    h[2 * e + 1] = silu_mul(bf16_hi(gv[e]), bf16_hi(uv[e]));
+    h[2 * e] = silu_mul(h16_lo<kF16>(gv[e]), h16_lo<kF16>(uv[e]));
+    h[2 * e + 1] = silu_mul(h16_hi<kF16>(gv[e]), h16_hi<kF16>(uv[e]));
   }
   if constexpr (kFp8Out) {
     u32x2 o;
@@ -40,16 +34,16 @@ __device__ __forceinline__ void swiglu8(const u32x4 gv, const u32x4 uv, void* ou
     __builtin_nontemporal_store(o, static_cast<u32x2*>(out) + i);
   } else {
     u32x4 o;
-    o.x = bf16_pair(h[0], h[1]);
-    o.y = bf16_pair(h[2], h[3]);
-    o.z = bf16_pair(h[4], h[5]);
-    o.w = bf16_pair(h[6], h[7]);
+    o.x = h16x2<kF16>(h[0], h[1]);
+    o.y = h16x2<kF16>(h[2], h[3]);
+    o.z = h16x2<kF16>(h[4], h[5]);
+    o.w = h16x2<kF16>(h[6], h[7]);
     __builtin_nontemporal_store(o, static_cast<u32x4*>(out) + i);
   }
 }
 
 // Full chunks with unguarded back-to-back loads, then a guarded tail.
-template <bool kFp8Out>
+template <bool kF16, bool kFp8Out>
 __global__ __launch_bounds__(kThreads) void swiglu_2in_kernel(const u32x4* __restrict__ g,
                                                               const u32x4* __restrict__ u, void* __restrict__ out,
                                                               int64_t nvec, float rs) {
@@ -64,28 +58,25 @@ __global__ __launch_bounds__(kThreads) void swiglu_2in_kernel(const u32x4* __res
       uv[k] = __builtin_nontemporal_load(u + base + k * kThreads);
     }
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) swiglu8<kFp8Out>(gv[k], uv[k], out, base + k * kThreads, rs);
+    for (int k = 0; k < kUnroll; ++k) swiglu8<kF16, kFp8Out>(gv[k], uv[k], out, base + k * kThreads, rs);
   }
   for (int64_t i = full + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads)
-    swiglu8<kFp8Out>(g[i], u[i], out, i, rs);
+    swiglu8<kF16, kFp8Out>(g[i], u[i], out, i, rs);
 }
 
 }  // namespace
 
-hipError_t launch_swiglu(const void* g, const void* u, void* out, bool fp8_out, int64_t n, float scale,
+hipError_t launch_swiglu(const void* g, const void* u, void* out, bool f16, bool fp8_out, int64_t n, float scale,
                          hipStream_t s) {
   const int64_t nvec = n / 8;
   const int64_t per_block = kThreads * kUnroll;
   int64_t blocks = (nvec + per_block - 1) / per_block;
   if (blocks > 65536) blocks = 65536;  // one chunk per workgroup up to 2^25 vectors
   const float rs = fp8_out ? 1.0f / scale : 1.0f;
-  if (fp8_out) {
-    hipLaunchKernelGGL(swiglu_2in_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       static_cast<const u32x4*>(g), static_cast<const u32x4*>(u), out, nvec, rs);
-  } else {
-    hipLaunchKernelGGL(swiglu_2in_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       static_cast<const u32x4*>(g), static_cast<const u32x4*>(u), out, nvec, rs);
-  }
+  auto kernel = f16 ? (fp8_out ? swiglu_2in_kernel<true, true> : swiglu_2in_kernel<true, false>)
+                    : (fp8_out ? swiglu_2in_kernel<false, true> : swiglu_2in_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, static_cast<const u32x4*>(g),
+                     static_cast<const u32x4*>(u), out, nvec, rs);
   return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@ E4M3_MAX = 448.0  # largest finite E4M3 magnitude: the calibrator's target
 __all__ = [
     "E4M3_MAX",
     "normal_bf16",
+    "normal_f16",
+    "normal_f32",
     "max_calibrated_scale",
     "random_e4m3_codes",
     "all_bf16_patterns",
@@ -51,6 +53,20 @@ def normal_bf16(shape, std, seed, device="cpu"):
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     t = torch.randn(tuple(shape), generator=gen, dtype=torch.float32) * float(std)
     return t.to(torch.bfloat16).to(device)
+
+
+def normal_f16(shape, std, seed, device="cpu"):
+    """IEEE binary16 tensor of N(0, std^2) draws (torch's round-to-nearest-even cast)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=gen, dtype=torch.float32) * float(std)
+    return t.to(torch.float16).to(device)
+
+
+def normal_f32(shape, std, seed, device="cpu"):
+    """float32 tensor of N(0, std^2) draws, reproducible from `seed`."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=gen, dtype=torch.float32) * float(std)
+    return t.to(device)
 
 
 def max_calibrated_scale(t):
