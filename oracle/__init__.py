@@ -32,6 +32,7 @@ Modules:
                and the float32-accumulation bound of W8A16 outputs
   dynamic   -- dynamic per-tensor quantization: the scale from a runtime amax
   swiglu    -- two-input SwiGLU with E4M3, bf16 or fp16 output
+  qknorm    -- per-head QK RMSNorm followed by rotate-half RoPE
   policy    -- diffusion_step_policy validation and per-step mode selection
 
 Parity pins: every function is pinned by tests in ``tests/test_oracle_*.py``
@@ -41,4 +42,4 @@ E4M3 path near rounding midpoints is pinned only up to the documented
 near-tie rule (see ``swiglu``).
 """
 
-from . import bf16, dynamic, e4m3, f16, linear, policy, swiglu  # noqa: F401
+from . import bf16, dynamic, e4m3, f16, linear, policy, qknorm, swiglu  # noqa: F401
