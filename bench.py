@@ -43,7 +43,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import w8a16_linear_layers_amd as fp8lin  # noqa: E402
-from workloads import config2, config3, config4, normal_bf16  # noqa: E402
+from workloads import config2, config3, config4, norm_weight_bf16, normal_bf16, rope_tables  # noqa: E402
 
 METRIC = "W8A8 FP8 GEMM TFLOP/s (% FP8 MFMA peak) at M=16384,K=N=4096; W8A16 TFLOP/s"
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 matrix-core peak
@@ -375,6 +375,18 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
         "f16_out_ms": round(th16, 4), "f16_out_gbps": round(6 * n2 / th16 / 1e6, 1),
     }
     del gh, o16h
+
+    # per-head QK RMSNorm + RoPE on the group's contiguous Q and K (32 heads of 128 per token)
+    hd = 128
+    cq, sq = (v.to(dev) for v in rope_tables(M, hd))
+    wq = norm_weight_bf16(hd, 950).to(dev)
+    wk = norm_weight_bf16(hd, 951).to(dev)
+    qo, ko = torch.empty_like(ys[0]), torch.empty_like(ys[1])
+    t_qk = timed(lambda: fp8lin.fp8lin_qk_norm_rope(ys[0], ys[1], wq, wk, cq, sq, hd, 1e-6, q_out=qo, k_out=ko), reps)
+    qk_bytes = 2 * M * N * 4 + M * hd * 4  # Q and K read and written once, plus the cos / sin tables
+    rows["qk_norm_rope_16384x2x4096"] = {"ms": round(t_qk, 4), "gbps": round(qk_bytes / t_qk / 1e6, 1),
+                                         "pct_hbm_peak": round(100 * qk_bytes / t_qk / 1e6 / PEAK_HBM_GBPS, 2)}
+    del qo, ko, cq, sq
 
     # W8A16 with binary16 and float32 activations at the headline shape
     x16 = x.half()

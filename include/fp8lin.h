@@ -309,6 +309,34 @@ int32_t fp8lin_gate_up_swiglu_w8a16(const void* x_bf16, int32_t x_dtype, int64_t
                                     hipStream_t stream);
 
 /*
+ * Per-head QK RMSNorm followed by rotary position embedding, reading the
+ * contiguous outputs of the separate Q and K projections ([TRT-17476] "It
+ * is also faster": with split projections these ops read contiguous rows,
+ * where the pages find the end-to-end gain; [DF-15170] "Logs": the
+ * processor views a projection as [tokens, heads, head_dim] and receives a
+ * precomputed rotary embedding). For every token t and head of D values x,
+ * in float32:
+ *   r = rsqrt(sum(x^2) / D + eps),  y = x * r * w
+ *   out[i]       = y[i] * cos[t, i] - y[i + D/2] * sin[t, i]
+ *   out[i + D/2] = y[i + D/2] * cos[t, i] + y[i] * sin[t, i],  i < D/2
+ * rounded once to bf16 (the rotate-half RoPE form; the pages fix neither
+ * eps nor the RoPE variant, so both are the caller's).
+ *   q, k          device, bf16 [tokens, q_heads * D] / [tokens, k_heads * D],
+ *                 contiguous; k may be NULL with k_heads = 0
+ *   q_out, k_out  device, same shapes; may equal q / k (in place), must not
+ *                 overlap them otherwise
+ *   q_weight, k_weight  device, bf16 [D] RMSNorm weights, or NULL for 1
+ *   cos, sin      device, float32 [tokens, D/2] rotary tables
+ *   head_dim      64 or 128 (else FP8LIN_EUNSUPPORTED)
+ *   eps           finite, > 0 (else FP8LIN_EINVAL)
+ * Pointers 16-byte aligned. One launch for Q and K, counted as
+ * FP8LIN_KERNEL_QK_NORM_ROPE; tokens = 0 is a no-op.
+ */
+int32_t fp8lin_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, int64_t tokens, int32_t q_heads,
+                            int32_t k_heads, int32_t head_dim, const void* q_weight, const void* k_weight,
+                            const float* cos, const float* sin, float eps, hipStream_t stream);
+
+/*
  * Dynamic per-tensor activation quantization: the scale comes from the
  * tensor itself at run time instead of a calibrated checkpoint value (the
  * dynamically quantized FP8 path the pages keep beside the static one,
@@ -375,7 +403,8 @@ enum {
   FP8LIN_KERNEL_GATE_UP_SWIGLU = 4,
   FP8LIN_KERNEL_AMAX = 5,
   FP8LIN_KERNEL_SPLIT = 6, /* float32 activation -> three bf16 pieces */
-  FP8LIN_KERNEL_KINDS = 7
+  FP8LIN_KERNEL_QK_NORM_ROPE = 7,
+  FP8LIN_KERNEL_KINDS = 8
 };
 
 /* Number of kernels of `kind` this process has enqueued through the library

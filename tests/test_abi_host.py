@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -44,7 +44,7 @@ def test_strerror_covers_every_status():
 
 def test_launch_count_rejects_unknown_kind():
     assert fp8lin.fp8lin_launch_count(-1) == -1
-    assert fp8lin.fp8lin_launch_count(7) == -1
+    assert fp8lin.fp8lin_launch_count(8) == -1
     assert fp8lin.fp8lin_launch_count(0) >= 0
 
 
@@ -353,3 +353,26 @@ def test_swiglu_2in_validation(lib):
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_SWIGLU)
     assert f(None, None, F16, None, F16, 0, 64, 0.0, None) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_SWIGLU) == before
+
+
+def qkn(lib, q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, t=4, qh=2, kh=2, d=128, wq=None, wk=None, c=FAKE, s=FAKE, eps=1e-6):
+    return lib.fp8lin_qk_norm_rope(q, k, qo, ko, t, qh, kh, d, wq, wk, c, s, eps, None)
+
+
+def test_qk_norm_rope_validation(lib):
+    assert qkn(lib, d=96) == fp8lin.EUNSUPPORTED
+    assert qkn(lib, d=256) == fp8lin.EUNSUPPORTED
+    assert qkn(lib, eps=0.0) == fp8lin.EINVAL
+    assert qkn(lib, eps=float("nan")) == fp8lin.EINVAL
+    assert qkn(lib, qh=0) == fp8lin.EINVAL
+    assert qkn(lib, t=-1) == fp8lin.EINVAL
+    assert qkn(lib, q=None) == fp8lin.EINVAL
+    assert qkn(lib, c=None) == fp8lin.EINVAL
+    assert qkn(lib, k=None) == fp8lin.EINVAL  # K heads without a K tensor
+    assert qkn(lib, k=FAKE + 8) == fp8lin.ELAYOUT
+    assert qkn(lib, s=FAKE + 4) == fp8lin.ELAYOUT
+    assert qkn(lib, wq=FAKE + 2) == fp8lin.ELAYOUT
+    assert qkn(lib, t=1 << 31) == fp8lin.EUNSUPPORTED
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_QK_NORM_ROPE)
+    assert qkn(lib, t=0, q=None, k=None, qo=None, ko=None, c=None, s=None) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_QK_NORM_ROPE) == before

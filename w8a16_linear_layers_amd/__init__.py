@@ -41,6 +41,7 @@ __all__ = [
     "fp8lin_gate_up_swiglu_w8a16",
     "fp8lin_quantize_dynamic",
     "fp8lin_gemm_w8a8_dev_scale",
+    "fp8lin_qk_norm_rope",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -52,6 +53,7 @@ __all__ = [
     "KERNEL_GATE_UP_SWIGLU",
     "KERNEL_AMAX",
     "KERNEL_SPLIT",
+    "KERNEL_QK_NORM_ROPE",
 ]
 
 MODE_W8A8, MODE_W8A16 = 0, 1
@@ -65,7 +67,8 @@ TOWER_GENERATION, TOWER_REASONER = 0, 1
     KERNEL_GATE_UP_SWIGLU,
     KERNEL_AMAX,
     KERNEL_SPLIT,
-) = range(7)
+    KERNEL_QK_NORM_ROPE,
+) = range(8)
 
 # torch dtype -> fp8lin_dtype (E4M3 codes travel as uint8 or float8_e4m3fn)
 _DT_OF = {
@@ -96,6 +99,7 @@ EXPORTS = (
     "fp8lin_gate_up_swiglu_w8a16",
     "fp8lin_quantize_dynamic",
     "fp8lin_gemm_w8a8_dev_scale",
+    "fp8lin_qk_norm_rope",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -161,6 +165,7 @@ def load_library():
     lib.fp8lin_gate_up_swiglu_w8a16.argtypes = [vp, i32, i64, i64, vp, vp, i64, f32, f32, vp, vp]
     lib.fp8lin_quantize_dynamic.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.fp8lin_gemm_w8a8_dev_scale.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, f32, vp]
+    lib.fp8lin_qk_norm_rope.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, f32, vp]
     lib.fp8lin_policy_validate.argtypes = [ctypes.POINTER(Policy)]
     lib.fp8lin_step_policy.argtypes = [ctypes.POINTER(Policy), i32, i32, i32, ctypes.POINTER(i32)]
     lib.fp8lin_strerror.argtypes = [i32]
@@ -415,6 +420,33 @@ def fp8lin_gate_up_swiglu_w8a16(x, qw_gate, qw_up, gate_scale, up_scale, out=Non
         "fp8lin_gate_up_swiglu_w8a16",
     )
     return out
+
+
+def fp8lin_qk_norm_rope(q, k, q_weight, k_weight, cos, sin, head_dim, eps=1e-6, q_out=None, k_out=None,
+                        stream=None):
+    """Per-head RMSNorm + rotate-half RoPE of bf16 q [tokens, Hq * D] and k [tokens, Hk * D].
+
+    cos, sin: float32 [tokens, D / 2]; weights bf16 [D] or None. Pass
+    q_out=q / k_out=k to work in place. Returns (q_out, k_out)."""
+    if q.dtype != torch.bfloat16 or (k is not None and k.dtype != torch.bfloat16):
+        raise TypeError("q and k must be bfloat16")
+    if cos.dtype != torch.float32 or sin.dtype != torch.float32:
+        raise TypeError("cos and sin must be float32")
+    tokens = q.shape[0] if q.dim() > 0 else 0
+    qh = q.shape[-1] // head_dim
+    kh = k.shape[-1] // head_dim if k is not None else 0
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k is not None and k_out is None:
+        k_out = torch.empty_like(k)
+    _check(
+        load_library().fp8lin_qk_norm_rope(
+            _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), tokens, qh, kh, int(head_dim), _ptr(q_weight),
+            _ptr(k_weight), _ptr(cos), _ptr(sin), float(eps), _stream(stream)
+        ),
+        "fp8lin_qk_norm_rope",
+    )
+    return q_out, k_out
 
 
 def fp8lin_quantize_dynamic(x, out=None, scale=None, workspace=None, stream=None):

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libfp8lin.so")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "swiglu.hip", "split.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "swiglu.hip", "split.hip", "qknorm.hip"]
 ARCH = "gfx950"
 
 COMPILE_FLAGS = [

@@ -399,6 +399,26 @@ int32_t fp8lin_swiglu_2in(const void* gate, const void* up, int32_t in_dtype, vo
       fp8lin::launch_swiglu(gate, up, out, in_dtype == FP8LIN_DT_F16, fp8_out, rows * cols, out_scale, stream));
 }
 
+int32_t fp8lin_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, int64_t tokens, int32_t q_heads,
+                            int32_t k_heads, int32_t head_dim, const void* q_weight, const void* k_weight,
+                            const float* cos, const float* sin, float eps, hipStream_t stream) {
+  if (tokens < 0 || q_heads <= 0 || k_heads < 0) return FP8LIN_EINVAL;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return FP8LIN_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return FP8LIN_EUNSUPPORTED;
+  const int64_t heads = (int64_t)q_heads + k_heads;
+  if (tokens > kMaxRows || heads * head_dim >= kMaxK || tokens * heads * head_dim >= kMaxElems)
+    return FP8LIN_EUNSUPPORTED;
+  if (tokens == 0) return FP8LIN_OK;
+  if (q == nullptr || q_out == nullptr || cos == nullptr || sin == nullptr) return FP8LIN_EINVAL;
+  if (k_heads > 0 && (k == nullptr || k_out == nullptr)) return FP8LIN_EINVAL;
+  if (!aligned16(q) || !aligned16(q_out) || !aligned16(k) || !aligned16(k_out) || !aligned16(cos) ||
+      !aligned16(sin) || !aligned16(q_weight) || !aligned16(k_weight))
+    return FP8LIN_ELAYOUT;
+  count_launch(FP8LIN_KERNEL_QK_NORM_ROPE);
+  return hip_status(fp8lin::launch_qk_norm_rope(q, q_out, q_heads, q_weight, k, k_out, k_heads, k_weight, tokens,
+                                                head_dim, cos, sin, eps, stream));
+}
+
 int32_t fp8lin_policy_validate(const fp8lin_policy* p) {
   if (p == nullptr) return FP8LIN_EINVAL;
   if ((p->present_mask & FP8LIN_PF_UNKNOWN_FIELD) != 0) return FP8LIN_EPOLICY;

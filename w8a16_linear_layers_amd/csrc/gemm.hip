@@ -734,7 +734,7 @@ struct W16Copier {
     } else {
       pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
     }
-    px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)a.xk * 2, tid);
+    px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)(kForm == kFormF32 ? a.xk : a.k) * 2, tid);
   }
 
   // Copy c of the current stage into buffer `buf`: c < 4 weight chunk c,
@@ -762,6 +762,13 @@ struct W16Copier {
         pw.exhaust();
         px.exhaust();
       }
+      // Use the copy offsets here: if the register allocator reloads them
+      // from scratch on this (once per tile) path, the load is waited for
+      // here rather than at their uses inside the stage loop.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(pw.voff[j]));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(px.voff[j]));
     }
   }
 };
@@ -856,7 +863,8 @@ gemm_w8a16_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.k, XK = a.xk;
+  const int K = a.k;
+  const int XK = kForm == kFormF32 ? a.xk : a.k;  // the 16-bit forms keep XK == K visible
   const int KT = (XK + 63) / 64;  // stages: 64 activation values each
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
   W16Addr ad;

@@ -56,6 +56,11 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
 // W8A16 activation forms: bf16, binary16, float32 as three bf16 pieces
 constexpr int kW16Bf16 = 0, kW16F16 = 1, kW16F32 = 2;
 hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s);
+// Per-head RMSNorm + rotate-half RoPE of q [tokens, q_heads * head_dim] and
+// k [tokens, k_heads * head_dim] (bf16; k_heads may be 0), head_dim 64 or 128.
+hipError_t launch_qk_norm_rope(const void* q, void* q_out, int q_heads, const void* q_w, const void* k, void* k_out,
+                               int k_heads, const void* k_w, int64_t tokens, int head_dim, const float* cos,
+                               const float* sin, float eps, hipStream_t s);
 // x [rows, k] float32 -> x3 [rows, 3 * 64 * ceil(k / 64)] bf16 pieces
 hipError_t launch_split3(const float* x, void* x3, int64_t rows, int64_t k, hipStream_t s);
 // Fused gate/up + SwiGLU: W8A8 (E4M3 h, a.out_rs) or W8A16 (bf16 h, or

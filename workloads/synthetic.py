@@ -28,6 +28,8 @@ __all__ = [
     "normal_bf16",
     "normal_f16",
     "normal_f32",
+    "rope_tables",
+    "norm_weight_bf16",
     "max_calibrated_scale",
     "random_e4m3_codes",
     "all_bf16_patterns",
@@ -67,6 +69,22 @@ def normal_f32(shape, std, seed, device="cpu"):
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     t = torch.randn(tuple(shape), generator=gen, dtype=torch.float32) * float(std)
     return t.to(device)
+
+
+def rope_tables(tokens, head_dim, base=10000.0, offset=0):
+    """float32 cos / sin tables [tokens, head_dim / 2] of the usual rotary angles
+    (position p, frequency base^(-2 i / head_dim)), as a caller precomputes them."""
+    half = head_dim // 2
+    pos = np.arange(offset, offset + tokens, dtype=np.float64)[:, None]
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    ang = pos * inv
+    return torch.from_numpy(np.cos(ang).astype(np.float32)), torch.from_numpy(np.sin(ang).astype(np.float32))
+
+
+def norm_weight_bf16(d, seed, std=0.1):
+    """bf16 RMSNorm weight [d]: 1 + N(0, std^2), reproducible from `seed`."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    return (1.0 + torch.randn((d,), generator=gen, dtype=torch.float32) * float(std)).to(torch.bfloat16)
 
 
 def max_calibrated_scale(t):
