@@ -18,13 +18,18 @@ In the same run, on the same resident inputs:
               last-level cache cannot serve repeats), the gated-MLP GEMMs,
               the gate/up + SwiGLU step split and fused,
               the 1024- and 8192-row projections, the dynamic-FP8 form of the
-              step, the step policy, and the
-              8-step denoising schedule over 4 blocks (config 5)
+              step, the per-head QK RMSNorm + RoPE on the step's Q and K, the
+              binary16 / float32 activation forms of W8A16 and SwiGLU, the
+              step policy, and the 8-step denoising schedule over 4 blocks
+              (config 5)
   * roofline  the grouped W8A8 GEMM launch against the dense FP8 matrix-core
               peak
   * cpu_baseline  the CPU oracle on a bounded sample of the same step
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+       (defaults K = W = 100: the matrix cores reach their sustained clock
+       only after some tens of milliseconds of load, so a short warm-up
+       under-reports the steady state)
        python bench.py --pmc   (a few launches of each step kernel and a
                                 plain copy, for rocprofv3 counter runs)
 """
@@ -145,8 +150,8 @@ def pmc_mode(dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 8-step schedule row")

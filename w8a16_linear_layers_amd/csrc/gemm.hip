@@ -387,15 +387,15 @@ __device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], 
 //                         buffer any more;
 //   MFMAs 8-15, k-step 1 MFMAs 0-7: one copy of stage s + 2 into that buffer
 //                         each (weight chunks, then activation chunks);
-//   after k-step 1 MFMA 8: vmcnt(16) + barrier: stage s + 1, copied during
+//   after k-step 1 MFMA 8: vmcnt(kVm) + barrier: stage s + 1, copied during
 //                         stage s - 1 (older than the 16 copies just issued),
-//                         has landed for every wave;
+//                         has landed for every wave; kVm = 16, and in stage
+//                         0 of a tile 16 + the previous tile's output stores,
+//                         which were issued after stage 1's copies;
 //   k-step 1 MFMAs 8-15 : read the k-step-0 fragments of stage s + 1 into
 //                         (wa, xa).
-// In stage 0 of a tile the copies of stage 1 are known to have landed
-// (kWaitVm = false), so that wait need not cover the previous tile's
-// output stores. sched_barrier keeps the compiler from regrouping slots.
-template <bool kWaitVm>
+// sched_barrier keeps the compiler from regrouping slots.
+template <int kVm>
 __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i (&xa)[4], v8i (&wb)[4], v8i (&xb)[4],
                                            const CopyPlan<8>& pw, const CopyPlan<8>& px, int s, int row_w, int row_x,
                                            int g, uint32_t wave_off) {
@@ -428,10 +428,7 @@ __device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i 
     } else {
       if (t == 8) {
         // stage s + 1 has landed for every wave (its copies are older than the 16 of stage s + 2)
-        if constexpr (kWaitVm)
-          asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-        else
-          asm volatile("s_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
       }
       const int f = t - 8;
       if (f == 0)
@@ -545,9 +542,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(void* h, int M, int m_b
 // Persistent W8A8 kernel: one workgroup per CU walks the tiles of dispatch
 // slots blockIdx.x, blockIdx.x + gridDim.x, ... After the last LDS read of
 // a tile the first two stages of the next tile are issued, so their latency
-// overlaps the last k-step; each wave waits for them before it issues the
-// tile's output stores (which go through an LDS area of its own), so the
-// next tile starts without waiting for those stores to complete.
+// overlaps the last k-step and the tile's output stores (which go through
+// an LDS area of each wave's own). The next tile then waits for its stage
+// 0 with a count that skips those stores (they were issued later), and
+// for stage 1 inside its stage 0, so it never waits for the stores.
 // kSwiGLU: the fused gate/up + SwiGLU form. A tile is 256 rows of M by 128
 // columns of h; weight rows 0-127 of the tile are the gate rows and 128-255
 // the up rows of those columns (a.g[0]: gate, h output, alpha s_in s_gate;
@@ -582,6 +580,9 @@ gemm_w8a8_kernel(const GemmArgs a) {
     px.init(static_cast<const uint8_t*>(a.x), t.m0, a.m - t.m0, K, tid);
   };
   constexpr int kTN = kSwiGLU ? kTileN / 2 : kTileN;
+  // buffer stores per thread of one tile's epilogue: 8 per 32-row block,
+  // or 2 for the fused SwiGLU's E4M3 h
+  constexpr int kStores = kSwiGLU ? 8 : 32;
 
   int slot = blockIdx.x;
   TileCoord tc = tile_at<kTN>(a, slot);
@@ -592,8 +593,12 @@ gemm_w8a8_kernel(const GemmArgs a) {
   for (;;) {
     const TileCoord cur = tc;
     const GemmGroup& grp = a.g[cur.group];
-    // every wave's copies of stages 0 and 1 have landed
-    asm volatile("s_barrier" ::: "memory");
+    // stage 0 has landed for every wave: after the first tile, only stage
+    // 1's copies (when KT > 1) and the previous tile's stores are younger
+    if (KT > 1)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(16 + kStores) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStores) : "memory");
     v8i wa[4], xa[4], wb[4], xb[4];
     w8a8_frags(0, 0, row_w, row_x, g, wa, xa);
     v16f acc[4][4];
@@ -605,8 +610,8 @@ gemm_w8a8_kernel(const GemmArgs a) {
     int s = 0;
     // steady state: stage s + 2 exists and is not the last (no K tail)
     if (KT >= 4) {
-      w8a8_stage<false>(acc, wa, xa, wb, xb, pw, px, 0, row_w, row_x, g, wave_off);
-      for (s = 1; s + 4 <= KT; ++s) w8a8_stage<true>(acc, wa, xa, wb, xb, pw, px, s, row_w, row_x, g, wave_off);
+      w8a8_stage<16 + kStores>(acc, wa, xa, wb, xb, pw, px, 0, row_w, row_x, g, wave_off);
+      for (s = 1; s + 4 <= KT; ++s) w8a8_stage<16>(acc, wa, xa, wb, xb, pw, px, s, row_w, row_x, g, wave_off);
     }
     // the stages before the last: copy only what exists, K tail masked
     for (; s + 1 < KT; ++s) {
@@ -632,7 +637,6 @@ gemm_w8a8_kernel(const GemmArgs a) {
       w8a8_first_stages(pw, px, K, KT, wave_off);
     }
     w8a8_mma(acc, wb, xb);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next tile's stages 0 and 1
     if constexpr (kSwiGLU) {
       const int I = grp.n;
       const __amdgpu_buffer_rsrc_t out = h_rsrc(grp.y, a.m, cur.m0 + wm * 128, I, 1);
