@@ -250,6 +250,13 @@ __device__ __forceinline__ TileCoord tile_at(const GemmArgs& a, int slot) {
 
 __device__ __forceinline__ uint32_t bf16x2(float a, float b) { return h16x2<false>(a, b); }
 
+// Cache policy of the GEMM output stores: slc (streaming). Output rows are
+// written once and never re-read by the kernel; streaming them keeps the
+// caches for the operand rows (measured on one box: a single 16384x4096x4096
+// launch +7.5%, the grouped QKV launch +2%, the split gated MLP 1.07 ->
+// 1.02 ms, no row slower).
+constexpr int kStreamStore = 2;
+
 // acc[i][j] holds D[n][m] of the 32 x 32 block (n-block i, m-block j):
 // lane l, register v -> m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4,
 // i.e. four consecutive n of one row per register quad. Written straight to
@@ -306,7 +313,7 @@ __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, ui
   for (int q = 0; q < 8; ++q) {
     const int ml = 32 * j + q * 4 + (lane >> 4);
     const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 2u : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kStreamStore);
   }
 }
 
@@ -344,7 +351,7 @@ __device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j
   for (int q = 0; q < 8; ++q) {
     const int ml = 32 * j + q * 4 + (lane >> 4);
     const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 4u : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kStreamStore);
   }
 }
 
