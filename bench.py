@@ -391,6 +391,20 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     qk_bytes = 2 * M * N * 4 + M * hd * 4  # Q and K read and written once, plus the cos / sin tables
     rows["qk_norm_rope_16384x2x4096"] = {"ms": round(t_qk, 4), "gbps": round(qk_bytes / t_qk / 1e6, 1),
                                          "pct_hbm_peak": round(100 * qk_bytes / t_qk / 1e6 / PEAK_HBM_GBPS, 2)}
+
+    # the same consumer fused into the grouped QKV launch's epilogue, against the two launches
+    def qkv_then_norm():
+        fp8lin.fp8lin_gemm_w8a8_group(qx, qws, s_in, sw, outs=ys)
+        fp8lin.fp8lin_qk_norm_rope(ys[0], ys[1], wq, wk, cq, sq, hd, 1e-6, q_out=qo, k_out=ko)
+
+    fused_outs = [qo, ko, ys[2]]
+    t_sep = timed(qkv_then_norm, reps)
+    t_fus = timed(lambda: fp8lin.fp8lin_qkv_w8a8_norm_rope(qx, qws, s_in, sw, wq, wk, cq, sq, 1e-6, outs=fused_outs),
+                  reps)
+    rows["qkv_w8a8_norm_rope_16384x4096x3x4096"] = {
+        "separate_ms": round(t_sep, 4), "fused_ms": round(t_fus, 4), "speedup": round(t_sep / t_fus, 3),
+        "fused_tflops": round(3 * GEMM_FLOP / t_fus / 1e9, 1),
+    }
     del qo, ko, cq, sq
 
     # W8A16 with binary16 and float32 activations at the headline shape

@@ -337,6 +337,33 @@ int32_t fp8lin_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_o
                             const float* cos, const float* sin, float eps, hipStream_t stream);
 
 /*
+ * The grouped W8A8 QKV projections with the per-head QK RMSNorm + RoPE of
+ * fp8lin_qk_norm_rope applied in the GEMM's epilogue to Q (group 0) and K
+ * (group 1), heads of 128 values: the consumer of the contiguous split
+ * outputs ([TRT-17476] "It is also faster") without its extra pass over Q
+ * and K. Per output row and head, with y = bf16_RNE(acc * input_scale *
+ * weight_scale) (the value fp8lin_gemm_w8a8_group writes):
+ *   r = rsqrt(sum(y^2) / 128 + eps)
+ *   out[d]      = y[d] r w[d] cos[m, d] - y[d + 64] r w[d + 64] sin[m, d]
+ *   out[d + 64] = y[d + 64] r w[d + 64] cos[m, d] + y[d] r w[d] sin[m, d]
+ * in float32, rounded once to bf16; group 2 (V) is the plain GEMM output.
+ * Same arguments and rules as fp8lin_gemm_w8a8_group, plus:
+ *   nproj          2 (Q, K) or 3 (Q, K, V)
+ *   n_out[0], n_out[1]  multiples of 128 (else FP8LIN_ELAYOUT)
+ *   q_norm_weight, k_norm_weight  device, bf16 [128], or NULL for 1
+ *   cos, sin       device, float32 [M, 64] rotary tables, 16-byte aligned
+ *   eps            finite, > 0 (else FP8LIN_EINVAL)
+ * The result is within the float32 error bound of the exact norm and
+ * rotation of y (the summation order differs from fp8lin_qk_norm_rope's,
+ * so the two may differ in the last bf16 bit). One launch, counted as
+ * FP8LIN_KERNEL_GEMM_W8A8.
+ */
+int32_t fp8lin_qkv_w8a8_norm_rope(const void* qx, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
+                                  const int64_t n_out[], const float weight_scale[], float input_scale,
+                                  void* const y_bf16[], const void* q_norm_weight, const void* k_norm_weight,
+                                  const float* cos, const float* sin, float eps, hipStream_t stream);
+
+/*
  * Dynamic per-tensor activation quantization: the scale comes from the
  * tensor itself at run time instead of a calibrated checkpoint value (the
  * dynamically quantized FP8 path the pages keep beside the static one,

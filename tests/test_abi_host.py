@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -376,3 +376,25 @@ def test_qk_norm_rope_validation(lib):
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_QK_NORM_ROPE)
     assert qkn(lib, t=0, q=None, k=None, qo=None, ko=None, c=None, s=None) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_QK_NORM_ROPE) == before
+
+
+def qnr(lib, nproj=3, n=(256, 256, 256), qx=FAKE, M=4, K=64, c=FAKE, s=FAKE, wq=None, eps=1e-6, si=0.01):
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    k = len(n)
+    return lib.fp8lin_qkv_w8a8_norm_rope(qx, M, K, nproj, (vp * k)(*[FAKE] * k), (i64 * k)(*n), (f32 * k)(*[0.001] * k),
+                                         si, (vp * k)(*[FAKE] * k), wq, None, c, s, eps, None)
+
+
+def test_qkv_norm_rope_validation(lib):
+    assert qnr(lib, nproj=1, n=(256,)) == fp8lin.EINVAL
+    assert qnr(lib, nproj=4, n=(256,) * 4) == fp8lin.EINVAL
+    assert qnr(lib, n=(192, 256, 256)) == fp8lin.ELAYOUT  # Q not whole heads of 128
+    assert qnr(lib, n=(256, 200, 256)) == fp8lin.ELAYOUT
+    assert qnr(lib, c=None) == fp8lin.EINVAL
+    assert qnr(lib, s=FAKE + 4) == fp8lin.ELAYOUT
+    assert qnr(lib, wq=FAKE + 2) == fp8lin.ELAYOUT
+    assert qnr(lib, eps=0.0) == fp8lin.EINVAL
+    assert qnr(lib, si=0.0) == fp8lin.ESCALE
+    before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
+    assert qnr(lib, M=0, qx=None, c=None, s=None) == fp8lin.OK
+    assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before

@@ -120,3 +120,52 @@ def test_on_the_qkv_group_outputs(gpu):
     qo, ko = fp8lin.fp8lin_qk_norm_rope(outs[0], outs[1], wq.to(gpu), wk.to(gpu), c.to(gpu), s.to(gpu), d, EPS)
     check(outs[0], qo, n // d, wq, c, s, "q of the group")
     check(outs[1], ko, n // d, wk, c, s, "k of the group")
+
+
+# ------------------------------------------- fused into the QKV GEMM epilogue
+
+
+@pytest.mark.parametrize("m,kdim,n,nproj", [(600, 1024, 1024, 3), (300, 528, 384, 3), (77, 64, 128, 2),
+                                            (16384, 4096, 4096, 3)])
+def test_fused_qkv_norm_rope(gpu, m, kdim, n, nproj):
+    """Q and K normalized and rotated in the grouped GEMM's epilogue: within the bound of the exact
+    norm + RoPE of the plain grouped GEMM's own bf16 outputs; V equal to the plain output bit for bit."""
+    announce("qkv_w8a8_norm_rope m=%d k=%d n=%d nproj=%d" % (m, kdim, n, nproj))
+    d = 128
+    case = config3(m=m, k=kdim, n=n)
+    qws = [fp8lin.fp8lin_quantize_static(w.to(gpu), sw) for w, sw in zip(case.ws, case.weight_scales)][:nproj]
+    sws = case.weight_scales[:nproj]
+    qx = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    plain = fp8lin.fp8lin_gemm_w8a8_group(qx, qws, case.input_scale, sws)
+    wq, wk = norm_weight_bf16(d, 251), norm_weight_bf16(d, 252)
+    c, s = rope_tables(m, d, offset=3)
+    c0 = [fp8lin.fp8lin_launch_count(i) for i in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_QK_NORM_ROPE)]
+    fused = fp8lin.fp8lin_qkv_w8a8_norm_rope(qx, qws, case.input_scale, sws, wq.to(gpu), wk.to(gpu), c.to(gpu),
+                                             s.to(gpu), EPS)
+    c1 = [fp8lin.fp8lin_launch_count(i) for i in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_QK_NORM_ROPE)]
+    assert [b - a for a, b in zip(c0, c1)] == [1, 0]
+    torch.cuda.synchronize()
+    if nproj == 3:
+        assert torch.equal(fused[2], plain[2])
+    rows = sample_rows(m, 64, 12) if m > 4096 else np.arange(m)
+    check(plain[0][rows], fused[0][rows], n // d, wq, c[rows], s[rows], "fused q")
+    check(plain[1][rows], fused[1][rows], n // d, wk, c[rows], s[rows], "fused k")
+
+
+def test_fused_qkv_norm_rope_unit_weight_and_standalone_agree(gpu):
+    """No weight = unit weight, and the fused and standalone forms differ by at most one bf16 ulp."""
+    announce("qkv_w8a8_norm_rope vs qk_norm_rope")
+    m, kdim, n, d = 513, 1024, 512, 128
+    case = config3(m=m, k=kdim, n=n)
+    qws = [fp8lin.fp8lin_quantize_static(w.to(gpu), sw) for w, sw in zip(case.ws, case.weight_scales)]
+    qx = fp8lin.fp8lin_quantize_static(case.x.to(gpu), case.input_scale)
+    c, s = (v.to(gpu) for v in rope_tables(m, d))
+    ones = torch.ones(d, dtype=torch.bfloat16, device=gpu)
+    a = fp8lin.fp8lin_qkv_w8a8_norm_rope(qx, qws, case.input_scale, case.weight_scales, ones, ones, c, s, EPS)
+    b = fp8lin.fp8lin_qkv_w8a8_norm_rope(qx, qws, case.input_scale, case.weight_scales, None, None, c, s, EPS)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    plain = fp8lin.fp8lin_gemm_w8a8_group(qx, qws, case.input_scale, case.weight_scales)
+    qs, ks = fp8lin.fp8lin_qk_norm_rope(plain[0], plain[1], ones, ones, c, s, d, EPS)
+    for fused, sep in ((a[0], qs), (a[1], ks)):
+        diff = np.abs(f64(fused) - f64(sep))
+        assert np.all(diff <= bf16.ulp(np.abs(f64(sep))))

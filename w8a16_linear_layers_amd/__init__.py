@@ -42,6 +42,7 @@ __all__ = [
     "fp8lin_quantize_dynamic",
     "fp8lin_gemm_w8a8_dev_scale",
     "fp8lin_qk_norm_rope",
+    "fp8lin_qkv_w8a8_norm_rope",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -100,6 +101,7 @@ EXPORTS = (
     "fp8lin_quantize_dynamic",
     "fp8lin_gemm_w8a8_dev_scale",
     "fp8lin_qk_norm_rope",
+    "fp8lin_qkv_w8a8_norm_rope",
     "fp8lin_policy_validate",
     "fp8lin_step_policy",
     "fp8lin_strerror",
@@ -166,6 +168,10 @@ def load_library():
     lib.fp8lin_quantize_dynamic.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.fp8lin_gemm_w8a8_dev_scale.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, f32, vp]
     lib.fp8lin_qk_norm_rope.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, f32, vp]
+    lib.fp8lin_qkv_w8a8_norm_rope.argtypes = [
+        vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32), f32, ctypes.POINTER(vp),
+        vp, vp, vp, vp, f32, vp,
+    ]
     lib.fp8lin_policy_validate.argtypes = [ctypes.POINTER(Policy)]
     lib.fp8lin_step_policy.argtypes = [ctypes.POINTER(Policy), i32, i32, i32, ctypes.POINTER(i32)]
     lib.fp8lin_strerror.argtypes = [i32]
@@ -447,6 +453,25 @@ def fp8lin_qk_norm_rope(q, k, q_weight, k_weight, cos, sin, head_dim, eps=1e-6, 
         "fp8lin_qk_norm_rope",
     )
     return q_out, k_out
+
+
+def fp8lin_qkv_w8a8_norm_rope(qx, qws, input_scale, weight_scales, q_weight, k_weight, cos, sin, eps=1e-6,
+                              outs=None, stream=None):
+    """Grouped W8A8 Q, K (, V) projections with the per-head (128) RMSNorm + RoPE on Q and K in the epilogue."""
+    m, k = _rows(qx)
+    n = len(qws)
+    if outs is None:
+        outs = [torch.empty(tuple(qx.shape[:-1]) + (w.shape[0],), dtype=torch.bfloat16, device=qx.device) for w in qws]
+    vp, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    _check(
+        load_library().fp8lin_qkv_w8a8_norm_rope(
+            _ptr(qx), m, k, n, (vp * n)(*[w.data_ptr() for w in qws]), (i64 * n)(*[w.shape[0] for w in qws]),
+            (f32 * n)(*[float(s) for s in weight_scales]), float(input_scale), (vp * n)(*[o.data_ptr() for o in outs]),
+            _ptr(q_weight), _ptr(k_weight), _ptr(cos), _ptr(sin), float(eps), _stream(stream)
+        ),
+        "fp8lin_qkv_w8a8_norm_rope",
+    )
+    return outs
 
 
 def fp8lin_quantize_dynamic(x, out=None, scale=None, workspace=None, stream=None):

@@ -294,6 +294,47 @@ int32_t fp8lin_gemm_w8a8_group(const void* qx, int64_t M, int64_t K, int32_t npr
   return hip_status(fp8lin::launch_gemm_w8a8(a, stream));
 }
 
+int32_t fp8lin_qkv_w8a8_norm_rope(const void* qx, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
+                                  const int64_t n_out[], const float weight_scale[], float input_scale,
+                                  void* const y_bf16[], const void* q_norm_weight, const void* k_norm_weight,
+                                  const float* cos, const float* sin, float eps, hipStream_t stream) {
+  if (qw == nullptr || n_out == nullptr || weight_scale == nullptr || y_bf16 == nullptr) return FP8LIN_EINVAL;
+  if (nproj < 2 || nproj > 3) return FP8LIN_EINVAL;
+  if (!std::isfinite(eps) || !(eps > 0.0f)) return FP8LIN_EINVAL;
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && (qx == nullptr || cos == nullptr || sin == nullptr))) return FP8LIN_EINVAL;
+  if (!aligned16(qx) || !aligned16(cos) || !aligned16(sin) || !aligned16(q_norm_weight) ||
+      !aligned16(k_norm_weight))
+    return FP8LIN_ELAYOUT;
+  if (!scale_ok(input_scale)) return FP8LIN_ESCALE;
+  GemmArgs a{};
+  a.x = qx;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ngroups = nproj;
+  for (int i = 0; i < nproj; ++i) {
+    if ((st = check_output(qw[i], y_bf16[i], n_out[i], n_out[i], M)) != FP8LIN_OK) return st;
+    if (i < 2 && n_out[i] % 128 != 0) return FP8LIN_ELAYOUT;  // whole heads of 128
+    if (!scale_ok(weight_scale[i])) return FP8LIN_ESCALE;
+    a.g[i].w = static_cast<const uint8_t*>(qw[i]);
+    a.g[i].y = y_bf16[i];
+    a.g[i].n = (int32_t)n_out[i];
+    a.g[i].ldy = (int32_t)n_out[i];
+    a.g[i].alpha = input_scale * weight_scale[i];
+    if (!std::isfinite(a.g[i].alpha) || a.g[i].alpha == 0.0f) return FP8LIN_ESCALE;
+  }
+  a.nr_w[0] = static_cast<const uint16_t*>(q_norm_weight);
+  a.nr_w[1] = static_cast<const uint16_t*>(k_norm_weight);
+  a.nr_cos = cos;
+  a.nr_sin = sin;
+  a.nr_eps = eps;
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  if (M == 0) return FP8LIN_OK;
+  count_launch(FP8LIN_KERNEL_GEMM_W8A8);
+  return hip_status(fp8lin::launch_gemm_w8a8_norm_rope(a, stream));
+}
+
 int32_t fp8lin_gate_up_swiglu_w8a8(const void* qx, int64_t M, int64_t K, const void* qw_gate, const void* qw_up,
                                    int64_t I, float input_scale, float gate_scale, float up_scale, float out_scale,
                                    void* h_e4m3, hipStream_t stream) {

@@ -355,6 +355,99 @@ __device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j
   }
 }
 
+// bf16 rounding of a float32 value, back as float32 (exact).
+__device__ __forceinline__ float bf16_round(float v) { return bf16_lo(bf16x2(v, 0.0f)); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// epilogue_rows for a 128-column block that is one head of a Q or K
+// projection: y = bf16(acc * alpha), the value the plain epilogue writes,
+// then per row the head's RMSNorm and rotate-half RoPE in float32
+// (r = rsqrt(sum(y^2) / 128 + eps); out[d] = y[d] r w[d] cos[t, d] -
+// y[d + 64] r w[d + 64] sin[t, d], out[d + 64] = y[d + 64] r w[d + 64]
+// cos[t, d] + y[d] r w[d] sin[t, d] for d < 64), rounded to bf16 and stored
+// like epilogue_rows. Lane (m, h) holds columns 32 i + 8 t + 4 h + e of row
+// m, lane m + 32 the rest of the row (one butterfly step completes the sum
+// of squares), and the RoPE partner of a column of block i < 2 is the same
+// position of block i + 2 in the same lane. row0: the first output row of
+// the wave's tile (rows at or past M are never stored; their table row is
+// clamped to M - 1). With active = false (a V tile) r = 1, w = 1 and no
+// rotation, which reproduces epilogue_rows bit for bit: one code path for
+// every tile of the launch (a second epilogue body in the same kernel costs
+// ~25 spilled registers).
+__device__ __forceinline__ void epilogue_rows_norm_rope(const v16f (&acc)[4][4], int j, uint8_t* stage,
+                                                        const GemmGroup& grp, float alpha,
+                                                        __amdgpu_buffer_rsrc_t out, int n_base, int lane, int row0,
+                                                        int M, bool active, const uint16_t* w, const float* cos,
+                                                        const float* sin, float eps) {
+  asm volatile("" : "+v"(lane));
+  const int h = lane >> 5;
+  const int m = lane & 31;
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float y = bf16_round(acc[i][j][k] * alpha);
+      ss += y * y;
+    }
+  ss += __shfl_xor(ss, 32);
+  const float r = active ? rsqrtf(ss * (1.0f / 128) + eps) : 1.0f;
+  // an opaque copy of alpha: the second pass recomputes y from the
+  // accumulators instead of keeping the first pass's 64 values alive
+  float alpha2 = alpha;
+  asm volatile("" : "+v"(alpha2));
+  const int token = min(row0 + 32 * j + m, M - 1);
+  const float* cr = cos + (int64_t)token * 64;
+  const float* sr = sin + (int64_t)token * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int d = 32 * i + 8 * t + 4 * h;
+      f32x4 c = {1.0f, 1.0f, 1.0f, 1.0f}, s = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (active) {
+        c = *reinterpret_cast<const f32x4*>(cr + d);
+        s = *reinterpret_cast<const f32x4*>(sr + d);
+      }
+      float wa[4] = {1.0f, 1.0f, 1.0f, 1.0f}, wb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (active && w != nullptr) {
+        const u32x2 ga = *reinterpret_cast<const u32x2*>(w + d);
+        const u32x2 gb = *reinterpret_cast<const u32x2*>(w + d + 64);
+        wa[0] = bf16_lo(ga.x); wa[1] = bf16_hi(ga.x); wa[2] = bf16_lo(ga.y); wa[3] = bf16_hi(ga.y);
+        wb[0] = bf16_lo(gb.x); wb[1] = bf16_hi(gb.x); wb[2] = bf16_lo(gb.y); wb[3] = bf16_hi(gb.y);
+      }
+      float oa[4], ob[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ya = bf16_round(acc[i][j][4 * t + e] * alpha2) * r * wa[e];
+        const float yb = bf16_round(acc[i + 2][j][4 * t + e] * alpha2) * r * wb[e];
+        oa[e] = active ? ya * c[e] - yb * s[e] : ya;  // inactive: no cross term (an inf stays inf)
+        ob[e] = active ? yb * c[e] + ya * s[e] : yb;
+      }
+      const int ca = i * 4 + t, cb = (i + 2) * 4 + t;  // 16-byte chunks of the staged row, as in epilogue_rows
+      *reinterpret_cast<u32x2*>(stage + m * 256 + ((ca ^ (m & 15)) * 16) + h * 8) =
+          u32x2{bf16x2(oa[0], oa[1]), bf16x2(oa[2], oa[3])};
+      *reinterpret_cast<u32x2*>(stage + m * 256 + ((cb ^ (m & 15)) * 16) + h * 8) =
+          u32x2{bf16x2(ob[0], ob[1]), bf16x2(ob[2], ob[3])};
+    }
+  }
+  const int c = lane & 15;
+  const int n = n_base + c * 8;
+  u32x4 v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int ml = q * 4 + (lane >> 4);
+    v[q] = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) * 16));
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int ml = 32 * j + q * 4 + (lane >> 4);
+    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kStreamStore);
+  }
+}
+
 // ------------------------------------------------------------------ W8A8
 
 // 32 x 64 E4M3 fragment of k-step h (0 or 1) of rows [row, row + 32) of a
@@ -558,7 +651,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(void* h, int M, int m_b
 // the up rows of those columns (a.g[0]: gate, h output, alpha s_in s_gate;
 // a.g[1]: up, alpha s_in s_up; a.out_rs = 1 / s_h), so the accumulators of
 // waves (wm, 0) and (wm, 1) are g and u of the same block.
-template <bool kSwiGLU>
+// kNormRope: groups 0 and 1 (Q and K, heads of 128 columns) take the
+// per-head RMSNorm + RoPE epilogue (a.nr_*), the other groups the plain one.
+template <bool kSwiGLU, bool kNormRope = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a8_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -653,8 +748,18 @@ gemm_w8a8_kernel(const GemmArgs a) {
         epilogue_swiglu<true>(acc, j, lds_mem + kW8A8EpiOffset, wm, wn, alpha, a.out_rs, out, cur.n0, I, lane);
     } else {
       const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
+      if constexpr (kNormRope) {
+        const bool active = cur.group < 2;
+        const uint16_t* nw = cur.group == 0 ? a.nr_w[0] : a.nr_w[1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) epilogue_rows(acc, j, epi, grp, grp.alpha * alpha_mul, out, cur.n0 + wn * 128, lane);
+        for (int j = 0; j < 4; ++j)
+          epilogue_rows_norm_rope(acc, j, epi, grp, grp.alpha, out, cur.n0 + wn * 128, lane, cur.m0 + wm * 128, a.m,
+                                  active, nw, a.nr_cos, a.nr_sin, a.nr_eps);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          epilogue_rows(acc, j, epi, grp, grp.alpha * alpha_mul, out, cur.n0 + wn * 128, lane);
+      }
     }
     if (next >= a.total_tiles) break;
     slot = next;
@@ -968,6 +1073,15 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
   hipLaunchKernelGGL(gemm_w8a8_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w8a8_norm_rope(const GemmArgs& a, hipStream_t s) {
+  static const int cus = cu_count();
+  int grid = cus - cus % kXcds;
+  if (grid <= 0) grid = kXcds;
+  if (grid > a.total_tiles) grid = a.total_tiles;
+  hipLaunchKernelGGL((gemm_w8a8_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

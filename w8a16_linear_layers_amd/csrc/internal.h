@@ -38,6 +38,13 @@ struct GemmArgs {
   float out_rs;   // fused gate/up + SwiGLU: 1 / s_h (the down projection's input scale)
   GemmGroup g[kMaxGroups];
   const float* in_scale_dev;  // W8A8 with a device input scale: alpha = g.alpha * *in_scale_dev
+  // W8A8 with the per-head QK RMSNorm + RoPE epilogue on groups 0 and 1
+  // (heads of 128 columns): bf16 norm weights (null: 1), float32 cos/sin
+  // tables [m, 64], epsilon
+  const uint16_t* nr_w[2];
+  const float* nr_cos;
+  const float* nr_sin;
+  float nr_eps;
 };
 
 // Fills tile_begin / tiles_n / tiles_m / total_tiles from m, n of each group.
@@ -53,6 +60,8 @@ hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipSt
 hipError_t launch_quantize_dynamic(const void* x, void* q, int64_t n, uint32_t* amax_ws, float* scale_out,
                                    hipStream_t s);
 hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
+// The same grouped launch with the QK RMSNorm + RoPE epilogue on groups 0, 1.
+hipError_t launch_gemm_w8a8_norm_rope(const GemmArgs& a, hipStream_t s);
 // W8A16 activation forms: bf16, binary16, float32 as three bf16 pieces
 constexpr int kW16Bf16 = 0, kW16F16 = 1, kW16F32 = 2;
 hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s);
