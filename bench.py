@@ -160,8 +160,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(
-            "bench.py measures one MI355X: the static-FP8 linear layer has no cross-GPU exchange in this build "
-            "(--gpus %d, WORLD_SIZE %d requested). Run with --gpus 1." % (args.gpus, world),
+            "bench.py measures one MI355X: the static-FP8 linear layer is benchmarked on a single GPU, with no "
+            "cross-GPU exchange (--gpus %d, WORLD_SIZE %d requested). Run with --gpus 1." % (args.gpus, world),
             file=sys.stderr,
         )
         sys.exit(2)

@@ -237,7 +237,7 @@ def test_gemm_w8a16_f32(gpu, m, n, k):
 
 def test_gemm_w8a16_f32_is_float32_accurate(gpu):
     """Far closer to the exact product than the bf16-activation path (which
-    would pass the benchmark spec's tolerance but not this)."""
+    would pass the GEMM tolerance but not this)."""
     announce("gemm_w8a16 f32 accuracy")
     m, n, k = 256, 256, 1024
     x = normal_f32((m, k), 0.35, 103)
