@@ -112,16 +112,29 @@ __device__ __forceinline__ uint32_t quant_word_exact(uint32_t w, float s, float 
   return quant_one_exact(w & 0xffffu, s, r, exact_ok) | (quant_one_exact(w >> 16, s, r, exact_ok) << 8);
 }
 
+// e^x on the exp2 instruction (v_exp_f32): x log2(e) = hi + lo, with hi =
+// fl32(x L) and lo its rounding error recovered by an FMA plus x times the
+// tail of log2(e), and e^x = 2^hi (1 + lo ln 2) to first order in lo (|lo|
+// <= 2^-17). About 2 float32 ulp in all (the instruction's 1 ulp, two
+// roundings); overflow gives inf and underflow 0, with no NaN in between.
+__device__ __forceinline__ float exp_via_exp2(float x) {
+  constexpr float kL = 0x1.715476p+0f;       // log2(e) rounded to float32
+  constexpr float kLtail = 0x1.4ae0cp-26f;   // log2(e) - kL
+  constexpr float kLn2 = 0x1.62e43p-1f;
+  const float hi = x * kL;
+  const float lo = fmaf(x, kLtail, fmaf(x, kL, -hi));
+  return __builtin_amdgcn_exp2f(hi) * fmaf(lo, kLn2, 1.0f);
+}
+
 // SwiGLU element rule ([TRT-17476] "What changed": silu(g) * u in float32
-// from the two bf16 inputs, emitted as E4M3 with the down projection's
-// static input scale). silu(g) * u = g * u / (1 + exp(-g)): expf is the
-// accurate (about 1 ulp) libm exponential, so h stays within a few float32
-// ulp of the exact value for every finite input; a very negative gate gives
-// exp(-g) = inf and h = -0 or 0, a large gate gives g * u. Shared by the
-// two-input SwiGLU kernel and the fused gate/up epilogue, so both produce
-// the same codes from the same bf16 inputs.
+// from the two 16-bit inputs, emitted as E4M3 with the down projection's
+// static input scale). silu(g) * u = g * u / (1 + exp(-g)), so h stays
+// within a few float32 ulp of the exact value for every finite input; a
+// very negative gate gives exp(-g) = inf and h = -0 or 0, a large gate gives
+// g * u. Shared by the two-input SwiGLU kernel and the fused gate/up
+// epilogue, so both produce the same codes from the same inputs.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = expf(-g);
+  const float e = exp_via_exp2(-g);
   return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
@@ -130,6 +143,20 @@ __device__ __forceinline__ uint32_t swiglu_code(float h, float rs) {
   const float t = h * rs;
   if (__builtin_isnan(t)) return 0x7fu | ((__float_as_uint(t) >> 24) & 0x80u);
   return e4m3_code(clamp448(t));
+}
+
+// The codes of h[0..3] * rs in one word (byte k from h[k]), by the rule of
+// swiglu_code: two packed converts of the clamped values; a word holding a
+// NaN (rare; their sum is then NaN, as it is for +inf + -inf) is redone
+// element by element.
+__device__ __forceinline__ uint32_t swiglu_codes4(float h0, float h1, float h2, float h3, float rs) {
+  const float t0 = h0 * rs, t1 = h1 * rs, t2 = h2 * rs, t3 = h3 * rs;
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(t0), clamp448(t1), 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(t2), clamp448(t3), (int)w, true);
+  const float probe = (t0 + t1) + (t2 + t3);
+  if (__builtin_isnan(probe))
+    w = swiglu_code(h0, rs) | (swiglu_code(h1, rs) << 8) | (swiglu_code(h2, rs) << 16) | (swiglu_code(h3, rs) << 24);
+  return w;
 }
 
 }  // namespace fp8lin

@@ -614,8 +614,7 @@ __device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, 
       u32x4 codes;
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        codes[w] = swiglu_code(hv[4 * w], rs) | (swiglu_code(hv[4 * w + 1], rs) << 8) |
-                   (swiglu_code(hv[4 * w + 2], rs) << 16) | (swiglu_code(hv[4 * w + 3], rs) << 24);
+        codes[w] = swiglu_codes4(hv[4 * w], hv[4 * w + 1], hv[4 * w + 2], hv[4 * w + 3], rs);
       __builtin_amdgcn_raw_buffer_store_b128(codes, out, (int)o, 0, 0);
     } else {
       u32x4 lo, hi;

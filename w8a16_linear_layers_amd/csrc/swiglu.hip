@@ -27,10 +27,8 @@ __device__ __forceinline__ void swiglu8(const u32x4 gv, const u32x4 uv, void* ou
   }
   if constexpr (kFp8Out) {
     u32x2 o;
-    o.x = swiglu_code(h[0], rs) | (swiglu_code(h[1], rs) << 8) | (swiglu_code(h[2], rs) << 16) |
-          (swiglu_code(h[3], rs) << 24);
-    o.y = swiglu_code(h[4], rs) | (swiglu_code(h[5], rs) << 8) | (swiglu_code(h[6], rs) << 16) |
-          (swiglu_code(h[7], rs) << 24);
+    o.x = swiglu_codes4(h[0], h[1], h[2], h[3], rs);
+    o.y = swiglu_codes4(h[4], h[5], h[6], h[7], rs);
     __builtin_nontemporal_store(o, static_cast<u32x2*>(out) + i);
   } else {
     u32x4 o;
