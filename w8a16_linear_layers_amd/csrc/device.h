@@ -86,11 +86,14 @@ __device__ __forceinline__ uint32_t pick_codes(uint32_t p0, uint32_t p1) {
 // where every candidate code is a signed zero, or overflows, where the
 // quotient saturates either way) and needs no bracket. Only a NaN input
 // sets `doubt`.
-__device__ __forceinline__ uint32_t quant_pair_pow2(uint32_t w, float r, uint32_t& doubt) {
-  uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_lo(w) * r), 0.0f, 0, false);
-  p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_hi(w) * r), 0.0f, (int)p, true);
-  doubt |= ((w & 0x7fff7fffu) + 0x007f007fu) & 0x80008000u;
-  return p;  // codes in bytes 0 and 2, like quant_pair_fast
+// The four codes of two such words (bytes 0-3 from w0 lo, w0 hi, w1 lo,
+// w1 hi): two packed converts, no byte shuffling.
+__device__ __forceinline__ uint32_t quant_quad_pow2(uint32_t w0, uint32_t w1, float r, uint32_t& doubt) {
+  uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_lo(w0) * r), clamp448(bf16_hi(w0) * r), 0,
+                                                         false);
+  p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_lo(w1) * r), clamp448(bf16_hi(w1) * r), (int)p, true);
+  doubt |= (((w0 & 0x7fff7fffu) + 0x007f007fu) | ((w1 & 0x7fff7fffu) + 0x007f007fu)) & 0x80008000u;
+  return p;
 }
 
 // Exact static quantization of one bf16 value (bits in the low 16 bits).

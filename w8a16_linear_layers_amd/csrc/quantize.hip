@@ -23,21 +23,18 @@ constexpr int kUnroll = 4;  // vectors in flight per thread
 template <bool kPow2>
 __device__ __forceinline__ u32x2 quantize8(const u32x4 v, float s, float r, bool exact_ok) {
   uint32_t doubt = 0;
-  uint32_t p0, p1, p2, p3;
-  if constexpr (kPow2) {
-    p0 = quant_pair_pow2(v.x, r, doubt);
-    p1 = quant_pair_pow2(v.y, r, doubt);
-    p2 = quant_pair_pow2(v.z, r, doubt);
-    p3 = quant_pair_pow2(v.w, r, doubt);
-  } else {
-    p0 = quant_pair_fast(v.x, r, doubt);
-    p1 = quant_pair_fast(v.y, r, doubt);
-    p2 = quant_pair_fast(v.z, r, doubt);
-    p3 = quant_pair_fast(v.w, r, doubt);
-  }
   u32x2 out;
-  out.x = pick_codes(p0, p1);
-  out.y = pick_codes(p2, p3);
+  if constexpr (kPow2) {
+    out.x = quant_quad_pow2(v.x, v.y, r, doubt);
+    out.y = quant_quad_pow2(v.z, v.w, r, doubt);
+  } else {
+    const uint32_t p0 = quant_pair_fast(v.x, r, doubt);
+    const uint32_t p1 = quant_pair_fast(v.y, r, doubt);
+    const uint32_t p2 = quant_pair_fast(v.z, r, doubt);
+    const uint32_t p3 = quant_pair_fast(v.w, r, doubt);
+    out.x = pick_codes(p0, p1);
+    out.y = pick_codes(p2, p3);
+  }
   if (doubt) {
     out.x = quant_word_exact(v.x, s, r, exact_ok) | (quant_word_exact(v.y, s, r, exact_ok) << 16);
     out.y = quant_word_exact(v.z, s, r, exact_ok) | (quant_word_exact(v.w, s, r, exact_ok) << 16);
