@@ -497,7 +497,14 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
         f = 2.0 * m * N * K
         a = timed(lambda: fp8lin.fp8lin_gemm_w8a8(q2[:m], qw2, c2.input_scale, c2.weight_scale, out=y2), reps)
         b = timed(lambda: fp8lin.fp8lin_gemm_w8a16(x2[:m], qw2, c2.weight_scale, out=y2), reps)
-        rows["proj_%dx4096x4096" % m] = {"w8a8_tflops": round(f / a / 1e9, 1), "w8a16_tflops": round(f / b / 1e9, 1)}
+        row = {"w8a8_tflops": round(f / a / 1e9, 1), "w8a16_tflops": round(f / b / 1e9, 1)}
+        sk = fp8lin.fp8lin_gemm_w8a8_splitk_choice(m, K, K)
+        if sk > 1:  # too few output tiles to fill the device: K split into float32 partials
+            ws_sk = torch.empty(sk * m * K * 4, dtype=torch.uint8, device=dev)
+            c = timed(lambda: fp8lin.fp8lin_gemm_w8a8_splitk(q2[:m], qw2, c2.input_scale, c2.weight_scale,
+                                                             splits=sk, out=y2, workspace=ws_sk), reps)
+            row["w8a8_splitk"] = {"splits": sk, "tflops": round(f / c / 1e9, 1)}
+        rows["proj_%dx4096x4096" % m] = row
 
     # step policy: host call per transformer forward
     pol = fp8lin.policy_from_json({"schema_version": 1, "type": "first_last_steps", "index_space": "scheduler_step",

@@ -188,6 +188,34 @@ int32_t fp8lin_gemm_w8a16_f32(const void* x_f32, const void* qw, void* y_f32, in
 int64_t fp8lin_w8a16_f32_workspace_bytes(int64_t M, int64_t K);
 
 /*
+ * fp8lin_gemm_w8a8 with the K dimension split into `splits` slices, for
+ * shapes whose 256 x 256 output tiles are too few to fill the device (at
+ * M = 1024, N = 4096: 64 tiles for 256 compute units). Each slice's product
+ * goes, unscaled, in float32 to its part of the workspace; a second kernel
+ * sums the parts in slice order and writes
+ *   y[m, n] = bf16_RNE( (sum_s partial_s[m, n]) * (input_scale * weight_scale) )
+ * (the float32 summation order differs from fp8lin_gemm_w8a8's, so the two
+ * may differ in the last bf16 bit; both meet the same tolerance).
+ *   splits     1 (plain fp8lin_gemm_w8a8, workspace unused), 2 or 4; K a
+ *              multiple of 16 * splits (else FP8LIN_ELAYOUT)
+ *   workspace  device, >= splits * M * N * 4 bytes, 16-byte aligned,
+ *              caller-owned scratch (else FP8LIN_EINVAL)
+ * Other arguments and rules as fp8lin_gemm_w8a8. Launches counted as
+ * FP8LIN_KERNEL_GEMM_W8A8 and FP8LIN_KERNEL_SPLITK_REDUCE.
+ */
+int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+                                int64_t ldy, float input_scale, float weight_scale, int32_t splits, void* workspace,
+                                int64_t workspace_bytes, hipStream_t stream);
+
+/* The split count fp8lin_gemm_w8a8_splitk does best with on the current
+ * device: doubled from 1 (up to 4) while the tiles of all slices still fill
+ * at most half the compute units and every slice keeps at least 512 K bytes
+ * (the reduction re-reads splits * M * N * 4 bytes, so more, shorter slices
+ * lose: at 1024 x 4096 x 4096 this gives 2).
+ * Host only (it reads the device's compute-unit count once). */
+int32_t fp8lin_gemm_w8a8_splitk_choice(int64_t M, int64_t N, int64_t K);
+
+/*
  * The GEMMs of a shared-input projection group on an activation quantized
  * once ([TRT-17476] "What changed": every projection of the group consumes
  * the same FP8 tensor, each with its own weight_scale), in one launch:
@@ -431,7 +459,8 @@ enum {
   FP8LIN_KERNEL_AMAX = 5,
   FP8LIN_KERNEL_SPLIT = 6, /* float32 activation -> three bf16 pieces */
   FP8LIN_KERNEL_QK_NORM_ROPE = 7,
-  FP8LIN_KERNEL_KINDS = 8
+  FP8LIN_KERNEL_SPLITK_REDUCE = 8, /* sum of split-K partials */
+  FP8LIN_KERNEL_KINDS = 9
 };
 
 /* Number of kernels of `kind` this process has enqueued through the library

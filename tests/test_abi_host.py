@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -44,7 +44,7 @@ def test_strerror_covers_every_status():
 
 def test_launch_count_rejects_unknown_kind():
     assert fp8lin.fp8lin_launch_count(-1) == -1
-    assert fp8lin.fp8lin_launch_count(8) == -1
+    assert fp8lin.fp8lin_launch_count(9) == -1
     assert fp8lin.fp8lin_launch_count(0) >= 0
 
 
@@ -398,3 +398,24 @@ def test_qkv_norm_rope_validation(lib):
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
     assert qnr(lib, M=0, qx=None, c=None, s=None) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before
+
+
+def gsk(lib, M=4, N=64, K=256, ldy=64, splits=2, ws=FAKE, wsb=None, si=0.01, sw=0.001, qx=FAKE):
+    if wsb is None:
+        wsb = splits * M * N * 4
+    return lib.fp8lin_gemm_w8a8_splitk(qx, FAKE, FAKE, M, N, K, ldy, si, sw, splits, ws, wsb, None)
+
+
+def test_gemm_splitk_validation(lib):
+    assert gsk(lib, splits=3) == fp8lin.EINVAL
+    assert gsk(lib, splits=8) == fp8lin.EINVAL
+    assert gsk(lib, K=16 * 4 + 16, splits=4) == fp8lin.ELAYOUT  # K not a multiple of 16 * splits
+    assert gsk(lib, wsb=2 * 4 * 64 * 4 - 1) == fp8lin.EINVAL
+    assert gsk(lib, ws=None) == fp8lin.EINVAL
+    assert gsk(lib, ws=FAKE + 8) == fp8lin.ELAYOUT
+    assert gsk(lib, si=0.0) == fp8lin.ESCALE
+    assert gsk(lib, ldy=32) == fp8lin.ELAYOUT
+    before = [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)]
+    assert gsk(lib, M=0, qx=None, ws=None, wsb=0) == fp8lin.OK
+    assert gsk(lib, M=0, qx=None, splits=1) == fp8lin.OK
+    assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)] == before

@@ -12,9 +12,10 @@ import pytest
 import torch
 
 import w8a16_linear_layers_amd as fp8lin
+from oracle import bf16 as obf16
 from oracle import linear
 from tests.helpers import announce, assert_gemm_close, f32, sample_rows, u8
-from workloads import config1, config2, config3, normal_bf16, random_e4m3_codes
+from workloads import config1, config2, config3, max_calibrated_scale, normal_bf16, random_e4m3_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +192,43 @@ def test_repeated_launches_are_bit_identical(gpu, kind):
         again = run()
         torch.cuda.synchronize()
         assert torch.equal(first.view(torch.uint8), again.view(torch.uint8))
+
+
+# ---------------------------------------------------------------- split-K
+
+
+@pytest.mark.parametrize("m,n,k,splits", [(1024, 4096, 4096, 4), (1024, 4096, 4096, 2), (300, 528, 1024, 4),
+                                          (77, 64, 128, 2)])
+def test_gemm_w8a8_splitk(gpu, m, n, k, splits):
+    """K split into float32 partials, summed in slice order: the oracle's tolerance, within one bf16 ulp of
+    the unsplit GEMM, and nothing written past the partials."""
+    announce("gemm_w8a8_splitk m=%d n=%d k=%d splits=%d" % (m, n, k, splits))
+    x = normal_bf16((m, k), 0.35, 61)
+    w = normal_bf16((n, k), 0.02, 62)
+    s_in, s_w = max_calibrated_scale(x), max_calibrated_scale(w)
+    qx = fp8lin.fp8lin_quantize_static(x.to(gpu), s_in)
+    qw = fp8lin.fp8lin_quantize_static(w.to(gpu), s_w)
+    need = splits * m * n * 4
+    ws = torch.full((need + 256,), 0x5A, dtype=torch.uint8, device=gpu)
+    c0 = [fp8lin.fp8lin_launch_count(i) for i in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)]
+    y = fp8lin.fp8lin_gemm_w8a8_splitk(qx, qw, s_in, s_w, splits=splits, workspace=ws)
+    c1 = [fp8lin.fp8lin_launch_count(i) for i in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)]
+    assert [b - a for a, b in zip(c0, c1)] == [1, 1]
+    y_plain = fp8lin.fp8lin_gemm_w8a8(qx, qw, s_in, s_w)
+    torch.cuda.synchronize()
+    assert torch.all(ws[need:] == 0x5A)
+    rows = sample_rows(m, 96, 21) if m > 512 else np.arange(m)
+    qr = linear.quantize_static(f32(x)[rows], s_in)
+    qwr = linear.quantize_static(f32(w), s_w)
+    assert np.array_equal(u8(qx)[rows], qr)
+    ref = linear.gemm_w8a8(qr, qwr, s_in, s_w)
+    assert_gemm_close(f32(y)[rows], ref, "split-K")
+    a, b = f32(y).astype(np.float64), f32(y_plain).astype(np.float64)
+    assert np.all(np.abs(a - b) <= obf16.ulp(np.maximum(np.abs(a), np.abs(b))))
+
+
+def test_gemm_splitk_choice():
+    """More slices only while the split grid fills at most half the device and slices keep >= 512 K bytes."""
+    assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(16384, 4096, 4096) == 1
+    assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(1024, 4096, 4096) == 2
+    assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(128, 512, 512) == 1

@@ -34,6 +34,8 @@ __all__ = [
     "fp8lin_gemm_w8a16_f32",
     "fp8lin_w8a16_f32_workspace_bytes",
     "fp8lin_gemm_w8a8_group",
+    "fp8lin_gemm_w8a8_splitk",
+    "fp8lin_gemm_w8a8_splitk_choice",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_swiglu_2in",
@@ -55,6 +57,7 @@ __all__ = [
     "KERNEL_AMAX",
     "KERNEL_SPLIT",
     "KERNEL_QK_NORM_ROPE",
+    "KERNEL_SPLITK_REDUCE",
 ]
 
 MODE_W8A8, MODE_W8A16 = 0, 1
@@ -69,7 +72,8 @@ TOWER_GENERATION, TOWER_REASONER = 0, 1
     KERNEL_AMAX,
     KERNEL_SPLIT,
     KERNEL_QK_NORM_ROPE,
-) = range(8)
+    KERNEL_SPLITK_REDUCE,
+) = range(9)
 
 # torch dtype -> fp8lin_dtype (E4M3 codes travel as uint8 or float8_e4m3fn)
 _DT_OF = {
@@ -93,6 +97,8 @@ EXPORTS = (
     "fp8lin_gemm_w8a16_f32",
     "fp8lin_w8a16_f32_workspace_bytes",
     "fp8lin_gemm_w8a8_group",
+    "fp8lin_gemm_w8a8_splitk",
+    "fp8lin_gemm_w8a8_splitk_choice",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_swiglu_2in",
@@ -167,6 +173,8 @@ def load_library():
     lib.fp8lin_gate_up_swiglu_w8a16.argtypes = [vp, i32, i64, i64, vp, vp, i64, f32, f32, vp, vp]
     lib.fp8lin_quantize_dynamic.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.fp8lin_gemm_w8a8_dev_scale.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, f32, vp]
+    lib.fp8lin_gemm_w8a8_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32, vp, i64, vp]
+    lib.fp8lin_gemm_w8a8_splitk_choice.argtypes = [i64, i64, i64]
     lib.fp8lin_qk_norm_rope.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, f32, vp]
     lib.fp8lin_qkv_w8a8_norm_rope.argtypes = [
         vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32), f32, ctypes.POINTER(vp),
@@ -265,6 +273,34 @@ def fp8lin_gemm_w8a16(x, qw, weight_scale, out=None, ldy=None, stream=None):
             _ptr(x), dtype, _ptr(qw), _ptr(out), m, n, k, ldy, float(weight_scale), _stream(stream)
         ),
         "fp8lin_gemm_w8a16",
+    )
+    return out
+
+
+def fp8lin_gemm_w8a8_splitk_choice(m, n, k):
+    """The split count fp8lin_gemm_w8a8_splitk does best with on this device (1 = no split)."""
+    return int(load_library().fp8lin_gemm_w8a8_splitk_choice(int(m), int(n), int(k)))
+
+
+def fp8lin_gemm_w8a8_splitk(qx, qw, input_scale, weight_scale, splits=None, out=None, ldy=None, workspace=None,
+                            stream=None):
+    """fp8lin_gemm_w8a8 with K split into `splits` float32 partial products (default: the device's choice)."""
+    if qx.dtype != torch.uint8 or qw.dtype != torch.uint8:
+        raise TypeError("qx and qw must hold E4M3 codes as torch.uint8")
+    m, k = _rows(qx)
+    n = qw.shape[0]
+    if splits is None:
+        splits = fp8lin_gemm_w8a8_splitk_choice(m, n, k)
+    out, ldy = _gemm_out(qx.shape[:-1], n, qx.device, out, ldy)
+    need = int(splits) * m * n * 4 if splits > 1 else 16
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=qx.device)
+    _check(
+        load_library().fp8lin_gemm_w8a8_splitk(
+            _ptr(qx), _ptr(qw), _ptr(out), m, n, k, ldy, float(input_scale), float(weight_scale), int(splits),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)
+        ),
+        "fp8lin_gemm_w8a8_splitk",
     )
     return out
 

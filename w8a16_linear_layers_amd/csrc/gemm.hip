@@ -256,6 +256,8 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) { return h16x2<fals
 // launch +7.5%, the grouped QKV launch +2%, the split gated MLP 1.07 ->
 // 1.02 ms, no row slower).
 constexpr int kStreamStore = 2;
+// Split-K partials are re-read at once by the reduction: default policy.
+constexpr int kSplitPartialStore = 0;
 
 // acc[i][j] holds D[n][m] of the 32 x 32 block (n-block i, m-block j):
 // lane l, register v -> m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4,
@@ -321,6 +323,7 @@ __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, ui
 // [32 j, 32 j + 32), scaled by alpha, through the same 8 KiB area (two calls
 // per row block; one wave's LDS operations complete in order, so a call's
 // staging writes follow the previous call's reads).
+template <int kPolicy = kStreamStore>
 __device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j, int hf, uint8_t* stage,
                                                   const GemmGroup& grp, float alpha, __amdgpu_buffer_rsrc_t out,
                                                   int n_base, int lane) {
@@ -351,7 +354,7 @@ __device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j
   for (int q = 0; q < 8; ++q) {
     const int ml = 32 * j + q * 4 + (lane >> 4);
     const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 4u : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kStreamStore);
+    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kPolicy);
   }
 }
 
@@ -652,13 +655,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(void* h, int M, int m_b
 // waves (wm, 0) and (wm, 1) are g and u of the same block.
 // kNormRope: groups 0 and 1 (Q and K, heads of 128 columns) take the
 // per-head RMSNorm + RoPE epilogue (a.nr_*), the other groups the plain one.
-template <bool kSwiGLU, bool kNormRope = false>
+// kSplit: split-K; every group is one K slice (a.ks bytes from g.koff, row
+// pitch a.k) of the same product and stores its unscaled float32 partial.
+template <bool kSwiGLU, bool kNormRope = false, bool kSplit = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a8_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.k;
+  const int LD = a.k;                 // row pitch of x and w
+  const int K = kSplit ? a.ks : a.k;  // K bytes this launch's groups multiply
   const int KT = (K + 127) / 128;
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
   const int row_w = wn * 128 + (lane & 31);
@@ -676,14 +682,15 @@ gemm_w8a8_kernel(const GemmArgs a) {
       const int rows = a.g[0].n - t.n0;
       pw.init2(a.g[0].w + off, rows, a.g[1].w + off, rows, K, tid);
     } else {
-      pw.init(a.g[t.group].w, t.n0, a.g[t.group].n - t.n0, K, tid);
+      pw.init(a.g[t.group].w + (kSplit ? a.g[t.group].koff : 0), t.n0, a.g[t.group].n - t.n0, LD, tid);
     }
-    px.init(static_cast<const uint8_t*>(a.x), t.m0, a.m - t.m0, K, tid);
+    px.init(static_cast<const uint8_t*>(a.x) + (kSplit ? a.g[t.group].koff : 0), t.m0, a.m - t.m0, LD, tid);
   };
   constexpr int kTN = kSwiGLU ? kTileN / 2 : kTileN;
-  // buffer stores per thread of one tile's epilogue: 8 per 32-row block,
-  // or 2 for the fused SwiGLU's E4M3 h
-  constexpr int kStores = kSwiGLU ? 8 : 32;
+  // buffer stores per thread of one tile's epilogue: 8 per 32-row block, 16
+  // for float32 partials, or 2 for the fused SwiGLU's E4M3 h; a vmcnt wait
+  // encodes at most 63 (a larger count waits for some stores too)
+  constexpr int kStores = kSwiGLU ? 8 : (kSplit ? 47 : 32);
 
   int slot = blockIdx.x;
   TileCoord tc = tile_at<kTN>(a, slot);
@@ -747,7 +754,14 @@ gemm_w8a8_kernel(const GemmArgs a) {
         epilogue_swiglu<true>(acc, j, lds_mem + kW8A8EpiOffset, wm, wn, alpha, a.out_rs, out, cur.n0, I, lane);
     } else {
       const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
-      if constexpr (kNormRope) {
+      if constexpr (kSplit) {
+        const __amdgpu_buffer_rsrc_t out4 = out_rsrc<4>(grp, a.m, cur.m0 + wm * 128);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            epilogue_rows_f32<kSplitPartialStore>(acc, j, hf, epi, grp, 1.0f, out4, cur.n0 + wn * 128, lane);
+      } else if constexpr (kNormRope) {
         const bool active = cur.group < 2;
         const uint16_t* nw = cur.group == 0 ? a.nr_w[0] : a.nr_w[1];
 #pragma unroll
@@ -1072,6 +1086,55 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
   hipLaunchKernelGGL(gemm_w8a8_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+int device_cu_count() { return cu_count(); }
+
+hipError_t launch_gemm_w8a8_splitk(const GemmArgs& a, hipStream_t s) {
+  static const int cus = cu_count();
+  int grid = cus - cus % kXcds;
+  if (grid <= 0) grid = kXcds;
+  if (grid > a.total_tiles) grid = a.total_tiles;
+  hipLaunchKernelGGL((gemm_w8a8_kernel<false, false, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// y[m, n] = bf16(alpha * sum_s p[s][m][n]) over `splits` float32 partials of
+// [m, n] each (s in order, so the result is deterministic); 8 columns per
+// thread: two 16-byte loads per partial, one 16-byte store.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const f32x4* __restrict__ p, int splits,
+                                                            uint16_t* __restrict__ y, int64_t m, int64_t n,
+                                                            int64_t ldy, float alpha) {
+  const int64_t groups_per_row = n / 8;
+  const int64_t total = m * groups_per_row;
+  const int64_t plane = m * n / 4;  // float4 per partial
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / groups_per_row;
+    const int64_t c = (i - row * groups_per_row) * 8;
+    const int64_t v = (row * n + c) / 4;
+    f32x4 lo = p[v], hi = p[v + 1];
+    for (int sp = 1; sp < splits; ++sp) {
+      lo += p[sp * plane + v];
+      hi += p[sp * plane + v + 1];
+    }
+    u32x4 o;
+    o.x = bf16x2(lo[0] * alpha, lo[1] * alpha);
+    o.y = bf16x2(lo[2] * alpha, lo[3] * alpha);
+    o.z = bf16x2(hi[0] * alpha, hi[1] * alpha);
+    o.w = bf16x2(hi[2] * alpha, hi[3] * alpha);
+    *reinterpret_cast<u32x4*>(y + row * ldy + c) = o;
+  }
+}
+
+hipError_t launch_splitk_reduce(const float* partials, int splits, void* y, int64_t m, int64_t n, int64_t ldy,
+                                float alpha, hipStream_t s) {
+  const int64_t total = m * (n / 8);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const f32x4*>(partials), splits, static_cast<uint16_t*>(y), m, n, ldy, alpha);
   return hipGetLastError();
 }
 

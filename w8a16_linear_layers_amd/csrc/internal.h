@@ -23,7 +23,7 @@ struct GemmGroup {
   float alpha;       // output scale: s_in * s_w (W8A8) or s_w (W8A16)
   int32_t tile_begin;  // first global tile index of this group
   int32_t tiles_n;     // ceil(n / kTileN)
-  int32_t pad_;
+  int32_t koff;        // split-K: first K byte of this group's slice (0 otherwise)
 };
 
 struct GemmArgs {
@@ -32,6 +32,7 @@ struct GemmArgs {
   int32_t k;
   int32_t xk;     // W8A16 activation row length: k, or 3 * 64 * ceil(k / 64) for
                   // the three-piece float32 form (0: set to k by the plans)
+  int32_t ks;     // split-K W8A8: the K length of each group's slice (k is the row pitch)
   int32_t tiles_m;
   int32_t ngroups;
   int32_t total_tiles;
@@ -60,6 +61,14 @@ hipError_t launch_quantize(const void* x, void* q, int64_t n, float scale, hipSt
 hipError_t launch_quantize_dynamic(const void* x, void* q, int64_t n, uint32_t* amax_ws, float* scale_out,
                                    hipStream_t s);
 hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
+// Split-K W8A8: group s multiplies K bytes [koff, koff + ks) of x and w and
+// writes float32 partial sums (no scale) to its y [m, ldy]; then
+// y = bf16(alpha * sum_s partial_s) over `splits` partials of [m, n] each.
+hipError_t launch_gemm_w8a8_splitk(const GemmArgs& a, hipStream_t s);
+// Compute units of the current device.
+int device_cu_count();
+hipError_t launch_splitk_reduce(const float* partials, int splits, void* y, int64_t m, int64_t n, int64_t ldy,
+                                float alpha, hipStream_t s);
 // The same grouped launch with the QK RMSNorm + RoPE epilogue on groups 0, 1.
 hipError_t launch_gemm_w8a8_norm_rope(const GemmArgs& a, hipStream_t s);
 // W8A16 activation forms: bf16, binary16, float32 as three bf16 pieces
