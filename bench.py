@@ -250,7 +250,7 @@ def main():
             "dtype": "bf16 activations x E4M3 weights (exact bf16 dequant), fp32 accumulate",
         },
         "roofline": {
-            "kernel": "gemm_w8a8 (v_mfma_f32_32x32x64_f8f6f4), one grouped launch of 3 projections, "
+            "kernel": "gemm_w8a8 (v_mfma_f32_16x16x128_f8f6f4), one grouped launch of 3 projections, "
             "each M=16384 N=4096 K=4096",
             "bound": "mfma",
             "achieved": round(achieved, 2),

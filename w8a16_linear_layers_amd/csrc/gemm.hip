@@ -2,7 +2,7 @@
 //
 //   W8A8  ([CF-157] "Verification", a real FP8 x FP8 GEMM):
 //     y[m, n] = bf16( sum_k qx[m, k] qw[n, k] * (s_in * s_w) )
-//     v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, float32 accumulate).
+//     v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3, float32 accumulate).
 //   W8A16 ([TRT-17476] "Denoising-step activation precision", same resident
 //   FP8 weight, 16-bit activation, no dequantized weight copy):
 //     y[m, n] = bf16( sum_k x[m, k] dec(qw[n, k]) * s_w )
@@ -12,7 +12,8 @@
 //
 // Shared structure:
 //   * A workgroup of 4 waves owns a 256 (M) x 256 (N) output tile; wave
-//     (wm, wn) owns the 128 x 128 quarter (wm, wn) as 4 x 4 blocks of 32 x 32.
+//     (wm, wn) owns the 128 x 128 quarter (wm, wn), as 8 x 8 blocks of
+//     16 x 16 (W8A8) or 4 x 4 blocks of 32 x 32 (W8A16).
 //   * The weight is the MFMA "A" operand and the activation the "B" operand,
 //     so the accumulator D[n][m] gives every lane four consecutive n of one
 //     output row.
@@ -24,6 +25,7 @@
 //     workgroups dispatched to one XCD (ids congruent mod 8) take a
 //     contiguous run of tiles, rasterized in bands of 8 M-tiles for L2 reuse.
 #include <type_traits>
+#include <utility>
 
 #include "device.h"
 #include "internal.h"
@@ -86,8 +88,15 @@ __device__ __forceinline__ uint8_t* lds16_x(int s) { return lds_mem + kStages16 
 // with {8k+32..8k+39}, or lanes sharing lane-index bits 1 and 4 -- the
 // grouping the LDS bank-conflict counters of a plain XOR layout pointed to),
 // for every read pattern of both kernels.
-//   128-byte rows (W8A8 E4M3 tiles, W8A16 bf16 tiles): chunk c of row r in
-//     physical chunk c ^ swz8(r).
+//   128-byte rows of the W8A16 bf16 tiles (32 x 32 fragments: 32 rows,
+//     lane halves 32 bytes apart): chunk c of row r in physical chunk
+//     c ^ swz8(r).
+//   128-byte rows of the W8A8 E4M3 tiles (16 x 128 fragments: 16 rows, lane
+//     quarters 32 bytes apart): chunk c of row r in physical chunk
+//     c ^ swz16(r). swz16 is linear in row bits 1-3; the one nonzero
+//     combination of those bits it maps to chunk bit 2 alone is bits 1 + 3,
+//     which no grouping above varies on its own (swz8 here would put two
+//     lanes of the bits-1-and-4 grouping on one bank).
 //   64-byte rows (W8A16 E4M3 weight tile): logical row r in physical row
 //     row64(r) = r ^ (bit3(r) << 1) (a swap inside groups of 4 rows), chunk
 //     c in physical chunk c ^ swz4(r).
@@ -96,6 +105,9 @@ __device__ __forceinline__ int row64(int r) { return r ^ (((r >> 3) & 1) << 1); 
 __device__ __forceinline__ int swz4(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
 __device__ __forceinline__ int swz8(int r) {
   return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+__device__ __forceinline__ int swz16(int r) {
+  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1) | (((r >> 1) & 1) << 2);
 }
 
 // ------------------------------------------------------------------ copies
@@ -144,7 +156,8 @@ __device__ __forceinline__ void wait_vmem_and_barrier() {
 // K offset travels in the scalar offset. The swizzles depend only on row
 // bits below 5, which j does not change, so a thread copies the same
 // logical chunk of every row it serves (kbyte).
-template <int kChunks>
+// kSwz16: 128-byte rows in the W8A8 layout (swz16 instead of swz8).
+template <int kChunks, bool kSwz16 = false>
 struct CopyPlan {
   i32x4 lo, hi;
   uint32_t voff[kChunks];
@@ -164,7 +177,7 @@ struct CopyPlan {
     for (int j = 0; j < kChunks; ++j) {
       const int p = j * kThreads + tid;
       const int r = kChunks == 4 ? row64(p / kChunks) : p / kChunks;
-      const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : swz8(r));
+      const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : kSwz16 ? swz16(r) : swz8(r));
       voff[j] = (uint32_t)((r & 127) * ld_bytes) + (uint32_t)c * 16u;
       if (j == 0) kbyte = c * 16;
     }
@@ -188,6 +201,13 @@ struct CopyPlan {
   // Chunk j of the full stage starting at byte `k0b` of each row.
   __device__ __forceinline__ void copy_one(const uint8_t* lds_tile, uint32_t k0b, int j, uint32_t wave_off) const {
     dma(j, voff[j], k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+  }
+
+  // Chunk j of the stage starting at byte `k0b`, zero at or beyond byte `kb`
+  // of a row (the K tail).
+  __device__ __forceinline__ void copy_masked(const uint8_t* lds_tile, int k0b, int kb, int j,
+                                              uint32_t wave_off) const {
+    dma(j, k0b + kbyte >= kb ? kOutOfRange : voff[j], (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
   }
 
   // All chunks of the stage starting at byte `k0b`; chunks at or beyond
@@ -259,37 +279,28 @@ constexpr int kStreamStore = 2;
 // Split-K partials are re-read at once by the reduction: default policy.
 constexpr int kSplitPartialStore = 0;
 
-// acc[i][j] holds D[n][m] of the 32 x 32 block (n-block i, m-block j):
-// lane l, register v -> m = l % 32, n = 8 (v / 4) + 4 (l / 32) + v % 4,
-// i.e. four consecutive n of one row per register quad. Written straight to
-// memory that would scatter every store instruction over 32 rows, so the
-// rows go through LDS: a staging row holds 128 bf16 of the wave's tile as
-// 16 chunks of 16 bytes, chunk c at physical chunk c ^ (row % 16). Read back
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Output rows leave through LDS: rows [32 j, 32 j + 32) of a wave's 128 x 128
+// tile are staged in its 8 KiB area, staged row m holding the tile's 128
+// columns as 16 chunks of 16 bytes (8 16-bit values, or 4 float32 values of
+// a 64-column half) with chunk c at physical chunk c ^ (m % 16). Read back
 // row by row, 16 lanes cover a row's 256 contiguous bytes and every global
-// store writes 16 bytes per lane.
+// store writes 16 bytes per lane; straight from the accumulators every
+// store instruction would scatter over 16 or 32 rows.
+//
+// Accumulator layouts (both give a lane four consecutive n of one row per
+// register quad):
+//   W8A16, 32 x 32 blocks, acc[i][j] = D[n][m] of n-block i, m-block j:
+//     lane l, register v -> m = 32 j + l % 32, n = 32 i + 8 (v / 4) +
+//     4 (l / 32) + v % 4.
+//   W8A8, 16 x 16 blocks, acc[i][b] = D[n][m] of n-block i, m-block b:
+//     lane l, register v -> m = 16 b + l % 16, n = 16 i + 4 (l / 16) + v;
+//     rows [32 j, 32 j + 32) are m-blocks 2 j and 2 j + 1.
 
-// Output resource of a wave's 128 x 128 tile: rows [m_base, min(M, m_base +
-// 128)) of y, so stores to rows beyond M fall outside it and are dropped.
-// Rows m_base..+128 of a group's output of kBytes-byte elements.
-template <int kBytes = 2>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const GemmGroup& grp, int M, int m_base) {
-  // readfirstlane keeps the (uniform) count scalar: a clamp may be computed
-  // in a vector register, and a resource in vector registers costs a loop
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(M - m_base, 128)));
-  uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(m_base, M) * grp.ldy * kBytes;
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * grp.ldy * kBytes, 0x00020000);
-}
-
-// Rows [32 j, 32 j + 32) of the wave's tile (scaled by alpha, rounded to
-// bf16, or to binary16 with kF16) through the wave's 8 KiB staging area.
-// Columns at or beyond N get an out-of-range offset, so every lane issues
-// the same eight stores.
-template <bool kF16 = false>
-__device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, uint8_t* stage, const GemmGroup& grp,
-                                              float alpha, __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
-  // The lane-dependent offsets below are cheap; an opaque copy of the lane
-  // index keeps the compiler from holding them in registers across the K loop.
-  asm volatile("" : "+v"(lane));
+// Stage bf16(acc * alpha) (binary16 with kF16) of rows [32 j, 32 j + 32).
+template <bool kF16>
+__device__ __forceinline__ void stage_rows(const v16f (&acc)[4][4], int j, uint8_t* stage, float alpha, int lane) {
   const int h = lane >> 5;
   const int m = lane & 31;
 #pragma unroll
@@ -303,31 +314,31 @@ __device__ __forceinline__ void epilogue_rows(const v16f (&acc)[4][4], int j, ui
       *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
     }
   }
-  const int c = lane & 15;
-  const int n = n_base + c * 8;
-  u32x4 v[8];
+}
+
+template <bool kF16>
+__device__ __forceinline__ void stage_rows(const f32x4 (&acc)[8][8], int j, uint8_t* stage, float alpha, int lane) {
+  const int q = lane >> 4;
+  const int r = lane & 15;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ml = q * 4 + (lane >> 4);
-    v[q] = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) * 16));
-  }
+  for (int b = 0; b < 2; ++b) {
+    const int m = 16 * b + r;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ml = 32 * j + q * 4 + (lane >> 4);
-    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 2u : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kStreamStore);
+    for (int i = 0; i < 8; ++i) {
+      const int c = 2 * i + (q >> 1);  // 16-byte chunk of n = 16 i + 4 q
+      const f32x4 x = acc[i][2 * j + b];
+      u32x2 v;
+      v[0] = h16x2<kF16>(x[0] * alpha, x[1] * alpha);
+      v[1] = h16x2<kF16>(x[2] * alpha, x[3] * alpha);
+      *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ r) * 16) + (q & 1) * 8) = v;
+    }
   }
 }
 
-// Float32 form of epilogue_rows: columns [64 hf, 64 hf + 64) of rows
-// [32 j, 32 j + 32), scaled by alpha, through the same 8 KiB area (two calls
-// per row block; one wave's LDS operations complete in order, so a call's
-// staging writes follow the previous call's reads).
-template <int kPolicy = kStreamStore>
-__device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j, int hf, uint8_t* stage,
-                                                  const GemmGroup& grp, float alpha, __amdgpu_buffer_rsrc_t out,
-                                                  int n_base, int lane) {
-  asm volatile("" : "+v"(lane));
+// Stage acc * alpha in float32, columns [64 hf, 64 hf + 64) of rows
+// [32 j, 32 j + 32).
+__device__ __forceinline__ void stage_rows_f32(const v16f (&acc)[4][4], int j, int hf, uint8_t* stage, float alpha,
+                                               int lane) {
   const int h = lane >> 5;
   const int m = lane & 31;
 #pragma unroll
@@ -342,8 +353,37 @@ __device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j
       *reinterpret_cast<u32x4*>(stage + m * 256 + ((c ^ (m & 15)) * 16)) = v;
     }
   }
+}
+
+__device__ __forceinline__ void stage_rows_f32(const f32x4 (&acc)[8][8], int j, int hf, uint8_t* stage, float alpha,
+                                               int lane) {
+  const int q = lane >> 4;
+  const int r = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int m = 16 * b + r;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int c = 4 * ii + q;  // 16-byte chunk of n = 64 hf + 16 ii + 4 q
+      const f32x4 x = acc[4 * hf + ii][2 * j + b];
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(x[e] * alpha);
+      *reinterpret_cast<u32x4*>(stage + m * 256 + ((c ^ r) * 16)) = v;
+    }
+  }
+}
+
+// Store the staged rows [32 j, 32 j + 32) of kElem-byte elements, 16 bytes
+// per lane, the row's first column being n0. Columns at or beyond N get an
+// out-of-range offset, so every lane issues the same eight stores. The
+// staging writes come from the same wave, whose LDS operations complete in
+// order.
+template <int kElem, int kPolicy>
+__device__ __forceinline__ void store_rows(const uint8_t* stage, int j, const GemmGroup& grp,
+                                           __amdgpu_buffer_rsrc_t out, int n0, int lane) {
   const int c = lane & 15;
-  const int n = n_base + 64 * hf + c * 4;
+  const int n = n0 + c * (16 / kElem);
   u32x4 v[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -353,61 +393,92 @@ __device__ __forceinline__ void epilogue_rows_f32(const v16f (&acc)[4][4], int j
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int ml = 32 * j + q * 4 + (lane >> 4);
-    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 4u : kOutOfRange;
+    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * (uint32_t)kElem : kOutOfRange;
     __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kPolicy);
   }
+}
+
+// Output resource of a wave's 128 x 128 tile: rows [m_base, min(M, m_base +
+// 128)) of y, so stores to rows beyond M fall outside it and are dropped.
+// Rows m_base..+128 of a group's output of kBytes-byte elements.
+template <int kBytes = 2>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const GemmGroup& grp, int M, int m_base) {
+  // readfirstlane keeps the (uniform) count scalar: a clamp may be computed
+  // in a vector register, and a resource in vector registers costs a loop
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(M - m_base, 128)));
+  uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(m_base, M) * grp.ldy * kBytes;
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * grp.ldy * kBytes, 0x00020000);
+}
+
+// Rows [32 j, 32 j + 32) of the wave's tile, scaled by alpha and rounded to
+// bf16 (binary16 with kF16), through the wave's 8 KiB staging area.
+template <bool kF16 = false, class Acc>
+__device__ __forceinline__ void epilogue_rows(const Acc& acc, int j, uint8_t* stage, const GemmGroup& grp, float alpha,
+                                              __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
+  // The lane-dependent offsets below are cheap; an opaque copy of the lane
+  // index keeps the compiler from holding them in registers across the K loop.
+  asm volatile("" : "+v"(lane));
+  stage_rows<kF16>(acc, j, stage, alpha, lane);
+  store_rows<2, kStreamStore>(stage, j, grp, out, n_base, lane);
+}
+
+// Float32 form: columns [64 hf, 64 hf + 64) of rows [32 j, 32 j + 32),
+// scaled by alpha, through the same 8 KiB area (two calls per row block).
+template <int kPolicy = kStreamStore, class Acc>
+__device__ __forceinline__ void epilogue_rows_f32(const Acc& acc, int j, int hf, uint8_t* stage, const GemmGroup& grp,
+                                                  float alpha, __amdgpu_buffer_rsrc_t out, int n_base, int lane) {
+  asm volatile("" : "+v"(lane));
+  stage_rows_f32(acc, j, hf, stage, alpha, lane);
+  store_rows<4, kPolicy>(stage, j, grp, out, n_base + 64 * hf, lane);
 }
 
 // bf16 rounding of a float32 value, back as float32 (exact).
 __device__ __forceinline__ float bf16_round(float v) { return bf16_lo(bf16x2(v, 0.0f)); }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 // epilogue_rows for a 128-column block that is one head of a Q or K
-// projection: y = bf16(acc * alpha), the value the plain epilogue writes,
-// then per row the head's RMSNorm and rotate-half RoPE in float32
-// (r = rsqrt(sum(y^2) / 128 + eps); out[d] = y[d] r w[d] cos[t, d] -
+// projection (W8A8 accumulators): y = bf16(acc * alpha), the value the plain
+// epilogue writes, then per row the head's RMSNorm and rotate-half RoPE in
+// float32 (r = rsqrt(sum(y^2) / 128 + eps); out[d] = y[d] r w[d] cos[t, d] -
 // y[d + 64] r w[d + 64] sin[t, d], out[d + 64] = y[d + 64] r w[d + 64]
 // cos[t, d] + y[d] r w[d] sin[t, d] for d < 64), rounded to bf16 and stored
-// like epilogue_rows. Lane (m, h) holds columns 32 i + 8 t + 4 h + e of row
-// m, lane m + 32 the rest of the row (one butterfly step completes the sum
-// of squares), and the RoPE partner of a column of block i < 2 is the same
-// position of block i + 2 in the same lane. row0: the first output row of
-// the wave's tile (rows at or past M are never stored; their table row is
-// clamped to M - 1). With active = false (a V tile) r = 1, w = 1 and no
-// rotation, which reproduces epilogue_rows bit for bit: one code path for
-// every tile of the launch (a second epilogue body in the same kernel costs
-// ~25 spilled registers).
-__device__ __forceinline__ void epilogue_rows_norm_rope(const v16f (&acc)[4][4], int j, uint8_t* stage,
+// like epilogue_rows. Lane (r, q) = (l % 16, l / 16) holds columns
+// 16 i + 4 q + v of rows 16 b + r (b = 0, 1 in the pass), lanes r + 16 q'
+// the rest of the row (two butterfly steps complete the sum of squares),
+// and the RoPE partner of a column of block i < 4 is the same position of
+// block i + 4 in the same lane. row0: the first output row of the wave's
+// tile (rows at or past M are never stored; their table row is clamped to
+// M - 1). With active = false (a V tile) r = 1, w = 1 and no rotation,
+// which reproduces epilogue_rows bit for bit: one code path for every tile
+// of the launch.
+__device__ __forceinline__ void epilogue_rows_norm_rope(const f32x4 (&acc)[8][8], int j, uint8_t* stage,
                                                         const GemmGroup& grp, float alpha,
                                                         __amdgpu_buffer_rsrc_t out, int n_base, int lane, int row0,
                                                         int M, bool active, const uint16_t* w, const float* cos,
                                                         const float* sin, float eps) {
   asm volatile("" : "+v"(lane));
-  const int h = lane >> 5;
-  const int m = lane & 31;
-  float ss = 0.0f;
+  const int q = lane >> 4;
+  const int r = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int b = 0; b < 2; ++b) {
+    const int mb = 2 * j + b;  // m-block
+    const int m = 16 * b + r;  // row within the pass
+    float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float y = bf16_round(acc[i][j][k] * alpha);
-      ss += y * y;
-    }
-  ss += __shfl_xor(ss, 32);
-  const float r = active ? rsqrtf(ss * (1.0f / 128) + eps) : 1.0f;
-  // an opaque copy of alpha: the second pass recomputes y from the
-  // accumulators instead of keeping the first pass's 64 values alive
-  float alpha2 = alpha;
-  asm volatile("" : "+v"(alpha2));
-  const int token = min(row0 + 32 * j + m, M - 1);
-  const float* cr = cos + (int64_t)token * 64;
-  const float* sr = sin + (int64_t)token * 64;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+      for (int e = 0; e < 4; ++e) {
+        const float y = bf16_round(acc[i][mb][e] * alpha);
+        ss += y * y;
+      }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rr = active ? rsqrtf(ss * (1.0f / 128) + eps) : 1.0f;
+    const int token = min(row0 + 32 * j + m, M - 1);
+    const float* cr = cos + (int64_t)token * 64;
+    const float* sr = sin + (int64_t)token * 64;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int d = 32 * i + 8 * t + 4 * h;
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * i + 4 * q;
       f32x4 c = {1.0f, 1.0f, 1.0f, 1.0f}, s = {0.0f, 0.0f, 0.0f, 0.0f};
       if (active) {
         c = *reinterpret_cast<const f32x4*>(cr + d);
@@ -423,131 +494,215 @@ __device__ __forceinline__ void epilogue_rows_norm_rope(const v16f (&acc)[4][4],
       float oa[4], ob[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float ya = bf16_round(acc[i][j][4 * t + e] * alpha2) * r * wa[e];
-        const float yb = bf16_round(acc[i + 2][j][4 * t + e] * alpha2) * r * wb[e];
+        const float ya = bf16_round(acc[i][mb][e] * alpha) * rr * wa[e];
+        const float yb = bf16_round(acc[i + 4][mb][e] * alpha) * rr * wb[e];
         oa[e] = active ? ya * c[e] - yb * s[e] : ya;  // inactive: no cross term (an inf stays inf)
         ob[e] = active ? yb * c[e] + ya * s[e] : yb;
       }
-      const int ca = i * 4 + t, cb = (i + 2) * 4 + t;  // 16-byte chunks of the staged row, as in epilogue_rows
-      *reinterpret_cast<u32x2*>(stage + m * 256 + ((ca ^ (m & 15)) * 16) + h * 8) =
+      const int ca = 2 * i + (q >> 1), cb = 2 * (i + 4) + (q >> 1);  // chunks of the staged row, as in stage_rows
+      *reinterpret_cast<u32x2*>(stage + m * 256 + ((ca ^ r) * 16) + (q & 1) * 8) =
           u32x2{bf16x2(oa[0], oa[1]), bf16x2(oa[2], oa[3])};
-      *reinterpret_cast<u32x2*>(stage + m * 256 + ((cb ^ (m & 15)) * 16) + h * 8) =
+      *reinterpret_cast<u32x2*>(stage + m * 256 + ((cb ^ r) * 16) + (q & 1) * 8) =
           u32x2{bf16x2(ob[0], ob[1]), bf16x2(ob[2], ob[3])};
     }
   }
-  const int c = lane & 15;
-  const int n = n_base + c * 8;
-  u32x4 v[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ml = q * 4 + (lane >> 4);
-    v[q] = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) * 16));
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ml = 32 * j + q * 4 + (lane >> 4);
-    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * 2u : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kStreamStore);
-  }
+  store_rows<2, kStreamStore>(stage, j, grp, out, n_base, lane);
 }
 
 // ------------------------------------------------------------------ W8A8
 
-// 32 x 64 E4M3 fragment of k-step h (0 or 1) of rows [row, row + 32) of a
-// 128-byte-row tile: lane (r, g) holds logical chunks 4h + 2g and 4h + 2g + 1.
-__device__ __forceinline__ v8i frag_w8a8(const uint8_t* tile, int row, int g, int h) {
-  const int s = swz8(row), base = row * 128;
-  const u32x4 a = lds_chunk(tile, base + ((4 * h + 2 * g) ^ s) * 16);
-  const u32x4 b = lds_chunk(tile, base + ((4 * h + 2 * g + 1) ^ s) * 16);
-  v8i v;
-  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-  return v;
+// Half e (16 bytes) of a 16 x 128 E4M3 fragment of a 128-byte-row stage
+// tile for v_mfma_f32_16x16x128_f8f6f4: lane (r, q) = (l % 16, l / 16)
+// holds bytes [32 q, 32 q + 32) of row r of the block, i.e. logical chunks
+// 2 q and 2 q + 1 (both operands use the same K bytes per lane, so the
+// products pair up). Blocks are 16 rows apart, which leaves row bits 1-3
+// and with them the swizzle unchanged, so the lane's two byte offsets in
+// block 0 (frag16_offset) serve every block f at + 2048 f.
+__device__ __forceinline__ int frag16_offset(int row, int q, int e) {
+  return row * 128 + (((2 * q + e) ^ swz16(row)) * 16);
 }
 
-__device__ __forceinline__ void w8a8_frags(int buf, int h, int row_w, int row_x, int g, v8i (&wf)[4], v8i (&xf)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wf[i] = frag_w8a8(lds8_w(buf), row_w + i * 32, g, h);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) xf[j] = frag_w8a8(lds8_x(buf), row_x + j * 32, g, h);
+__device__ __forceinline__ u32x4 frag16_half(const uint8_t* tile, int off, int f) {
+  return lds_chunk(tile, off + 2048 * f);
 }
 
-__device__ __forceinline__ void w8a8_mma(v16f (&acc)[4][4], const v8i (&wf)[4], const v8i (&xf)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], xf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+__device__ __forceinline__ void set_half(v8i& f, int e, const u32x4 v) {
+  f[4 * e + 0] = (int)v[0];
+  f[4 * e + 1] = (int)v[1];
+  f[4 * e + 2] = (int)v[2];
+  f[4 * e + 3] = (int)v[3];
 }
 
-// Steady-state stage s (fragments of its k-step 0 in (wa, xa)); K stages of
-// 128 bytes in two LDS buffers. Each of the 32 MFMAs is followed by at most
-// one kind of memory work, so the texture path and the LDS see an even
-// stream:
-//   k-step 0, MFMAs 0-7 : read the k-step-1 fragments of stage s into
-//                         (wb, xb), one per MFMA (order W0, X0..X3, W1..W3);
-//   after MFMA 8        : lgkmcnt(0) + barrier: no wave reads stage s's
-//                         buffer any more;
-//   MFMAs 8-15, k-step 1 MFMAs 0-7: one copy of stage s + 2 into that buffer
-//                         each (weight chunks, then activation chunks);
-//   after k-step 1 MFMA 8: vmcnt(kVm) + barrier: stage s + 1, copied during
-//                         stage s - 1 (older than the 16 copies just issued),
-//                         has landed for every wave; kVm = 16, and in stage
-//                         0 of a tile 16 + the previous tile's output stores,
-//                         which were issued after stage 1's copies;
-//   k-step 1 MFMAs 8-15 : read the k-step-0 fragments of stage s + 1 into
-//                         (wa, xa).
-// sched_barrier keeps the compiler from regrouping slots.
-template <int kVm>
-__device__ __forceinline__ void w8a8_stage(v16f (&acc)[4][4], v8i (&wa)[4], v8i (&xa)[4], v8i (&wb)[4], v8i (&xb)[4],
-                                           const CopyPlan<8>& pw, const CopyPlan<8>& px, int s, int row_w, int row_x,
-                                           int g, uint32_t wave_off) {
-  const int cur = s & 1, nxt = cur ^ 1;
-  const uint32_t k2 = (uint32_t)(s + 2) * 128u;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int i = t >> 2, j = t & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[i], xa[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-    if (t < 8) {
-      const int f = t;
-      if (f == 0)
-        wb[0] = frag_w8a8(lds8_w(cur), row_w, g, 1);
-      else if (f < 5)
-        xb[f - 1] = frag_w8a8(lds8_x(cur), row_x + (f - 1) * 32, g, 1);
-      else
-        wb[f - 4] = frag_w8a8(lds8_w(cur), row_w + (f - 4) * 32, g, 1);
-    } else {
-      if (t == 8) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage s's buffer is free
-      pw.copy_one(lds8_w(cur), k2, t - 8, wave_off);
+__device__ __forceinline__ void read_frag16(v8i& v, const uint8_t* tile, const int (&off)[2], int f) {
+  set_half(v, 0, frag16_half(tile, off[0], f));
+  set_half(v, 1, frag16_half(tile, off[1], f));
+}
+
+// One stage (128 K bytes) of a wave's 128 x 128 tile: 64 MFMAs
+// v_mfma_f32_16x16x128_f8f6f4 over weight blocks wf[i] (16 rows of N each)
+// and activation blocks xf[b] (16 rows of M each), in two halves: MFMA t of
+// the first half multiplies (i, b) = (t % 4, t / 4), of the second half
+// (4 + t % 4, t / 4). So wf[0..3] are done after the first half, xf[b] after
+// MFMA 32 + 4 b + 3 of the second, and wf[4..7] are first needed in the
+// second half -- each register block is refilled in place as soon as it is
+// done, and the 16 blocks (128 VGPRs) are all the fragments there are.
+// Each MFMA is followed by at most one memory operation (slot plan below);
+// a tile's last stage (kLast) has no stage s + 1: after the barrier that
+// frees its buffer no wave reads either buffer, and the next tile's stages 0
+// and 1 are issued, one copy per slot (plans pw, px of that tile; none when
+// has_next is false). sched_barrier keeps the compiler from regrouping slots.
+//
+// Why 16 x 16 x 128 and not 32 x 32 x 64 (same 128 x 128 wave tile, same
+// LDS traffic): on one MI355X, back-to-back FP8 MFMAs sustain 4.36-4.47
+// PFLOP/s in the 16 x 16 form against 3.96-4.10 in the 32 x 32 form, and the
+// GEMM held 1.96 GHz against 1.67 GHz under the 32 x 32 form -- the board is
+// power-limited and the smaller instruction costs less energy per FLOP. The
+// twice as many, half as long MFMAs leave half the time per slot, so the
+// copies are spread three slots apart (two: -1%, one: -6%).
+constexpr int kSlotFree = 12;   // barrier that frees this stage's buffer
+constexpr int kCopyStride = 3;  // slots between the copies of stage s + 2
+constexpr int kSlotMid = 32;    // barrier after which stage s + 1 is readable
+
+// What one stage needs besides the fragments and accumulators.
+struct StageCtx {
+  const CopyPlan<8, true>& pw;
+  const CopyPlan<8, true>& px;
+  int cur, nxt;   // LDS buffer of this stage and of the next
+  uint32_t k2;    // K byte of stage s + 2
+  int K, KT;
+  bool has_next;  // kLast: a next tile exists
+  const int (&ow)[2];
+  const int (&ox)[2];
+  uint32_t wave_off;
+};
+
+// The memory operation after MFMA t of a steady stage (at most one each).
+enum SlotKind : int { kSlotNone, kSlotOwn, kSlotCopy, kSlotW, kSlotX };
+struct SlotOp {
+  int kind, a, e;  // own: read a (0..9); copy: chunk a (0..15); W / X: block a, half e
+};
+struct SlotPlan {
+  SlotOp op[64];
+  int copies_before_mid;  // copies of stage s + 2 issued before the mid-stage barrier
+  bool ok;
+};
+
+// Slot plan of a steady stage: this stage's xf[7] and wf[4..7] at slots
+// 0-9; the barrier that frees this stage's buffer at kFree; the 16 copies of
+// stage s + 2 at kFree + kStride u (or the next free slot); the mid-stage
+// barrier (stage s + 1 landed) at kMid; then stage s + 1's wf[0..3] and
+// xf[0..6] in the earliest free slots at or after kMid and after the last
+// use of the register block they replace (wf[f]: MFMA 28 + f; xf[b]: MFMA
+// 35 + 4 b). Copies issued in consecutive slots cost matrix-core time.
+constexpr SlotPlan make_slot_plan(int kFree, int kStride, int kMid) {
+  SlotPlan p{};
+  p.ok = kFree >= 10 && kMid >= 28;
+  for (int t = 0; t < 64; ++t) p.op[t] = SlotOp{kSlotNone, 0, 0};
+  for (int r = 0; r < 10; ++r) p.op[r] = SlotOp{kSlotOwn, r, 0};
+  int t = kFree;
+  for (int u = 0; u < 16; ++u) {
+    int want = kFree + kStride * u;
+    if (want < t) want = t;
+    while (want < 64 && p.op[want].kind != kSlotNone) ++want;
+    if (want >= 64) {
+      p.ok = false;
+      return p;
     }
-    __builtin_amdgcn_sched_barrier(0);
+    p.op[want] = SlotOp{kSlotCopy, u, 0};
+    if (want < kMid) ++p.copies_before_mid;
+    t = want + 1;
   }
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int i = t >> 2, j = t & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wb[i], xb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-    if (t < 8) {
-      px.copy_one(lds8_x(cur), k2, t, wave_off);
-    } else {
-      if (t == 8) {
-        // stage s + 1 has landed for every wave (its copies are older than the 16 of stage s + 2)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
+  auto place = [&](int kind, int blk, int e, int earliest) {
+    int s = earliest < kMid ? kMid : earliest;
+    while (s < 64 && p.op[s].kind != kSlotNone) ++s;
+    if (s >= 64) {
+      p.ok = false;
+      return;
+    }
+    p.op[s] = SlotOp{kind, blk, e};
+  };
+  for (int f = 0; f < 4; ++f)
+    for (int e = 0; e < 2; ++e) place(kSlotW, f, e, 28 + f);
+  for (int b = 0; b < 7; ++b)
+    for (int e = 0; e < 2; ++e) place(kSlotX, b, e, 35 + 4 * b);
+  return p;
+}
+
+constexpr SlotPlan kSlotPlan = make_slot_plan(kSlotFree, kCopyStride, kSlotMid);
+static_assert(kSlotPlan.ok, "the W8A8 stage's memory operations must fit its 64 slots");
+
+// MFMA t of the stage and the memory operation that follows it. kExtraVm:
+// VMEM operations issued after stage s + 1's copies besides this stage's
+// (the previous tile's output stores, in a tile's stage 0).
+template <int t, int kCopy, int kExtraVm, bool kLast>
+__device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8], const StageCtx& c) {
+  constexpr int kFree = kSlotFree, kMid = kSlotMid;
+  constexpr SlotOp op = kSlotPlan.op[t];
+  constexpr int i = (t < 32 ? 0 : 4) + (t & 3), b = (t & 31) >> 2;
+  acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf[b], acc[i][b], 0, 0, 0, 0, 0, 0);
+  if constexpr (op.kind == kSlotOwn) {
+    constexpr int r = op.a;
+    if constexpr (r < 2)
+      set_half(xf[7], r, frag16_half(lds8_x(c.cur), c.ox[r], 7));
+    else
+      set_half(wf[4 + (r - 2) / 2], r & 1, frag16_half(lds8_w(c.cur), c.ow[r & 1], 4 + (r - 2) / 2));
+  }
+  if constexpr (t == kFree) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // this stage's buffer is free
+  if constexpr (kLast) {
+    // no stage s + 1: the next tile's stages 0 and 1, one copy per slot
+    if constexpr (t >= kFree && t < kFree + 32) {
+      constexpr int u = t - kFree, st = u >> 4, j = u & 7;
+      if (c.has_next && (st == 0 || c.KT > 1)) {
+        if constexpr ((u & 15) < 8)
+          c.pw.copy_masked(lds8_w(st), st * 128, c.K, j, c.wave_off);
+        else
+          c.px.copy_masked(lds8_x(st), st * 128, c.K, j, c.wave_off);
       }
-      const int f = t - 8;
-      if (f == 0)
-        wa[0] = frag_w8a8(lds8_w(nxt), row_w, g, 0);
-      else if (f < 5)
-        xa[f - 1] = frag_w8a8(lds8_x(nxt), row_x + (f - 1) * 32, g, 0);
-      else
-        wa[f - 4] = frag_w8a8(lds8_w(nxt), row_w + (f - 4) * 32, g, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    if constexpr (op.kind == kSlotCopy) {
+      constexpr int u = op.a, j = u & 7;
+      if constexpr (kCopy == 1) {
+        if constexpr (u < 8)
+          c.pw.copy_one(lds8_w(c.cur), c.k2, j, c.wave_off);
+        else
+          c.px.copy_one(lds8_x(c.cur), c.k2, j, c.wave_off);
+      } else if constexpr (kCopy == 2) {
+        if constexpr (u < 8)
+          c.pw.copy_masked(lds8_w(c.cur), (int)c.k2, c.K, j, c.wave_off);
+        else
+          c.px.copy_masked(lds8_x(c.cur), (int)c.k2, c.K, j, c.wave_off);
+      }
+    }
+    if constexpr (t == kMid) {
+      constexpr int kVm = (kCopy != 0 ? kSlotPlan.copies_before_mid : 0) + kExtraVm;
+      static_assert(kVm < 64, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
+    }
+    if constexpr (op.kind == kSlotW) set_half(wf[op.a], op.e, frag16_half(lds8_w(c.nxt), c.ow[op.e], op.a));
+    if constexpr (op.kind == kSlotX) set_half(xf[op.a], op.e, frag16_half(lds8_x(c.nxt), c.ox[op.e], op.a));
   }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int kCopy, int kExtraVm, bool kLast, int... ts>
+__device__ __forceinline__ void w8a8_slots(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8], const StageCtx& c,
+                                           std::integer_sequence<int, ts...>) {
+  (w8a8_slot<ts, kCopy, kExtraVm, kLast>(acc, wf, xf, c), ...);
+}
+
+template <int kCopy, int kExtraVm, bool kLast>
+__device__ __forceinline__ void w8a8_stage(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8],
+                                           const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int s, int K,
+                                           int KT, bool has_next, const int (&ow)[2], const int (&ox)[2],
+                                           uint32_t wave_off) {
+  const StageCtx c{pw, px, s & 1, (s & 1) ^ 1, (uint32_t)(s + 2) * 128u, K, KT, has_next, ow, ox, wave_off};
+  w8a8_slots<kCopy, kExtraVm, kLast>(acc, wf, xf, c, std::make_integer_sequence<int, 64>{});
 }
 
 // Issue the copies of stages 0 and 1 of a tile into buffers 0 and 1.
-__device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8>& pw, const CopyPlan<8>& px, int K, int KT,
-                                                  uint32_t wave_off) {
+__device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int K,
+                                                  int KT, uint32_t wave_off) {
   pw.copy(lds8_w(0), 0, K, wave_off);
   px.copy(lds8_x(0), 0, K, wave_off);
   if (KT > 1) {
@@ -568,27 +723,11 @@ __device__ __forceinline__ void w8a8_first_stages(const CopyPlan<8>& pw, const C
 // columns past I dropped). A second barrier frees the areas. With kF16 the
 // staged values and a 16-bit h are binary16 instead of bf16 (the fp16
 // activation form of the separate GEMMs and SwiGLU).
-template <bool kFp8Out, bool kF16 = false>
-__device__ __forceinline__ void epilogue_swiglu(const v16f (&acc)[4][4], int j, uint8_t* epi, int wm, int wn,
-                                                float alpha, float rs, __amdgpu_buffer_rsrc_t out, int n_base,
-                                                int I, int lane) {
+template <bool kFp8Out, bool kF16 = false, class Acc>
+__device__ __forceinline__ void epilogue_swiglu(const Acc& acc, int j, uint8_t* epi, int wm, int wn, float alpha,
+                                                float rs, __amdgpu_buffer_rsrc_t out, int n_base, int I, int lane) {
   asm volatile("" : "+v"(lane));
-  {
-    uint8_t* stage = epi + (wm * 2 + wn) * kW8A8EpiWave;
-    const int h = lane >> 5;
-    const int m = lane & 31;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = i * 4 + t;
-        u32x2 v;
-        v[0] = h16x2<kF16>(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
-        v[1] = h16x2<kF16>(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
-        *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
-      }
-    }
-  }
+  stage_rows<kF16>(acc, j, epi + (wm * 2 + wn) * kW8A8EpiWave, alpha, lane);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const uint8_t* ga = epi + (wm * 2) * kW8A8EpiWave;
   const uint8_t* ua = ga + kW8A8EpiWave;
@@ -642,12 +781,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(void* h, int M, int m_b
 }
 
 // Persistent W8A8 kernel: one workgroup per CU walks the tiles of dispatch
-// slots blockIdx.x, blockIdx.x + gridDim.x, ... After the last LDS read of
-// a tile the first two stages of the next tile are issued, so their latency
-// overlaps the last k-step and the tile's output stores (which go through
-// an LDS area of each wave's own). The next tile then waits for its stage
-// 0 with a count that skips those stores (they were issued later), and
-// for stage 1 inside its stage 0, so it never waits for the stores.
+// slots blockIdx.x, blockIdx.x + gridDim.x, ... In a tile's last stage,
+// once no wave reads the pipeline buffers, the first two stages of the next
+// tile are issued, so their latency overlaps the last MFMAs and the tile's
+// output stores (which go through an LDS area of each wave's own). The next
+// tile then waits for its stage 0 with a count that skips those stores
+// (they were issued later), and for stage 1 inside its stage 0, so it never
+// waits for the stores.
 // kSwiGLU: the fused gate/up + SwiGLU form. A tile is 256 rows of M by 128
 // columns of h; weight rows 0-127 of the tile are the gate rows and 128-255
 // the up rows of those columns (a.g[0]: gate, h output, alpha s_in s_gate;
@@ -667,15 +807,17 @@ gemm_w8a8_kernel(const GemmArgs a) {
   const int K = kSplit ? a.ks : a.k;  // K bytes this launch's groups multiply
   const int KT = (K + 127) / 128;
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
-  const int row_w = wn * 128 + (lane & 31);
-  const int row_x = wm * 128 + (lane & 31);
-  const int g = lane >> 5;
+  // the lane's fragment offsets in weight / activation block 0 (halves 0, 1)
+  const int ow[2] = {frag16_offset(wn * 128 + (lane & 15), lane >> 4, 0),
+                     frag16_offset(wn * 128 + (lane & 15), lane >> 4, 1)};
+  const int ox[2] = {frag16_offset(wm * 128 + (lane & 15), lane >> 4, 0),
+                     frag16_offset(wm * 128 + (lane & 15), lane >> 4, 1)};
   uint8_t* epi = lds_mem + kW8A8EpiOffset + wave * kW8A8EpiWave;
   // dynamic quantization: the input scale is read from device memory and
   // multiplies the host's weight_scale (the same float product as s_in * s_w)
   const float alpha_mul = a.in_scale_dev != nullptr ? *a.in_scale_dev : 1.0f;
 
-  CopyPlan<8> pw, px;
+  CopyPlan<8, true> pw, px;
   auto plan_tile = [&](const TileCoord& t) {
     if constexpr (kSwiGLU) {
       const int64_t off = (int64_t)t.n0 * K;
@@ -701,50 +843,56 @@ gemm_w8a8_kernel(const GemmArgs a) {
   for (;;) {
     const TileCoord cur = tc;
     const GemmGroup& grp = a.g[cur.group];
+    const int next = slot + (int)gridDim.x;
+    const bool has_next = next < a.total_tiles;
     // stage 0 has landed for every wave: after the first tile, only stage
     // 1's copies (when KT > 1) and the previous tile's stores are younger
     if (KT > 1)
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(16 + kStores) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStores) : "memory");
-    v8i wa[4], xa[4], wb[4], xb[4];
-    w8a8_frags(0, 0, row_w, row_x, g, wa, xa);
-    v16f acc[4][4];
+    // stage 0's fragments but xf[7] and wf[4..7], which the stage reads itself
+    v8i wf[8], xf[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int f = 0; f < 4; ++f) read_frag16(wf[f], lds8_w(0), ow, f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int f = 0; f < 7; ++f) read_frag16(xf[f], lds8_x(0), ox, f);
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[i][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // Stage kinds: s <= KT - 4 copies stage s + 2 (never the last, so no K
+    // tail); s = KT - 3 copies the last stage with its tail masked; s = KT - 2
+    // copies nothing; s = KT - 1 is the last. The mid-stage wait of stage 0
+    // also skips the previous tile's stores.
     int s = 0;
-    // steady state: stage s + 2 exists and is not the last (no K tail)
-    if (KT >= 4) {
-      w8a8_stage<16 + kStores>(acc, wa, xa, wb, xb, pw, px, 0, row_w, row_x, g, wave_off);
-      for (s = 1; s + 4 <= KT; ++s) w8a8_stage<16>(acc, wa, xa, wb, xb, pw, px, s, row_w, row_x, g, wave_off);
-    }
-    // the stages before the last: copy only what exists, K tail masked
-    for (; s + 1 < KT; ++s) {
-      w8a8_frags(s & 1, 1, row_w, row_x, g, wb, xb);
-      w8a8_mma(acc, wa, xa);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (s + 2 < KT) {
-        pw.copy(lds8_w(s & 1), (s + 2) * 128, K, wave_off);
-        px.copy(lds8_x(s & 1), (s + 2) * 128, K, wave_off);
+    if (KT >= 2) {
+      if (KT >= 4)
+        w8a8_stage<1, kStores, false>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off);
+      else if (KT == 3)
+        w8a8_stage<2, kStores, false>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off);
+      else
+        w8a8_stage<0, kStores, false>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off);
+      for (s = 1; s + 3 < KT; ++s)
+        w8a8_stage<1, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+      if (s == KT - 3) {
+        w8a8_stage<2, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+        ++s;
       }
-      w8a8_frags((s + 1) & 1, 0, row_w, row_x, g, wa, xa);
-      w8a8_mma(acc, wb, xb);
+      if (s == KT - 2) {
+        w8a8_stage<0, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+        ++s;
+      }
     }
-    // the last stage: once its k-step-1 fragments are in registers no wave
-    // reads the pipeline buffers, and the next tile's first stages go out
-    w8a8_frags(s & 1, 1, row_w, row_x, g, wb, xb);
-    w8a8_mma(acc, wa, xa);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int next = slot + (int)gridDim.x;
-    if (next < a.total_tiles) {
+    // the last stage issues the next tile's first stages: plan them now
+    if (has_next) {
       tc = tile_at<kTN>(a, next);
       plan_tile(tc);
-      w8a8_first_stages(pw, px, K, KT, wave_off);
     }
-    w8a8_mma(acc, wb, xb);
+    w8a8_stage<0, 0, true>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+
     if constexpr (kSwiGLU) {
       const int I = grp.n;
       const __amdgpu_buffer_rsrc_t out = h_rsrc(grp.y, a.m, cur.m0 + wm * 128, I, 1);
@@ -774,7 +922,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
           epilogue_rows(acc, j, epi, grp, grp.alpha * alpha_mul, out, cur.n0 + wn * 128, lane);
       }
     }
-    if (next >= a.total_tiles) break;
+    if (!has_next) break;
     slot = next;
   }
 }
