@@ -30,7 +30,9 @@ def both_weights(w, s_w, gpu):
 
 @pytest.mark.parametrize(
     "m,n,k",
-    [(1, 8, 16), (7, 24, 48), (33, 40, 80), (64, 64, 64), (300, 520, 1040), (257, 264, 4096 + 16), (513, 1032, 272)],
+    # K = 128, 256, 384, 512: exactly 1, 2, 3 and 4 K stages of 128 bytes (every stage kind of the pipeline)
+    [(1, 8, 16), (7, 24, 48), (33, 40, 80), (64, 64, 64), (300, 520, 1040), (257, 264, 4096 + 16), (513, 1032, 272),
+     (31, 48, 128), (200, 256, 256), (65, 136, 384), (129, 264, 512)],
 )
 def test_w8a8_random_codes(gpu, m, n, k):
     announce("w8a8 random codes m=%d n=%d k=%d" % (m, n, k))
@@ -42,7 +44,8 @@ def test_w8a8_random_codes(gpu, m, n, k):
     assert_gemm_close(y, linear.gemm_w8a8(q.numpy(), qw.numpy(), s_in, s_w), "w8a8 %dx%dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 8, 16), (33, 40, 80), (300, 520, 1040), (257, 264, 4096 + 16)])
+@pytest.mark.parametrize("m,n,k", [(1, 8, 16), (33, 40, 80), (300, 520, 1040), (257, 264, 4096 + 16), (65, 136, 64),
+                                   (129, 264, 128), (40, 256, 192)])
 def test_w8a16_random_codes(gpu, m, n, k):
     announce("w8a16 random codes m=%d n=%d k=%d" % (m, n, k))
     x = normal_bf16((m, k), 0.35, 3000 + m)

@@ -8,12 +8,11 @@
 //     y[m, n] = bf16( sum_k x[m, k] dec(qw[n, k]) * s_w )
 //     The E4M3 weight tile is staged in LDS at one byte per element and
 //     converted exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1) on its
-//     way to v_mfma_f32_32x32x16_bf16.
+//     way to v_mfma_f32_16x16x32_bf16.
 //
 // Shared structure:
 //   * A workgroup of 4 waves owns a 256 (M) x 256 (N) output tile; wave
-//     (wm, wn) owns the 128 x 128 quarter (wm, wn), as 8 x 8 blocks of
-//     16 x 16 (W8A8) or 4 x 4 blocks of 32 x 32 (W8A16).
+//     (wm, wn) owns the 128 x 128 quarter (wm, wn) as 8 x 8 blocks of 16 x 16.
 //   * The weight is the MFMA "A" operand and the activation the "B" operand,
 //     so the accumulator D[n][m] gives every lane four consecutive n of one
 //     output row.
@@ -47,7 +46,6 @@ void gemm_plan(GemmArgs& a) {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -82,24 +80,23 @@ __device__ __forceinline__ uint8_t* lds8_x(int buf) { return lds_mem + (2 + buf)
 __device__ __forceinline__ uint8_t* lds16_w(int s) { return lds_mem + s * kStageE4M3; }
 __device__ __forceinline__ uint8_t* lds16_x(int s) { return lds_mem + kStages16 * kStageE4M3 + s * kStageBf16; }
 
-// LDS tile layouts. A ds_read_b128 wave is served 16 lanes per cycle; the
-// layouts keep every MFMA fragment read free of bank conflicts for the lane
-// groupings a 64-bank LDS may use (16 consecutive lanes, lanes {8k..8k+7}
-// with {8k+32..8k+39}, or lanes sharing lane-index bits 1 and 4 -- the
-// grouping the LDS bank-conflict counters of a plain XOR layout pointed to),
-// for every read pattern of both kernels.
-//   128-byte rows of the W8A16 bf16 tiles (32 x 32 fragments: 32 rows,
-//     lane halves 32 bytes apart): chunk c of row r in physical chunk
-//     c ^ swz8(r).
-//   128-byte rows of the W8A8 E4M3 tiles (16 x 128 fragments: 16 rows, lane
-//     quarters 32 bytes apart): chunk c of row r in physical chunk
-//     c ^ swz16(r). swz16 is linear in row bits 1-3; the one nonzero
-//     combination of those bits it maps to chunk bit 2 alone is bits 1 + 3,
-//     which no grouping above varies on its own (swz8 here would put two
-//     lanes of the bits-1-and-4 grouping on one bank).
-//   64-byte rows (W8A16 E4M3 weight tile): logical row r in physical row
-//     row64(r) = r ^ (bit3(r) << 1) (a swap inside groups of 4 rows), chunk
-//     c in physical chunk c ^ swz4(r).
+// LDS tile layouts (fragment reads take 16-row blocks, lane (r, q) =
+// (l % 16, l / 16) reading row r). The swizzles were chosen against the lane
+// groupings a 64-bank LDS may serve together for a 16-byte read (16
+// consecutive lanes, lanes {8k..8k+7} with {8k+32..8k+39}, or lanes sharing
+// lane-index bits 1 and 4); the hardware's conflict counter does not follow
+// that model closely (it reads the same for several W8A8 layouts), so the
+// choices are measured rather than proven.
+//   128-byte rows of the W8A8 E4M3 tiles (lane quarters 32 bytes apart):
+//     chunk c of row r in physical chunk c ^ swz16(r). swz16 is linear in
+//     row bits 1-3; the one nonzero combination of those bits it maps to
+//     chunk bit 2 alone is bits 1 + 3, which no grouping above varies on its
+//     own.
+//   128-byte rows of the W8A16 bf16 activation tiles (lane quarters 16
+//     bytes apart): chunk c of row r in physical chunk c ^ swz8(r).
+//   64-byte rows of the W8A16 E4M3 weight tile (lane quarters 8 bytes
+//     apart): logical row r in physical row row64(r) = r ^ (bit3(r) << 1) (a
+//     swap inside groups of 4 rows), chunk c in physical chunk c ^ swz4(r).
 // All are XORs / involutions, hence bijections on the tile.
 __device__ __forceinline__ int row64(int r) { return r ^ (((r >> 3) & 1) << 1); }
 __device__ __forceinline__ int swz4(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
@@ -289,33 +286,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // store writes 16 bytes per lane; straight from the accumulators every
 // store instruction would scatter over 16 or 32 rows.
 //
-// Accumulator layouts (both give a lane four consecutive n of one row per
-// register quad):
-//   W8A16, 32 x 32 blocks, acc[i][j] = D[n][m] of n-block i, m-block j:
-//     lane l, register v -> m = 32 j + l % 32, n = 32 i + 8 (v / 4) +
-//     4 (l / 32) + v % 4.
-//   W8A8, 16 x 16 blocks, acc[i][b] = D[n][m] of n-block i, m-block b:
-//     lane l, register v -> m = 16 b + l % 16, n = 16 i + 4 (l / 16) + v;
-//     rows [32 j, 32 j + 32) are m-blocks 2 j and 2 j + 1.
+// Accumulators: 16 x 16 blocks, acc[i][b] = D[n][m] of n-block i, m-block b;
+// lane l, register v -> m = 16 b + l % 16, n = 16 i + 4 (l / 16) + v (four
+// consecutive n of one row per lane); rows [32 j, 32 j + 32) are m-blocks
+// 2 j and 2 j + 1.
 
 // Stage bf16(acc * alpha) (binary16 with kF16) of rows [32 j, 32 j + 32).
-template <bool kF16>
-__device__ __forceinline__ void stage_rows(const v16f (&acc)[4][4], int j, uint8_t* stage, float alpha, int lane) {
-  const int h = lane >> 5;
-  const int m = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = i * 4 + t;  // 16-byte chunk of n = 32 i + 8 t + 4 h
-      u32x2 v;
-      v[0] = h16x2<kF16>(acc[i][j][4 * t] * alpha, acc[i][j][4 * t + 1] * alpha);
-      v[1] = h16x2<kF16>(acc[i][j][4 * t + 2] * alpha, acc[i][j][4 * t + 3] * alpha);
-      *reinterpret_cast<u32x2*>(stage + m * 256 + ((c ^ (m & 15)) * 16) + h * 8) = v;
-    }
-  }
-}
-
 template <bool kF16>
 __device__ __forceinline__ void stage_rows(const f32x4 (&acc)[8][8], int j, uint8_t* stage, float alpha, int lane) {
   const int q = lane >> 4;
@@ -337,24 +313,6 @@ __device__ __forceinline__ void stage_rows(const f32x4 (&acc)[8][8], int j, uint
 
 // Stage acc * alpha in float32, columns [64 hf, 64 hf + 64) of rows
 // [32 j, 32 j + 32).
-__device__ __forceinline__ void stage_rows_f32(const v16f (&acc)[4][4], int j, int hf, uint8_t* stage, float alpha,
-                                               int lane) {
-  const int h = lane >> 5;
-  const int m = lane & 31;
-#pragma unroll
-  for (int ii = 0; ii < 2; ++ii) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = ii * 8 + t * 2 + h;  // 16-byte chunk of n = 64 hf + 32 ii + 8 t + 4 h
-      const int i = 2 * hf + ii;
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(acc[i][j][4 * t + e] * alpha);
-      *reinterpret_cast<u32x4*>(stage + m * 256 + ((c ^ (m & 15)) * 16)) = v;
-    }
-  }
-}
-
 __device__ __forceinline__ void stage_rows_f32(const f32x4 (&acc)[8][8], int j, int hf, uint8_t* stage, float alpha,
                                                int lane) {
   const int q = lane >> 4;
@@ -968,11 +926,11 @@ __device__ __forceinline__ W16Op<kForm> dequant8(uint32_t d0, uint32_t d1) {
 }
 
 template <int kForm>
-__device__ __forceinline__ v16f w16_mfma(W16Op<kForm> w, u32x4 x, v16f acc) {
+__device__ __forceinline__ f32x4 w16_mfma(W16Op<kForm> w, u32x4 x, f32x4 acc) {
   if constexpr (kForm == kFormF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(w, __builtin_bit_cast(v8h, x), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(w, __builtin_bit_cast(v8h, x), acc, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, __builtin_bit_cast(v8bf, x), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, __builtin_bit_cast(v8bf, x), acc, 0, 0, 0);
 }
 
 constexpr int kW16Copies = 12;  // copies per thread per stage
@@ -1050,48 +1008,60 @@ struct W16Copier {
   }
 };
 
-// One half stage of fragments: weight chunk (2h + g) of rows row_w + 32 i
-// (16 E4M3 each) and activation chunks 4h + 2g + e of rows row_x + 32 j
-// (8 bf16 each, x[2 j + e]).
+// One half stage (32 K values) of fragments for v_mfma_f32_16x16x32_bf16
+// (or _f16): lane (r, q) = (l % 16, l / 16) holds K values [8 q, 8 q + 8) of
+// the half for row r of each 16-row block -- weight block i as 8 E4M3 bytes
+// (w[i]), activation block b as 8 bf16 (x[b]). Both operands take the same
+// K values per lane, so the products pair up.
 struct W16Half {
-  u32x4 w[4];
+  u32x2 w[8];
   u32x4 x[8];
 };
 
-// Per-lane byte offsets of a lane's chunks for half h (e: activation chunk
-// of the pair), inside the weight and activation tiles of a buffer; block
-// i or j adds 2048 (64-byte rows) or 4096 (128-byte rows).
+// Per-lane byte offsets of a lane's fragments for half h inside the weight
+// and activation tiles of a buffer; block i or b adds 1024 (16 rows of 64
+// bytes) or 2048 (16 rows of 128 bytes). Blocks 16 rows apart keep row bits
+// 0-3 and with them row64, swz4 and swz8 of the lane's row.
 struct W16Addr {
-  uint32_t w[2], x[2][2];
-  __device__ __forceinline__ void init(int row_w, int row_x, int g) {
+  uint32_t w[2], x[2];
+  __device__ __forceinline__ void init(int row_w, int row_x, int q) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      w[h] = row64(row_w) * 64 + ((2 * h + g) ^ swz4(row_w)) * 16;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) x[h][e] = row_x * 128 + ((4 * h + 2 * g + e) ^ swz8(row_x)) * 16;
+      // E4M3 bytes [32 h + 8 q, +8) of the 64-byte weight row: half (q & 1) of chunk 2 h + q / 2
+      w[h] = row64(row_w) * 64 + ((2 * h + (q >> 1)) ^ swz4(row_w)) * 16 + (q & 1) * 8;
+      // bf16 values [32 h + 8 q, +8) of the 128-byte activation row: chunk 4 h + q
+      x[h] = row_x * 128 + ((4 * h + q) ^ swz8(row_x)) * 16;
     }
   }
 };
 
-// Read number r (0..11) of half h of buffer b into f.
-__device__ __forceinline__ void w16_read(W16Half& f, int r, int b, int h, const W16Addr& ad) {
-  if (r < 4)
-    f.w[r] = lds_chunk(lds16_w(b), ad.w[h] + r * 2048);
+// Read r (0..15) of half h of the stage in buffer b into f: r < 8 weight
+// block r, else activation block r - 8. The buffer's base is passed in
+// (lds_w, lds_x) so that the compiler forms one address per half and uses
+// the instruction offset for the block.
+__device__ __forceinline__ void w16_read(W16Half& f, int r, const uint8_t* lds_w, const uint8_t* lds_x, int h,
+                                         const W16Addr& ad) {
+  if (r < 8)
+    f.w[r] = *reinterpret_cast<const u32x2*>(lds_w + ad.w[h] + r * 1024);
   else
-    f.x[r - 4] = lds_chunk(lds16_x(b), ad.x[h][(r - 4) & 1] + ((r - 4) >> 1) * 4096);
+    f.x[r - 8] = lds_chunk(lds_x, ad.x[h] + (r - 8) * 2048);
 }
 
-// Half stage on set f: 32 MFMAs (two k-steps of 16), each followed by at
-// most one memory operation:
-//   first half : the 12 reads of the second half's fragments (set nf) and
-//                copies 0-5 of stage g + 2. Its buffer held stage g - 1,
-//                which every wave finished reading before the previous
-//                stage's barrier (lgkmcnt(0) precedes it).
+// Half stage on set f: 64 MFMAs, weight-block-major (MFMA t: weight block
+// t / 8, activation block t % 8); weight block i + 1 is dequantized four
+// MFMAs before its first use. Each MFMA is followed by at most one memory
+// operation:
+//   first half : the 16 reads of the second half's fragments (set nf) at
+//                odd slots 1-31, and copies 0-5 of stage g + 2 five slots
+//                apart from slot 34. Their buffer held stage g - 1, which
+//                every wave finished reading before the previous stage's
+//                barrier (lgkmcnt(0) precedes it).
 //   second half: after MFMA 3, vmcnt + lgkmcnt(0) + barrier: stage g + 1 has
-//                landed for every wave (only the 6 copies just issued, and
-//                after a tile change the previous tile's 32 output stores,
-//                are younger than its copies); then the 12 reads of the
-//                next stage's first-half fragments and copies 6-11.
+//                landed for every wave (only the 6 copies of the first half,
+//                and after a tile change the previous tile's output stores,
+//                are younger than its copies); then the 16 reads of the next
+//                stage's first-half fragments at even slots 4-34, and copies
+//                6-11 five slots apart from slot 37.
 // vmcnt encodes at most 63: a larger count waits for some of the younger
 // stores too, which is still correct.
 template <bool kSwiGLU, int kForm>
@@ -1100,18 +1070,25 @@ constexpr int kW16AfterStoresWait = kW16Copies / 2 + kW16EpilogueStores<kSwiGLU,
                                         : 63;
 
 template <bool kSwiGLU, int kForm, class Copier>
-__device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W16Half& nf, int nb, int nh,
+__device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W16Half& nf, int nb, int nh,
                                          const W16Addr& ad, Copier& cp, int cbuf, int K, int XK, uint32_t wave_off,
                                          bool second, bool after_stores) {
-  W16Op<kForm> wf[4];
+  // the next set's buffer base, kept opaque so that per-block addresses are
+  // not precomputed for every buffer
+  uint32_t bw = lds_addr(lds16_w(nb)), bx = lds_addr(lds16_x(nb));
+  asm volatile("" : "+v"(bw), "+v"(bx));
+  const uint8_t* nw = lds_mem + (bw - lds_addr(lds_mem));
+  const uint8_t* nx = lds_mem + (bx - lds_addr(lds_mem));
+  W16Op<kForm> wcur = dequant8<kForm>(f.w[0][0], f.w[0][1]), wnext;
 #pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const int e = t >> 4, i = (t >> 2) & 3, j = t & 3;
-    if (j == 0) wf[i] = dequant8<kForm>(f.w[i][2 * e], f.w[i][2 * e + 1]);
-    acc[i][j] = w16_mfma<kForm>(wf[i], f.x[2 * j + e], acc[i][j]);
+  for (int t = 0; t < 64; ++t) {
+    const int i = t >> 3, b = t & 7;
+    if (b == 4 && i < 7) wnext = dequant8<kForm>(f.w[i + 1][0], f.w[i + 1][1]);
+    acc[i][b] = w16_mfma<kForm>(wcur, f.x[b], acc[i][b]);
+    if (b == 7) wcur = wnext;
     if (!second) {
-      if ((t & 1) && t < 24) w16_read(nf, t >> 1, nb, nh, ad);
-      if (t >= 4 && t <= 24 && (t & 3) == 0) cp.issue((t >> 2) - 1, cbuf, K, XK, wave_off);
+      if ((t & 1) && t < 32) w16_read(nf, t >> 1, nw, nx, nh, ad);
+      if (t >= 34 && (t - 34) % 5 == 0 && t <= 59) cp.issue((t - 34) / 5, cbuf, K, XK, wave_off);
     } else {
       if (t == 3) {
         if (after_stores)
@@ -1120,8 +1097,8 @@ __device__ __forceinline__ void w16_half(v16f (&acc)[4][4], const W16Half& f, W1
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2) : "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      if (t >= 4 && t < 28 && (t & 1) == 0) w16_read(nf, (t - 4) >> 1, nb, nh, ad);
-      if (t >= 5 && t <= 25 && (t & 3) == 1) cp.issue(6 + ((t - 5) >> 2), cbuf, K, XK, wave_off);
+      if (t >= 4 && t <= 34 && (t & 1) == 0) w16_read(nf, (t - 4) >> 1, nw, nx, nh, ad);
+      if (t >= 37 && (t - 37) % 5 == 0 && t <= 62) cp.issue(6 + (t - 37) / 5, cbuf, K, XK, wave_off);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1145,7 +1122,7 @@ gemm_w8a16_kernel(const GemmArgs a) {
   const int KT = (XK + 63) / 64;  // stages: 64 activation values each
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
   W16Addr ad;
-  ad.init(wn * 128 + (lane & 31), wm * 128 + (lane & 31), lane >> 5);
+  ad.init(wn * 128 + (lane & 15), wm * 128 + (lane & 15), lane >> 4);
 
   W16Copier<kSwiGLU, kForm> cp;
   cp.start_tile(a, blockIdx.x, tid);
@@ -1159,16 +1136,16 @@ gemm_w8a16_kernel(const GemmArgs a) {
 
   W16Half fa, fb;
 #pragma unroll
-  for (int r = 0; r < 12; ++r) w16_read(fa, r, 0, 0, ad);
+  for (int r = 0; r < 16; ++r) w16_read(fa, r, lds16_w(0), lds16_x(0), 0, ad);
   int b = 0;  // buffer of the current stage
 
   for (int tile_slot = blockIdx.x; tile_slot < a.total_tiles; tile_slot += (int)gridDim.x) {
     const bool first = tile_slot == (int)blockIdx.x;
-    v16f acc[4][4];
+    f32x4 acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int s = 0; s < KT; ++s) {
       const int nb = b == 2 ? 0 : b + 1;      // next stage's buffer
