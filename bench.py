@@ -504,6 +504,14 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
             c = timed(lambda: fp8lin.fp8lin_gemm_w8a8_splitk(q2[:m], qw2, c2.input_scale, c2.weight_scale,
                                                              splits=sk, out=y2, workspace=ws_sk), reps)
             row["w8a8_splitk"] = {"splits": sk, "tflops": round(f / c / 1e9, 1)}
+        sk16 = fp8lin.fp8lin_gemm_w8a16_splitk_choice(m, K, K)
+        if sk16 > 1:
+            ws16 = torch.empty(4 * m * K * 4, dtype=torch.uint8, device=dev)
+            row["w8a16_splitk"] = {"splits": sk16}
+            for sp in (2, 4):
+                c = timed(lambda: fp8lin.fp8lin_gemm_w8a16_splitk(x2[:m], qw2, c2.weight_scale, splits=sp, out=y2,
+                                                                  workspace=ws16), reps)
+                row["w8a16_splitk"]["tflops_%d_splits" % sp] = round(f / c / 1e9, 1)
         rows["proj_%dx4096x4096" % m] = row
 
     # step policy: host call per transformer forward

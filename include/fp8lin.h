@@ -216,6 +216,39 @@ int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, in
 int32_t fp8lin_gemm_w8a8_splitk_choice(int64_t M, int64_t N, int64_t K);
 
 /*
+ * fp8lin_gemm_w8a16 with K split into `splits` slices, for shapes with too
+ * few output tiles to fill the device (e.g. M = 1024 tokens of a 4096 ->
+ * 4096 projection: 64 tiles of 256 x 256 for 256 compute units). The same
+ * W8A16 product ([DF-14664] "Behavior": the 16-bit step keeps the FP8
+ * weight and the 16-bit activation) computed as one launch over the
+ * slices, each writing its unscaled float32 partial to `workspace`
+ * ([splits][M][N] float32), then a reduction that sums the parts in slice
+ * order and writes
+ *   y[m, n] = bf16_RNE( (sum_s partial_s[m, n]) * weight_scale )
+ * (the float32 summation order differs from fp8lin_gemm_w8a16's, so the
+ * two may differ in the last bf16 bit; both meet the same tolerance).
+ *   x_dtype    FP8LIN_DT_BF16 (binary16 activations: FP8LIN_EUNSUPPORTED
+ *              when splits > 1, the reduction writes bf16; E4M3 or float32:
+ *              FP8LIN_EDTYPE)
+ *   splits     1 (plain fp8lin_gemm_w8a16, workspace unused), 2 or 4; K a
+ *              multiple of 16 * splits (else FP8LIN_ELAYOUT)
+ *   workspace  device, >= splits * M * N * 4 bytes, 16-byte aligned,
+ *              caller-owned scratch (else FP8LIN_EINVAL)
+ * Other arguments and rules as fp8lin_gemm_w8a16. Launches counted as
+ * FP8LIN_KERNEL_GEMM_W8A16 and FP8LIN_KERNEL_SPLITK_REDUCE.
+ */
+int32_t fp8lin_gemm_w8a16_splitk(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,
+                                 int64_t K, int64_t ldy, float weight_scale, int32_t splits, void* workspace,
+                                 int64_t workspace_bytes, hipStream_t stream);
+
+/* The split count fp8lin_gemm_w8a16_splitk does best with on the current
+ * device: doubled from 1 (up to 4) while the tiles of all slices still fit
+ * the compute units and every slice keeps at least 512 K elements (at
+ * 1024 x 4096 x 4096 this gives 4). Host only (it reads the device's
+ * compute-unit count once). */
+int32_t fp8lin_gemm_w8a16_splitk_choice(int64_t M, int64_t N, int64_t K);
+
+/*
  * The GEMMs of a shared-input projection group on an activation quantized
  * once ([TRT-17476] "What changed": every projection of the group consumes
  * the same FP8 tensor, each with its own weight_scale), in one launch:

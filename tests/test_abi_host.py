@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -419,3 +419,37 @@ def test_gemm_splitk_validation(lib):
     assert gsk(lib, M=0, qx=None, ws=None, wsb=0) == fp8lin.OK
     assert gsk(lib, M=0, qx=None, splits=1) == fp8lin.OK
     assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)] == before
+
+
+def gsk16(lib, M=2, N=64, K=64, ldy=64, sw=0.5, splits=2, ws=FAKE, wsb=2 * 2 * 64 * 4, x=FAKE, dt=fp8lin.DT_BF16):
+    return lib.fp8lin_gemm_w8a16_splitk(x, dt, FAKE, FAKE, M, N, K, ldy, sw, splits, ws, wsb, None)
+
+
+def test_gemm_w8a16_splitk_validation(lib):
+    """Every failing call returns before any launch (no GPU here); M = 0 is a no-op."""
+    assert gsk16(lib, splits=3) == fp8lin.EINVAL
+    assert gsk16(lib, dt=fp8lin.DT_E4M3) == fp8lin.EDTYPE
+    assert gsk16(lib, dt=fp8lin.DT_F32) == fp8lin.EDTYPE
+    assert gsk16(lib, dt=fp8lin.DT_F16) == fp8lin.EUNSUPPORTED  # the reduction writes bf16
+    assert gsk16(lib, K=16 * 4 + 16, splits=4) == fp8lin.ELAYOUT
+    assert gsk16(lib, wsb=2 * 2 * 64 * 4 - 1) == fp8lin.EINVAL
+    assert gsk16(lib, ws=None) == fp8lin.EINVAL
+    assert gsk16(lib, ws=FAKE + 8) == fp8lin.ELAYOUT
+    assert gsk16(lib, x=FAKE + 8) == fp8lin.ELAYOUT
+    assert gsk16(lib, sw=float("nan")) == fp8lin.ESCALE
+    assert gsk16(lib, ldy=32) == fp8lin.ELAYOUT
+    before = [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A16, fp8lin.KERNEL_SPLITK_REDUCE)]
+    assert gsk16(lib, M=0, x=None, ws=None, wsb=0) == fp8lin.OK
+    assert gsk16(lib, M=0, x=None, splits=1) == fp8lin.OK
+    assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A16, fp8lin.KERNEL_SPLITK_REDUCE)] == before
+
+
+def test_gemm_w8a16_splitk_choice(lib):
+    """Without a GPU the compute-unit count falls back to 256 (MI355X)."""
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(16384, 4096, 4096) == 1  # 1024 tiles fill the device
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(8192, 4096, 4096) == 1
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 4096) == 4  # 64 tiles x 4 slices of 1024
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 1024) == 2  # two slices of 512; four would be 256
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 512) == 1
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(128, 512, 512) == 1
+    assert lib.fp8lin_gemm_w8a16_splitk_choice(0, 4096, 4096) == 1

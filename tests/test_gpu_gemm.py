@@ -230,6 +230,39 @@ def test_gemm_w8a8_splitk(gpu, m, n, k, splits):
     assert np.all(np.abs(a - b) <= obf16.ulp(np.maximum(np.abs(a), np.abs(b))))
 
 
+@pytest.mark.parametrize("m,n,k,splits", [(1024, 4096, 4096, 2), (1024, 4096, 4096, 4), (300, 528, 1024, 4),
+                                          (77, 64, 128, 2)])
+def test_gemm_w8a16_splitk(gpu, m, n, k, splits):
+    """W8A16 with K split into float32 partials, summed in slice order: the oracle's tolerance, both the split
+    and the unsplit GEMM within the float32-summation bound of the exact product (their summation orders
+    differ, and bf16 x E4M3 products carry more bits than one bf16 ulp can absorb under cancellation), and
+    nothing written past the partials."""
+    announce("gemm_w8a16_splitk m=%d n=%d k=%d splits=%d" % (m, n, k, splits))
+    x = normal_bf16((m, k), 0.35, 63)
+    w = normal_bf16((n, k), 0.02, 64)
+    s_w = max_calibrated_scale(w)
+    qw = fp8lin.fp8lin_quantize_static(w.to(gpu), s_w)
+    xg = x.to(gpu)
+    need = splits * m * n * 4
+    ws = torch.full((need + 256,), 0x5A, dtype=torch.uint8, device=gpu)
+    c0 = [fp8lin.fp8lin_launch_count(i) for i in (fp8lin.KERNEL_GEMM_W8A16, fp8lin.KERNEL_SPLITK_REDUCE)]
+    y = fp8lin.fp8lin_gemm_w8a16_splitk(xg, qw, s_w, splits=splits, workspace=ws)
+    c1 = [fp8lin.fp8lin_launch_count(i) for i in (fp8lin.KERNEL_GEMM_W8A16, fp8lin.KERNEL_SPLITK_REDUCE)]
+    assert [b - a for a, b in zip(c0, c1)] == [1, 1]
+    y_plain = fp8lin.fp8lin_gemm_w8a16(xg, qw, s_w)
+    torch.cuda.synchronize()
+    assert torch.all(ws[need:] == 0x5A)
+    rows = sample_rows(m, 96, 23) if m > 512 else np.arange(m)
+    qwr = linear.quantize_static(f32(w), s_w)
+    assert np.array_equal(u8(qw), qwr)
+    ref = linear.gemm_w8a16(f32(x)[rows], qwr, s_w)
+    assert_gemm_close(f32(y)[rows], ref, "W8A16 split-K")
+    bound = linear.gemm_w8a16_bound(f32(x)[rows].astype(np.float64), qwr, s_w, k, obf16.ulp)
+    for got, what in ((y, "split"), (y_plain, "unsplit")):
+        err = np.abs(f32(got)[rows].astype(np.float64) - ref)
+        assert np.all(err <= bound), "%s: %d elements outside the float32 bound" % (what, int((err > bound).sum()))
+
+
 def test_gemm_splitk_choice():
     """More slices only while the split grid fills at most half the device and slices keep >= 512 K bytes."""
     assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(16384, 4096, 4096) == 1

@@ -36,6 +36,8 @@ __all__ = [
     "fp8lin_gemm_w8a8_group",
     "fp8lin_gemm_w8a8_splitk",
     "fp8lin_gemm_w8a8_splitk_choice",
+    "fp8lin_gemm_w8a16_splitk",
+    "fp8lin_gemm_w8a16_splitk_choice",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_swiglu_2in",
@@ -99,6 +101,8 @@ EXPORTS = (
     "fp8lin_gemm_w8a8_group",
     "fp8lin_gemm_w8a8_splitk",
     "fp8lin_gemm_w8a8_splitk_choice",
+    "fp8lin_gemm_w8a16_splitk",
+    "fp8lin_gemm_w8a16_splitk_choice",
     "fp8lin_qkv_shared",
     "fp8lin_swiglu_2in_quant",
     "fp8lin_swiglu_2in",
@@ -175,6 +179,8 @@ def load_library():
     lib.fp8lin_gemm_w8a8_dev_scale.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, f32, vp]
     lib.fp8lin_gemm_w8a8_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32, vp, i64, vp]
     lib.fp8lin_gemm_w8a8_splitk_choice.argtypes = [i64, i64, i64]
+    lib.fp8lin_gemm_w8a16_splitk.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, f32, i32, vp, i64, vp]
+    lib.fp8lin_gemm_w8a16_splitk_choice.argtypes = [i64, i64, i64]
     lib.fp8lin_qk_norm_rope.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, f32, vp]
     lib.fp8lin_qkv_w8a8_norm_rope.argtypes = [
         vp, i64, i64, i32, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(f32), f32, ctypes.POINTER(vp),
@@ -301,6 +307,35 @@ def fp8lin_gemm_w8a8_splitk(qx, qw, input_scale, weight_scale, splits=None, out=
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)
         ),
         "fp8lin_gemm_w8a8_splitk",
+    )
+    return out
+
+
+def fp8lin_gemm_w8a16_splitk_choice(m, n, k):
+    """The split count for fp8lin_gemm_w8a16_splitk on this device (1 = no split)."""
+    return int(load_library().fp8lin_gemm_w8a16_splitk_choice(int(m), int(n), int(k)))
+
+
+def fp8lin_gemm_w8a16_splitk(x, qw, weight_scale, splits=None, out=None, ldy=None, workspace=None, stream=None):
+    """fp8lin_gemm_w8a16 with K split into `splits` float32 partial products (default: the device's choice);
+    bf16 activations (binary16 ones only with splits = 1)."""
+    if x.dtype not in _DT_OF:
+        raise TypeError("x must be bfloat16 or float16")
+    dtype = _DT_OF[x.dtype]
+    m, k = _rows(x)
+    n = qw.shape[0]
+    if splits is None:
+        splits = fp8lin_gemm_w8a16_splitk_choice(m, n, k) if dtype == DT_BF16 else 1
+    out, ldy = _gemm_out(x.shape[:-1], n, x.device, out, ldy, x.dtype)
+    need = int(splits) * m * n * 4 if splits > 1 else 16
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(
+        load_library().fp8lin_gemm_w8a16_splitk(
+            _ptr(x), dtype, _ptr(qw), _ptr(out), m, n, k, ldy, float(weight_scale), int(splits),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)
+        ),
+        "fp8lin_gemm_w8a16_splitk",
     )
     return out
 

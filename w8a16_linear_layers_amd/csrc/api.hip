@@ -348,6 +348,60 @@ int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, in
       fp8lin::launch_splitk_reduce(static_cast<const float*>(workspace), splits, y_bf16, M, N, ldy, alpha, stream));
 }
 
+int32_t fp8lin_gemm_w8a16_splitk_choice(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 1;
+  const int64_t tiles = ((M + fp8lin::kTileM - 1) / fp8lin::kTileM) * ((N + fp8lin::kTileN - 1) / fp8lin::kTileN);
+  const int64_t cus = fp8lin::device_cu_count();
+  int32_t splits = 1;
+  // Double while the split grid still fits the device and each slice keeps >= 512 K elements. The
+  // 16-bit product takes twice the matrix-core time of the FP8 one for the same partials, so the
+  // reduction weighs less than in the W8A8 rule (1024 x 4096 x 4096: 2 splits 1.44x, 4 splits 1.72x).
+  while (splits < 4 && tiles * splits * 2 <= cus && K % (16 * 2 * splits) == 0 && K / (2 * splits) >= 512)
+    splits *= 2;
+  return splits;
+}
+
+int32_t fp8lin_gemm_w8a16_splitk(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,
+                                 int64_t K, int64_t ldy, float weight_scale, int32_t splits, void* workspace,
+                                 int64_t workspace_bytes, hipStream_t stream) {
+  if (splits != 1 && splits != 2 && splits != 4) return FP8LIN_EINVAL;
+  if (x_dtype == FP8LIN_DT_E4M3 || x_dtype == FP8LIN_DT_F32) return FP8LIN_EDTYPE;
+  if (x_dtype != FP8LIN_DT_BF16 && x_dtype != FP8LIN_DT_F16) return FP8LIN_EINVAL;
+  if (splits == 1) return fp8lin_gemm_w8a16(x, x_dtype, qw, y_bf16, M, N, K, ldy, weight_scale, stream);
+  if (x_dtype != FP8LIN_DT_BF16) return FP8LIN_EUNSUPPORTED;  // the reduction writes bf16
+  int32_t st = check_gemm_matrix(M, K);
+  if (st != FP8LIN_OK) return st;
+  if (K == 0 || (M > 0 && x == nullptr)) return FP8LIN_EINVAL;
+  if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
+  if (!aligned16(x) || !aligned16(workspace)) return FP8LIN_ELAYOUT;
+  if (K % (16 * splits) != 0) return FP8LIN_ELAYOUT;
+  if (!scale_ok(weight_scale)) return FP8LIN_ESCALE;
+  if (M == 0) return FP8LIN_OK;
+  if (M * N >= kMaxElems) return FP8LIN_EUNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < (int64_t)splits * M * N * 4) return FP8LIN_EINVAL;
+  GemmArgs a{};
+  a.x = x;
+  a.m = (int32_t)M;
+  a.k = (int32_t)K;
+  a.ks = (int32_t)(K / splits);
+  a.ngroups = splits;
+  for (int sp = 0; sp < splits; ++sp) {
+    a.g[sp].w = static_cast<const uint8_t*>(qw);
+    a.g[sp].y = static_cast<uint8_t*>(workspace) + (int64_t)sp * M * N * 4;
+    a.g[sp].n = (int32_t)N;
+    a.g[sp].ldy = (int32_t)N;
+    a.g[sp].alpha = 1.0f;
+    a.g[sp].koff = sp * a.ks;
+  }
+  if ((st = finish_plan(a)) != FP8LIN_OK) return st;
+  count_launch(FP8LIN_KERNEL_GEMM_W8A16);
+  count_launch(FP8LIN_KERNEL_SPLITK_REDUCE);
+  hipError_t e = fp8lin::launch_gemm_w8a16_splitk(a, stream);
+  if (e != hipSuccess) return FP8LIN_EHIP;
+  return hip_status(fp8lin::launch_splitk_reduce(static_cast<const float*>(workspace), splits, y_bf16, M, N, ldy,
+                                                 weight_scale, stream));
+}
+
 int32_t fp8lin_qkv_w8a8_norm_rope(const void* qx, int64_t M, int64_t K, int32_t nproj, const void* const qw[],
                                   const int64_t n_out[], const float weight_scale[], float input_scale,
                                   void* const y_bf16[], const void* q_norm_weight, const void* k_norm_weight,

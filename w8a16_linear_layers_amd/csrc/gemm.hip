@@ -936,8 +936,8 @@ __device__ __forceinline__ f32x4 w16_mfma(W16Op<kForm> w, u32x4 x, f32x4 acc) {
 constexpr int kW16Copies = 12;  // copies per thread per stage
 // Buffer stores per thread per tile: per 32-row block 8 (16-bit output),
 // 16 (float32) or 4 (the fused SwiGLU's 16-bit h).
-template <bool kSwiGLU, int kForm>
-constexpr int kW16EpilogueStores = kSwiGLU ? 16 : (kForm == kFormF32 ? 64 : 32);
+template <bool kSwiGLU, int kForm, bool kSplit = false>
+constexpr int kW16EpilogueStores = kSwiGLU ? 16 : (kForm == kFormF32 || kSplit ? 64 : 32);
 
 // Persistent W8A16 pipeline: K stages of 64 elements; one workgroup per CU
 // walks the tiles of dispatch slots blockIdx.x, blockIdx.x + gridDim.x, ...
@@ -951,7 +951,9 @@ constexpr int kW16EpilogueStores = kSwiGLU ? 16 : (kForm == kFormF32 ? 64 : 32);
 // 128-255 up rows (a.g[0], a.g[1]), as in the fused W8A8 kernel.
 // kForm == kFormF32: the activation is the three-piece bf16 form, 3 stages
 // per 64-element weight block (stage k reads weight block k / 3).
-template <bool kSwiGLU, int kForm>
+// kSplit: group g multiplies K elements [g.koff, g.koff + a.ks) (row pitch
+// a.k), so its copies start koff elements into the weight and activation rows.
+template <bool kSwiGLU, int kForm, bool kSplit = false>
 struct W16Copier {
   CopyPlan<4> pw;  // E4M3 weight, 64-byte stage rows
   CopyPlan<8> px;  // bf16 activation, 128-byte stage rows
@@ -967,9 +969,10 @@ struct W16Copier {
       const int rows = a.g[0].n - tc.n0;
       pw.init2(a.g[0].w + off, rows, a.g[1].w + off, rows, a.k, tid);
     } else {
-      pw.init(a.g[tc.group].w, tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
+      pw.init(a.g[tc.group].w + (kSplit ? a.g[tc.group].koff : 0), tc.n0, a.g[tc.group].n - tc.n0, a.k, tid);
     }
-    px.init(static_cast<const uint8_t*>(a.x), tc.m0, a.m - tc.m0, (int64_t)(kForm == kFormF32 ? a.xk : a.k) * 2, tid);
+    px.init(static_cast<const uint8_t*>(a.x) + (kSplit ? 2 * (int64_t)a.g[tc.group].koff : 0), tc.m0, a.m - tc.m0,
+            (int64_t)(kForm == kFormF32 ? a.xk : a.k) * 2, tid);
   }
 
   // Copy c of the current stage into buffer `buf`: c < 4 weight chunk c,
@@ -1064,12 +1067,12 @@ __device__ __forceinline__ void w16_read(W16Half& f, int r, const uint8_t* lds_w
 //                6-11 five slots apart from slot 37.
 // vmcnt encodes at most 63: a larger count waits for some of the younger
 // stores too, which is still correct.
-template <bool kSwiGLU, int kForm>
-constexpr int kW16AfterStoresWait = kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm> < 63
-                                        ? kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm>
+template <bool kSwiGLU, int kForm, bool kSplit = false>
+constexpr int kW16AfterStoresWait = kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm, kSplit> < 63
+                                        ? kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm, kSplit>
                                         : 63;
 
-template <bool kSwiGLU, int kForm, class Copier>
+template <bool kSwiGLU, int kForm, bool kSplit, class Copier>
 __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W16Half& nf, int nb, int nh,
                                          const W16Addr& ad, Copier& cp, int cbuf, int K, int XK, uint32_t wave_off,
                                          bool second, bool after_stores) {
@@ -1092,7 +1095,7 @@ __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W
     } else {
       if (t == 3) {
         if (after_stores)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16AfterStoresWait<kSwiGLU, kForm>) : "memory");
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16AfterStoresWait<kSwiGLU, kForm, kSplit>) : "memory");
         else
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2) : "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1110,21 +1113,25 @@ __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W
 // a.g[0]: gate, h output, alpha s_gate; a.g[1]: up, alpha s_up.
 // kForm: bf16, binary16 or (not with kSwiGLU) the float32 three-piece form,
 // whose activation rows hold a.xk = 3 * 64 * ceil(K / 64) bf16 values.
-template <bool kSwiGLU, int kForm>
+// kSplit (bf16 only): split-K; every group is one K slice (a.ks elements
+// from g.koff, row pitch a.k) of the same product and stores its unscaled
+// float32 partial to its y.
+template <bool kSwiGLU, int kForm, bool kSplit = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a16_kernel(const GemmArgs a) {
   static_assert(!(kSwiGLU && kForm == kFormF32), "the fused SwiGLU form has a 16-bit h");
+  static_assert(!kSplit || (!kSwiGLU && kForm == kFormBf16), "split-K: the plain bf16 form");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.k;
-  const int XK = kForm == kFormF32 ? a.xk : a.k;  // the 16-bit forms keep XK == K visible
+  const int K = kSplit ? a.ks : a.k;              // K elements this launch's groups multiply
+  const int XK = kForm == kFormF32 ? a.xk : K;  // the 16-bit forms keep XK == K visible
   const int KT = (XK + 63) / 64;  // stages: 64 activation values each
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
   W16Addr ad;
   ad.init(wn * 128 + (lane & 15), wm * 128 + (lane & 15), lane >> 4);
 
-  W16Copier<kSwiGLU, kForm> cp;
+  W16Copier<kSwiGLU, kForm, kSplit> cp;
   cp.start_tile(a, blockIdx.x, tid);
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -1150,8 +1157,8 @@ gemm_w8a16_kernel(const GemmArgs a) {
     for (int s = 0; s < KT; ++s) {
       const int nb = b == 2 ? 0 : b + 1;      // next stage's buffer
       const int cb = b == 0 ? 2 : b - 1;      // buffer of stage + 2
-      w16_half<kSwiGLU, kForm>(acc, fa, fb, b, 1, ad, cp, cb, K, XK, wave_off, false, false);
-      w16_half<kSwiGLU, kForm>(acc, fb, fa, nb, 0, ad, cp, cb, K, XK, wave_off, true, s == 0 && !first);
+      w16_half<kSwiGLU, kForm, kSplit>(acc, fa, fb, b, 1, ad, cp, cb, K, XK, wave_off, false, false);
+      w16_half<kSwiGLU, kForm, kSplit>(acc, fb, fa, nb, 0, ad, cp, cb, K, XK, wave_off, true, s == 0 && !first);
       cp.advance(a, KT, tid);
       b = nb;
     }
@@ -1172,7 +1179,14 @@ gemm_w8a16_kernel(const GemmArgs a) {
       const TileCoord tc = tile_at(a, tile_slot);
       const GemmGroup& grp = a.g[tc.group];
       uint8_t* stage = area + wave * (32 * 256);
-      if constexpr (kForm == kFormF32) {
+      if constexpr (kSplit) {
+        const __amdgpu_buffer_rsrc_t out = out_rsrc<4>(grp, a.m, tc.m0 + wm * 128);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            epilogue_rows_f32<kSplitPartialStore>(acc, j, hf, stage, grp, 1.0f, out, tc.n0 + wn * 128, lane);
+      } else if constexpr (kForm == kFormF32) {
         const __amdgpu_buffer_rsrc_t out = out_rsrc<4>(grp, a.m, tc.m0 + wm * 128);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -1289,6 +1303,15 @@ hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, bool f16, hipStr
                 : f16  ? gemm_w8a16_kernel<true, kFormF16>
                        : gemm_w8a16_kernel<true, kFormBf16>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w8a16_splitk(const GemmArgs& a, hipStream_t s) {
+  static const int cus = cu_count();
+  int grid = cus - cus % kXcds;
+  if (grid <= 0) grid = kXcds;
+  if (grid > a.total_tiles) grid = a.total_tiles;
+  hipLaunchKernelGGL((gemm_w8a16_kernel<false, kFormBf16, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

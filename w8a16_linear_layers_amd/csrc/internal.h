@@ -23,7 +23,7 @@ struct GemmGroup {
   float alpha;       // output scale: s_in * s_w (W8A8) or s_w (W8A16)
   int32_t tile_begin;  // first global tile index of this group
   int32_t tiles_n;     // ceil(n / kTileN)
-  int32_t koff;        // split-K: first K byte of this group's slice (0 otherwise)
+  int32_t koff;        // split-K: first K element of this group's slice (0 otherwise)
 };
 
 struct GemmArgs {
@@ -32,7 +32,7 @@ struct GemmArgs {
   int32_t k;
   int32_t xk;     // W8A16 activation row length: k, or 3 * 64 * ceil(k / 64) for
                   // the three-piece float32 form (0: set to k by the plans)
-  int32_t ks;     // split-K W8A8: the K length of each group's slice (k is the row pitch)
+  int32_t ks;     // split-K: the K length (elements) of each group's slice (k is the row pitch)
   int32_t tiles_m;
   int32_t ngroups;
   int32_t total_tiles;
@@ -74,6 +74,10 @@ hipError_t launch_gemm_w8a8_norm_rope(const GemmArgs& a, hipStream_t s);
 // W8A16 activation forms: bf16, binary16, float32 as three bf16 pieces
 constexpr int kW16Bf16 = 0, kW16F16 = 1, kW16F32 = 2;
 hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s);
+// Split-K W8A16 (bf16 activations): group s multiplies K elements [koff,
+// koff + ks) of x and w and writes its float32 partial sums (no scale) to its
+// y [m, ldy]; launch_splitk_reduce then writes y = bf16(alpha * sum).
+hipError_t launch_gemm_w8a16_splitk(const GemmArgs& a, hipStream_t s);
 // Per-head RMSNorm + rotate-half RoPE of q [tokens, q_heads * head_dim] and
 // k [tokens, k_heads * head_dim] (bf16; k_heads may be 0), head_dim 64 or 128.
 hipError_t launch_qk_norm_rope(const void* q, void* q_out, int q_heads, const void* q_w, const void* k, void* k_out,
