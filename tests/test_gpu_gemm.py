@@ -32,7 +32,9 @@ def both_weights(w, s_w, gpu):
     "m,n,k",
     # K = 128, 256, 384, 512: exactly 1, 2, 3 and 4 K stages of 128 bytes (every stage kind of the pipeline)
     [(1, 8, 16), (7, 24, 48), (33, 40, 80), (64, 64, 64), (300, 520, 1040), (257, 264, 4096 + 16), (513, 1032, 272),
-     (31, 48, 128), (200, 256, 256), (65, 136, 384), (129, 264, 512)],
+     (31, 48, 128), (200, 256, 256), (65, 136, 384), (129, 264, 512),
+     # more tiles than compute units at 1 and 2 K stages: workgroups change tiles inside the last stage
+     (4100, 4104, 128), (2100, 8200, 256)],
 )
 def test_w8a8_random_codes(gpu, m, n, k):
     announce("w8a8 random codes m=%d n=%d k=%d" % (m, n, k))
@@ -45,7 +47,7 @@ def test_w8a8_random_codes(gpu, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 8, 16), (33, 40, 80), (300, 520, 1040), (257, 264, 4096 + 16), (65, 136, 64),
-                                   (129, 264, 128), (40, 256, 192)])
+                                   (129, 264, 128), (40, 256, 192), (4100, 4104, 64), (2100, 8200, 128)])
 def test_w8a16_random_codes(gpu, m, n, k):
     announce("w8a16 random codes m=%d n=%d k=%d" % (m, n, k))
     x = normal_bf16((m, k), 0.35, 3000 + m)
