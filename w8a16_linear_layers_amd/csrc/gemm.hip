@@ -513,7 +513,7 @@ __device__ __forceinline__ void read_frag16(v8i& v, const uint8_t* tile, const i
 // Why 16 x 16 x 128 and not 32 x 32 x 64 (same 128 x 128 wave tile, same
 // LDS traffic): on one MI355X, back-to-back FP8 MFMAs sustain 4.36-4.47
 // PFLOP/s in the 16 x 16 form against 3.96-4.10 in the 32 x 32 form, and the
-// GEMM held 1.96 GHz against 1.67 GHz under the 32 x 32 form -- the board is
+// GEMM held 1.79-1.96 GHz against 1.67 GHz with the 32 x 32 form -- the board is
 // power-limited and the smaller instruction costs less energy per FLOP. The
 // twice as many, half as long MFMAs leave half the time per slot, so the
 // copies are spread three slots apart (two: -1%, one: -6%).
