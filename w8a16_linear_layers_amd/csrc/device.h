@@ -29,12 +29,12 @@ __device__ __forceinline__ float h16_hi(uint32_t w) {
 }
 template <bool kF16>
 __device__ __forceinline__ uint32_t h16x2(float a, float b) {
+  // one packed round-to-nearest-even convert of the pair
+  typedef float f2 __attribute__((ext_vector_type(2)));
   if constexpr (kF16) {
-    const _Float16 lo = (_Float16)a, hi = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
   } else {
-    // one packed round-to-nearest-even convert of the pair
-    typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
   }
