@@ -68,11 +68,22 @@ def events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def timed(fn, reps, warmup=3):
-    """Average device time of fn() over `reps` calls (HIP events on the current stream), ms."""
+def timed(fn, reps, warmup=3, warm_ms=30.0):
+    """Average device time of fn() over `reps` calls (HIP events on the current stream), ms.
+
+    Before timing, fn() runs for about `warm_ms` of device time (sized from one timed call): the shader
+    clock takes a few tens of milliseconds to settle under matrix-core load, and short rows timed right
+    after a different shape would otherwise read low."""
     for _ in range(warmup):
         fn()
     e0, e1 = events(2)
+    torch.cuda.synchronize()
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(min(2000, int(warm_ms / max(e0.elapsed_time(e1), 1e-3)))):
+        fn()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
