@@ -416,6 +416,15 @@ __device__ __forceinline__ void epilogue_rows_norm_rope(const f32x4 (&acc)[8][8]
   asm volatile("" : "+v"(lane));
   const int q = lane >> 4;
   const int r = lane & 15;
+  // the lane's norm weights, the same for both rows of the pass: loaded once per pass
+  u32x2 wv[8];
+  if (active && w != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wv[i] = *reinterpret_cast<const u32x2*>(w + 16 * i + 4 * q);
+      wv[i + 4] = *reinterpret_cast<const u32x2*>(w + 64 + 16 * i + 4 * q);
+    }
+  }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int mb = 2 * j + b;  // m-block
@@ -444,8 +453,7 @@ __device__ __forceinline__ void epilogue_rows_norm_rope(const f32x4 (&acc)[8][8]
       }
       float wa[4] = {1.0f, 1.0f, 1.0f, 1.0f}, wb[4] = {1.0f, 1.0f, 1.0f, 1.0f};
       if (active && w != nullptr) {
-        const u32x2 ga = *reinterpret_cast<const u32x2*>(w + d);
-        const u32x2 gb = *reinterpret_cast<const u32x2*>(w + d + 64);
+        const u32x2 ga = wv[i], gb = wv[i + 4];
         wa[0] = bf16_lo(ga.x); wa[1] = bf16_hi(ga.x); wa[2] = bf16_lo(ga.y); wa[3] = bf16_hi(ga.y);
         wb[0] = bf16_lo(gb.x); wb[1] = bf16_hi(gb.x); wb[2] = bf16_lo(gb.y); wb[3] = bf16_hi(gb.y);
       }
