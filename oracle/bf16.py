@@ -16,14 +16,6 @@ def bits_to_f32(bits):
     return b.view(np.float32)
 
 
-def f32_to_bits_truncate(x):
-    """float32 values that are exactly bf16 -> uint16 bit patterns."""
-    u = np.asarray(x, dtype=np.float32).view(np.uint32)
-    if np.any((u & 0xFFFF) != 0):
-        raise ValueError("value is not exactly representable in bf16")
-    return (u >> 16).astype(np.uint16)
-
-
 def round_rne(v):
     """Round float64 values to the nearest bfloat16 value, ties to even.
 
@@ -45,7 +37,10 @@ def round_rne(v):
 
 
 def ulp(v):
-    """Spacing of bf16 values at |v| (float64)."""
+    """Spacing of bf16 values at |v| (float64): the gap from |v| to the next
+    larger bf16 value, 2**(e-8) for 2**(e-1) <= |v| < 2**e, and the subnormal
+    quantum 2**-133 below the normal range and at zero."""
     v = np.abs(np.asarray(v, dtype=np.float64))
-    _, e = np.frexp(np.where(v > 0, v, 1.0))
+    _, e = np.frexp(v)
+    e = np.where(v > 0, e, -1000)  # zero: the subnormal quantum
     return np.ldexp(1.0, np.maximum(e - 8, -133))

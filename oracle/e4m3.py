@@ -69,11 +69,6 @@ def encode(values):
     return code.astype(np.uint8)
 
 
-def is_nan_code(codes):
-    c = np.asarray(codes, dtype=np.uint8)
-    return (c & 0x7F) == NAN_CODE
-
-
 def midpoints():
     """The 126 rounding midpoints between consecutive non-negative codes."""
     return (_POS_VALUES[:-1] + _POS_VALUES[1:]) / 2.0

@@ -29,11 +29,6 @@ def quantize_static(x, input_scale):
     return e4m3.encode(quotient.astype(np.float64))
 
 
-def dequantize_weight(qw, weight_scale):
-    """weight_scale * decode(qW) in float64 (no rounding to 16 bits)."""
-    return e4m3.decode(qw) * float(np.float32(weight_scale))
-
-
 def gemm_w8a8(q, qw, input_scale, weight_scale):
     """W8A8: y = (sum_k dec(q)[m,k] dec(qW)[n,k]) * s_in * s_w, float64.
 
