@@ -27,11 +27,14 @@ In the same run, on the same resident inputs:
   * cpu_baseline  the CPU oracle on a bounded sample of the same step
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-       (defaults K = W = 100: the matrix cores reach their sustained clock
-       only after some tens of milliseconds of load, so a short warm-up
-       under-reports the steady state)
+       (defaults K = W = 100; after the W warm-up steps, further untimed
+       steps run for about 30 ms of device time, reported as settle_ms: the
+       matrix cores reach their sustained clock only after some tens of
+       milliseconds of load, and every row gets the same settling)
        python bench.py --pmc   (a few launches of each step kernel and a
                                 plain copy, for rocprofv3 counter runs)
+       python bench.py --schedule-only   (the 8-step schedule row alone,
+                                for its kernel trace)
 """
 
 import argparse
@@ -93,6 +96,24 @@ def timed(fn, reps, warmup=3, warm_ms=30.0):
     return e0.elapsed_time(e1) / reps
 
 
+def settle(fn, warm_ms=30.0):
+    """Run fn() for about `warm_ms` of device time (sized from one timed call), so that the shader clock
+    has settled under the load before timing starts; returns the device time spent, ms."""
+    e0, e1 = events(2)
+    torch.cuda.synchronize()
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    n = min(2000, int(np.ceil(warm_ms / max(e0.elapsed_time(e1), 1e-3))))
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def rotating(make, total_bytes, per_set_bytes):
     sets = max(2, int(np.ceil(total_bytes / per_set_bytes)))
     return [make(i) for i in range(sets)]
@@ -148,14 +169,26 @@ def pmc_mode(dev):
     src = torch.ones(256 * 2**20, dtype=torch.uint8, device=dev)  # 256 MiB plain copy
     dst = torch.empty_like(src)
     sw = case.weight_scales
+    # the SwiGLU at [8192, 16384] (E4M3 and bf16 out) and the QK RMSNorm + RoPE on Q and K [16384, 4096]
+    mi, inter, hd = 8192, 16384, 128
+    g = normal_bf16((mi, inter), 0.45, 910).to(dev)
+    u = normal_bf16((mi, inter), 0.45, 911).to(dev)
+    h8 = torch.empty((mi, inter), dtype=torch.uint8, device=dev)
+    h16 = torch.empty((mi, inter), dtype=torch.bfloat16, device=dev)
+    cq, sq = (v.to(dev) for v in rope_tables(M, hd))
+    wq, wk = norm_weight_bf16(hd, 950).to(dev), norm_weight_bf16(hd, 951).to(dev)
+    qo, ko = torch.empty_like(ys[0]), torch.empty_like(ys[1])
     for _ in range(3):
         dst.copy_(src)
         fp8lin.fp8lin_quantize_static(x, case.input_scale, out=qx)
         fp8lin.fp8lin_gemm_w8a8_group(qx, qws, case.input_scale, sw, outs=ys)
         fp8lin.fp8lin_qkv_shared(x, qws, sw, [case.input_scale] * 3, fp8lin.MODE_W8A16, outs=ys)
+        fp8lin.fp8lin_swiglu_2in_quant(g, u, 2.1 / 448, fp8lin.DT_E4M3, out=h8)
+        fp8lin.fp8lin_swiglu_2in_quant(g, u, 1.0, fp8lin.DT_BF16, out=h16)
+        fp8lin.fp8lin_qk_norm_rope(ys[0], ys[1], wq, wk, cq, sq, hd, 1e-6, q_out=qo, k_out=ko)
     torch.cuda.synchronize()
-    log("pmc mode done: 3 x (copy 256 MiB, quantize, grouped gemm_w8a8, grouped gemm_w8a16), "
-        "3 projections of 16384x4096x4096")
+    log("pmc mode done: 3 x (copy 256 MiB, quantize, grouped gemm_w8a8, grouped gemm_w8a16 (3 projections of "
+        "16384x4096x4096), swiglu 8192x16384 E4M3 out, swiglu bf16 out, qk_norm_rope 16384 x 2 x 32 heads of 128)")
 
 
 def main():
@@ -167,6 +200,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 8-step schedule row")
     ap.add_argument("--pmc", action="store_true")
+    ap.add_argument("--schedule-only", action="store_true",
+                    help="only the 8-step schedule row (one warm-up and two timed schedules), for kernel traces")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -182,6 +217,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.pmc:
         pmc_mode(dev)
+        return
+    if args.schedule_only:
+        print(json.dumps({"schedule_cfg5": schedule_cfg5(dev, step_policy_of_workload())}), flush=True)
         return
 
     log("generating the shared-QKV workload (x [16384, 4096], three 4096x4096 weights)")
@@ -206,7 +244,7 @@ def main():
 
     for _ in range(args.warmup):
         step_w8a8()
-    torch.cuda.synchronize()
+    settle_ms = settle(step_w8a8)
     log("timing %d W8A8 steps" % args.steps)
     gemm_ev = [events(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -222,7 +260,7 @@ def main():
 
     for _ in range(args.warmup):
         step_w8a16()
-    torch.cuda.synchronize()
+    settle16_ms = settle(step_w8a16)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step_w8a16()
@@ -238,6 +276,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        # after the warm-up steps, further untimed steps for ~30 ms of device time (the clock settles under
+        # matrix-core load; every row below gets the same)
+        "settle_ms": round(settle_ms, 2),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -258,6 +299,7 @@ def main():
             "unit": "TFLOP/s",
             "ms_per_step": round(ms16, 4),
             "pct_bf16_peak": round(100 * tf16 / PEAK_BF16_TFLOPS, 2),
+            "settle_ms": round(settle16_ms, 2),
             "dtype": "bf16 activations x E4M3 weights (exact bf16 dequant), fp32 accumulate",
         },
         "roofline": {
@@ -526,9 +568,7 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
         rows["proj_%dx4096x4096" % m] = row
 
     # step policy: host call per transformer forward
-    pol = fp8lin.policy_from_json({"schema_version": 1, "type": "first_last_steps", "index_space": "scheduler_step",
-                                   "default_mode": "w8a8", "overlap": "a16", "first_steps": 3, "last_steps": 3,
-                                   "reasoner": "a16"})
+    pol = step_policy_of_workload()
     trace = [fp8lin.fp8lin_step_policy(pol, 0, i, 8) for i in range(8)]
     t0 = time.perf_counter()
     for i in range(10000):
@@ -538,6 +578,13 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     if schedule_row:
         rows["schedule_cfg5"] = schedule_cfg5(dev, pol)
     return rows
+
+
+def step_policy_of_workload():
+    """The denoising policy of the schedule workload: first 3 and last 3 steps W8A16, the rest W8A8."""
+    return fp8lin.policy_from_json({"schema_version": 1, "type": "first_last_steps", "index_space": "scheduler_step",
+                                    "default_mode": "w8a8", "overlap": "a16", "first_steps": 3, "last_steps": 3,
+                                    "reasoner": "a16"})
 
 
 def schedule_cfg5(dev, pol):
@@ -562,33 +609,43 @@ def schedule_cfg5(dev, pol):
     buf = schedule.Buffers(m, hidden, inter, dev)
     log("schedule row: generating the 16 per-pass inputs")
     inputs = {(st, b): config5_step_input(st, b, m, hidden).to(dev) for st in range(steps) for b in range(2)}
-    run = lambda: schedule.run_schedule(blocks, pol, steps, lambda st, b: inputs[(st, b)], buf)  # noqa: E731
-    run()  # warm-up pass
+    step_ev = {st: events(2) for st in range(steps)}
+
+    def hook(st, mode, done):
+        step_ev[st][1 if done else 0].record()
+
+    def run(fused):
+        return schedule.run_schedule(blocks, pol, steps, lambda st, b: inputs[(st, b)], buf, fused_mlp=fused,
+                                     step_hook=hook)
+
+    run(True)  # warm-up pass
     torch.cuda.synchronize()
-    e0, e1 = events(2)
-    e0.record()
-    trace = run()
-    e1.record()
+    # the schedule as it runs by default: gate/up + SwiGLU in one fused launch on every step
+    trace = run(True)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    # the same schedule with the fused gate/up + SwiGLU launch on its W8A8 steps
-    e2, e3 = events(2)
-    e2.record()
-    schedule.run_schedule(blocks, pol, steps, lambda st, b: inputs[(st, b)], buf, fused_mlp=True)
-    e3.record()
+    step_ms = [step_ev[st][0].elapsed_time(step_ev[st][1]) for st in range(steps)]
+    ms = step_ev[0][0].elapsed_time(step_ev[steps - 1][1])
+    # the same schedule with the split gate/up launch and a separate SwiGLU kernel
+    run(False)
     torch.cuda.synchronize()
-    ms_fused = e2.elapsed_time(e3)
+    ms_split = step_ev[0][0].elapsed_time(step_ev[steps - 1][1])
     flop_pass = 2.0 * m * hidden * (4 * hidden + 3 * inter)  # QKV + out + gate/up + down of one block
-    n8 = sum(1 for t in trace if t == fp8lin.MODE_W8A8)
-    flop = flop_pass * nblocks * 2 * steps
+    flop_step = flop_pass * nblocks * 2
+    flop = flop_step * steps
+    w8 = [t for st, t in enumerate(step_ms) if trace[st] == fp8lin.MODE_W8A8]
+    w16 = [t for st, t in enumerate(step_ms) if trace[st] != fp8lin.MODE_W8A8]
+    kind = lambda ts: {"steps": len(ts), "ms_per_step": round(float(np.mean(ts)), 3),  # noqa: E731
+                       "tflops": round(flop_step / float(np.mean(ts)) / 1e9, 1)} if ts else None
     return {
         "ms": round(ms, 2),
         "tflops": round(flop / ms / 1e9, 1),
-        "ms_fused_mlp": round(ms_fused, 2),
+        "mlp": "fused gate/up + SwiGLU",
+        "ms_split_mlp": round(ms_split, 2),
         "tflop": round(flop / 1e12, 1),
         "trace": "".join("8" if t == fp8lin.MODE_W8A8 else "6" for t in trace),
-        "w8a8_steps": n8,
-        "w8a16_steps": steps - n8,
+        "w8a8_steps": kind(w8),
+        "w8a16_steps": kind(w16),
+        "step_ms": [round(t, 3) for t in step_ms],
     }
 
 

@@ -40,7 +40,8 @@
  *   - Layout requirements (else FP8LIN_ELAYOUT): K and cols multiples of 16;
  *     N and ldy multiples of 8 with ldy >= N; every pointer 16-byte aligned.
  *   - Size limits (else FP8LIN_EUNSUPPORTED): M and rows < 2^31, cols
- *     < 2^24, M*K and rows*cols < 2^40; for the GEMMs K, N and ldy < 2^22.
+ *     < 2^24, M*K and rows*cols < 2^40; for the GEMMs K, N and ldy < 2^22
+ *     and M <= 2^31 - 256.
  *   - A HIP launch error is reported as FP8LIN_EHIP.
  */
 #ifndef FP8LIN_H

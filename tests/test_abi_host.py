@@ -169,6 +169,8 @@ def test_gemm_w8a8_validation(lib):
     assert g8(lib, sw=0.0) == fp8lin.ESCALE
     assert g8(lib, si=2.0**-100, sw=2.0**-100) == fp8lin.ESCALE  # product underflows
     assert g8(lib, M=1 << 31) == fp8lin.EUNSUPPORTED
+    # the tile plans count 256-row tiles in 32 bits: M + 255 must not overflow
+    assert g8(lib, M=(1 << 31) - 255, K=16) == fp8lin.EUNSUPPORTED
     assert g8(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
     assert g8(lib, N=1 << 22, ldy=1 << 22) == fp8lin.EUNSUPPORTED
     assert g8(lib, ldy=1 << 22) == fp8lin.EUNSUPPORTED
@@ -233,6 +235,7 @@ def test_gemm_w8a8_group_validation(lib):
     assert grp(lib, sw=(0.001, 0.0, 0.001)) == fp8lin.ESCALE
     assert grp(lib, si=2.0**-100, sw=(2.0**-100,) * 3) == fp8lin.ESCALE  # alpha underflows
     assert grp(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
+    assert grp(lib, M=(1 << 31) - 255, K=16) == fp8lin.EUNSUPPORTED
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8)
     assert grp(lib, M=0) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GEMM_W8A8) == before
@@ -256,6 +259,7 @@ def test_gate_up_swiglu_validation(lib):
     assert gus(lib, si=2.0**-100, sg=2.0**-100) == fp8lin.ESCALE  # alpha underflows
     assert gus(lib, inter=1 << 22) == fp8lin.EUNSUPPORTED
     assert gus(lib, K=1 << 22) == fp8lin.EUNSUPPORTED
+    assert gus(lib, M=(1 << 31) - 255, K=16) == fp8lin.EUNSUPPORTED
     before = fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU)
     assert gus(lib, M=0, qx=None, h=None) == fp8lin.OK
     assert fp8lin.fp8lin_launch_count(fp8lin.KERNEL_GATE_UP_SWIGLU) == before

@@ -34,7 +34,9 @@ def both_weights(w, s_w, gpu):
     [(1, 8, 16), (7, 24, 48), (33, 40, 80), (64, 64, 64), (300, 520, 1040), (257, 264, 4096 + 16), (513, 1032, 272),
      (31, 48, 128), (200, 256, 256), (65, 136, 384), (129, 264, 512),
      # more tiles than compute units at 1 and 2 K stages: workgroups change tiles inside the last stage
-     (4100, 4104, 128), (2100, 8200, 256)],
+     (4100, 4104, 128), (2100, 8200, 256),
+     # the down projection's K = 16384 (128 stages), and with a K tail
+     (300, 264, 16384), (513, 136, 16384 + 16)],
 )
 def test_w8a8_random_codes(gpu, m, n, k):
     announce("w8a8 random codes m=%d n=%d k=%d" % (m, n, k))
@@ -47,7 +49,8 @@ def test_w8a8_random_codes(gpu, m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 8, 16), (33, 40, 80), (300, 520, 1040), (257, 264, 4096 + 16), (65, 136, 64),
-                                   (129, 264, 128), (40, 256, 192), (4100, 4104, 64), (2100, 8200, 128)])
+                                   (129, 264, 128), (40, 256, 192), (4100, 4104, 64), (2100, 8200, 128),
+                                   (300, 264, 16384), (129, 520, 16384 + 16)])
 def test_w8a16_random_codes(gpu, m, n, k):
     announce("w8a16 random codes m=%d n=%d k=%d" % (m, n, k))
     x = normal_bf16((m, k), 0.35, 3000 + m)

@@ -39,10 +39,14 @@ int32_t check_matrix(int64_t rows, int64_t cols) {
   return FP8LIN_OK;
 }
 
+// The tile plans count M in 256-row tiles with 32-bit arithmetic: M + 255
+// must not overflow.
+constexpr int64_t kMaxGemmRows = (int64_t(1) << 31) - 256;
+
 int32_t check_gemm_matrix(int64_t M, int64_t K) {
   const int32_t st = check_matrix(M, K);
   if (st != FP8LIN_OK) return st;
-  return K >= kMaxGemmDim ? FP8LIN_EUNSUPPORTED : FP8LIN_OK;
+  return K >= kMaxGemmDim || M > kMaxGemmRows ? FP8LIN_EUNSUPPORTED : FP8LIN_OK;
 }
 
 // Shared checks of one projection of a GEMM (weight [n, k], output [m, ldy]).

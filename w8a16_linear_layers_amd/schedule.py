@@ -131,16 +131,23 @@ def stack_forward(blocks: List[BlockWeights], x: torch.Tensor, mode: int, buf: B
     return h
 
 
-def run_schedule(blocks, policy, num_steps, step_inputs, buf, branches=2, fused_mlp=False):
+def run_schedule(blocks, policy, num_steps, step_inputs, buf, branches=2, fused_mlp=False, step_hook=None):
     """Run `num_steps` denoising steps of `branches` CFG passes each.
 
     step_inputs(step, branch) returns the bf16 input of that pass. Returns
     the per-step mode trace (the policy is asked once per step).
+    step_hook(step, mode, done), if given, is called before (done = False)
+    and after (done = True) the passes of each step are enqueued, e.g. to
+    record events that time the step kinds apart.
     """
     trace = []
     for step in range(num_steps):
         mode = fp8lin_step_policy(policy, TOWER_GENERATION, step, num_steps)
         trace.append(mode)
+        if step_hook is not None:
+            step_hook(step, mode, False)
         for branch in range(branches):
             stack_forward(blocks, step_inputs(step, branch), mode, buf, fused_mlp)
+        if step_hook is not None:
+            step_hook(step, mode, True)
     return trace
