@@ -216,6 +216,32 @@ int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, in
  * Host only (it reads the device's compute-unit count once). */
 int32_t fp8lin_gemm_w8a8_splitk_choice(int64_t M, int64_t N, int64_t K);
 
+/* Size of the library's static device scratch array (32 MiB), which each GPU
+ * the library runs on holds until the process ends. */
+#define FP8LIN_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * fp8lin_gemm_w8a8_splitk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result bit for bit, with the
+ * float32 partials in the library's static scratch array instead of a
+ * caller workspace. It calls no allocating routine; on a device's first call
+ * it looks the array's device address up once (hipGetSymbolAddress).
+ *   splits  1 (plain fp8lin_gemm_w8a8, no scratch), 2 or 4; K a multiple of
+ *           16 * splits (else FP8LIN_ELAYOUT)
+ * splits * M * N * 4 must not exceed FP8LIN_SCRATCH_BYTES (else
+ * FP8LIN_EUNSUPPORTED, nothing enqueued): e.g. M = 1024, N = 4096 with 2
+ * splits, or M = 512 with 4.
+ * Every call on one GPU uses that GPU's one scratch array: calls that
+ * overlap on a GPU (concurrent streams, several host threads) race and
+ * give wrong results; calls in stream order on one stream are safe. The
+ * partials are fully overwritten by every call, nothing needs clearing.
+ * Other arguments, rules and launch counts as fp8lin_gemm_w8a8_splitk.
+ */
+int32_t fp8lin_gemm_w8a8_splitk_noalloc(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N,
+                                        int64_t K, int64_t ldy, float input_scale, float weight_scale, int32_t splits,
+                                        hipStream_t stream);
+
 /*
  * fp8lin_gemm_w8a16 with K split into `splits` slices, for shapes with too
  * few output tiles to fill the device (e.g. M = 1024 tokens of a 4096 ->

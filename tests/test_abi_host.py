@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_entry_point(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(fp8lin.EXPORTS)
@@ -457,3 +457,23 @@ def test_gemm_w8a16_splitk_choice(lib):
     assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 512) == 1
     assert lib.fp8lin_gemm_w8a16_splitk_choice(128, 512, 512) == 1
     assert lib.fp8lin_gemm_w8a16_splitk_choice(0, 4096, 4096) == 1
+
+
+def skna(lib, qx=FAKE, qw=FAKE, y=FAKE, M=1024, N=4096, K=4096, ldy=4096, si=0.01, sw=0.001, splits=2):
+    return lib.fp8lin_gemm_w8a8_splitk_noalloc(qx, qw, y, M, N, K, ldy, si, sw, splits, None)
+
+
+def test_gemm_w8a8_splitk_noalloc_validation(lib):
+    """Everything is refused before the scratch array is looked up or anything is enqueued."""
+    assert skna(lib, splits=3) == fp8lin.EINVAL
+    assert skna(lib, qw=None) == fp8lin.EINVAL
+    assert skna(lib, K=4096 + 16, splits=2) == fp8lin.ELAYOUT  # K a multiple of 16 * splits
+    assert skna(lib, qx=FAKE + 4) == fp8lin.ELAYOUT
+    assert skna(lib, si=float("nan")) == fp8lin.ESCALE
+    # the float32 partials must fit the 32 MiB scratch array: 4 x 1024 x 4096 x 4 bytes is 64 MiB
+    assert fp8lin.SCRATCH_BYTES == 32 * 1024 * 1024
+    assert skna(lib, splits=4) == fp8lin.EUNSUPPORTED
+    assert skna(lib, M=1025, splits=2) == fp8lin.EUNSUPPORTED
+    before = [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)]
+    assert skna(lib, M=0, qx=None, y=None) == fp8lin.OK
+    assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A8, fp8lin.KERNEL_SPLITK_REDUCE)] == before

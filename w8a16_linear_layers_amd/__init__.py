@@ -36,6 +36,7 @@ __all__ = [
     "fp8lin_gemm_w8a8_group",
     "fp8lin_gemm_w8a8_splitk",
     "fp8lin_gemm_w8a8_splitk_choice",
+    "fp8lin_gemm_w8a8_splitk_noalloc",
     "fp8lin_gemm_w8a16_splitk",
     "fp8lin_gemm_w8a16_splitk_choice",
     "fp8lin_qkv_shared",
@@ -101,6 +102,7 @@ EXPORTS = (
     "fp8lin_gemm_w8a8_group",
     "fp8lin_gemm_w8a8_splitk",
     "fp8lin_gemm_w8a8_splitk_choice",
+    "fp8lin_gemm_w8a8_splitk_noalloc",
     "fp8lin_gemm_w8a16_splitk",
     "fp8lin_gemm_w8a16_splitk_choice",
     "fp8lin_qkv_shared",
@@ -179,6 +181,7 @@ def load_library():
     lib.fp8lin_gemm_w8a8_dev_scale.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, f32, vp]
     lib.fp8lin_gemm_w8a8_splitk.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32, vp, i64, vp]
     lib.fp8lin_gemm_w8a8_splitk_choice.argtypes = [i64, i64, i64]
+    lib.fp8lin_gemm_w8a8_splitk_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32, vp]
     lib.fp8lin_gemm_w8a16_splitk.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, f32, i32, vp, i64, vp]
     lib.fp8lin_gemm_w8a16_splitk_choice.argtypes = [i64, i64, i64]
     lib.fp8lin_qk_norm_rope.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, f32, vp]
@@ -307,6 +310,30 @@ def fp8lin_gemm_w8a8_splitk(qx, qw, input_scale, weight_scale, splits=None, out=
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)
         ),
         "fp8lin_gemm_w8a8_splitk",
+    )
+    return out
+
+
+SCRATCH_BYTES = 32 * 1024 * 1024  # FP8LIN_SCRATCH_BYTES: the library's static scratch array per GPU
+
+
+def fp8lin_gemm_w8a8_splitk_noalloc(qx, qw, input_scale, weight_scale, splits=None, out=None, ldy=None, stream=None):
+    """fp8lin_gemm_w8a8_splitk with the float32 partials in the library's static scratch array: the C call
+    allocates nothing (the output is allocated here only when `out` is not given). splits * M * N * 4 must fit
+    SCRATCH_BYTES; calls that overlap on one GPU race (one scratch array per GPU)."""
+    if qx.dtype != torch.uint8 or qw.dtype != torch.uint8:
+        raise TypeError("qx and qw must hold E4M3 codes as torch.uint8")
+    m, k = _rows(qx)
+    n = qw.shape[0]
+    if splits is None:
+        splits = fp8lin_gemm_w8a8_splitk_choice(m, n, k)
+    out, ldy = _gemm_out(qx.shape[:-1], n, qx.device, out, ldy)
+    _check(
+        load_library().fp8lin_gemm_w8a8_splitk_noalloc(
+            _ptr(qx), _ptr(qw), _ptr(out), m, n, k, ldy, float(input_scale), float(weight_scale), int(splits),
+            _stream(stream)
+        ),
+        "fp8lin_gemm_w8a8_splitk_noalloc",
     )
     return out
 

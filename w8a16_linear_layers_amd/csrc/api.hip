@@ -311,24 +311,33 @@ int32_t fp8lin_gemm_w8a8_splitk_choice(int64_t M, int64_t N, int64_t K) {
   return splits;
 }
 
-int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
-                                int64_t ldy, float input_scale, float weight_scale, int32_t splits, void* workspace,
-                                int64_t workspace_bytes, hipStream_t stream) {
-  if (splits != 1 && splits != 2 && splits != 4) return FP8LIN_EINVAL;
-  if (splits == 1)
-    return fp8lin_gemm_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, stream);
+}  // extern "C"
+
+namespace {
+
+// Checks of a split-K W8A8 call (splits 2 or 4) apart from its workspace.
+int32_t check_splitk_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                          float input_scale, float weight_scale, int32_t splits) {
   int32_t st = check_gemm_matrix(M, K);
   if (st != FP8LIN_OK) return st;
   if (K == 0 || (M > 0 && qx == nullptr)) return FP8LIN_EINVAL;
   if ((st = check_output(qw, y_bf16, N, ldy, M)) != FP8LIN_OK) return st;
-  if (!aligned16(qx) || !aligned16(workspace)) return FP8LIN_ELAYOUT;
+  if (!aligned16(qx)) return FP8LIN_ELAYOUT;
   if (K % (16 * splits) != 0) return FP8LIN_ELAYOUT;
   if (!scale_ok(input_scale) || !scale_ok(weight_scale)) return FP8LIN_ESCALE;
   const float alpha = input_scale * weight_scale;
   if (!std::isfinite(alpha) || alpha == 0.0f) return FP8LIN_ESCALE;
-  if (M == 0) return FP8LIN_OK;
   if (M * N >= kMaxElems) return FP8LIN_EUNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < (int64_t)splits * M * N * 4) return FP8LIN_EINVAL;
+  return FP8LIN_OK;
+}
+
+// The split-K W8A8 launches on a checked call with M > 0 and a workspace of
+// at least splits * M * N * 4 bytes.
+int32_t launch_splitk_w8a8(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                           float input_scale, float weight_scale, int32_t splits, void* workspace,
+                           hipStream_t stream) {
+  const float alpha = input_scale * weight_scale;
+  int32_t st;
   GemmArgs a{};
   a.x = qx;
   a.m = (int32_t)M;
@@ -350,6 +359,39 @@ int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, in
   if (e != hipSuccess) return FP8LIN_EHIP;
   return hip_status(
       fp8lin::launch_splitk_reduce(static_cast<const float*>(workspace), splits, y_bf16, M, N, ldy, alpha, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+                                int64_t ldy, float input_scale, float weight_scale, int32_t splits, void* workspace,
+                                int64_t workspace_bytes, hipStream_t stream) {
+  if (splits != 1 && splits != 2 && splits != 4) return FP8LIN_EINVAL;
+  if (splits == 1)
+    return fp8lin_gemm_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, stream);
+  int32_t st = check_splitk_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, splits);
+  if (st != FP8LIN_OK) return st;
+  if (!aligned16(workspace)) return FP8LIN_ELAYOUT;
+  if (M == 0) return FP8LIN_OK;
+  if (workspace == nullptr || workspace_bytes < (int64_t)splits * M * N * 4) return FP8LIN_EINVAL;
+  return launch_splitk_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, splits, workspace, stream);
+}
+
+int32_t fp8lin_gemm_w8a8_splitk_noalloc(const void* qx, const void* qw, void* y_bf16, int64_t M, int64_t N, int64_t K,
+                                        int64_t ldy, float input_scale, float weight_scale, int32_t splits,
+                                        hipStream_t stream) {
+  if (splits != 1 && splits != 2 && splits != 4) return FP8LIN_EINVAL;
+  if (splits == 1)
+    return fp8lin_gemm_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, stream);
+  int32_t st = check_splitk_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, splits);
+  if (st != FP8LIN_OK) return st;
+  if (M == 0) return FP8LIN_OK;
+  if ((int64_t)splits * M * N * 4 > FP8LIN_SCRATCH_BYTES) return FP8LIN_EUNSUPPORTED;
+  void* scratch = nullptr;
+  if (fp8lin::device_scratch(&scratch) != hipSuccess) return FP8LIN_EHIP;
+  return launch_splitk_w8a8(qx, qw, y_bf16, M, N, K, ldy, input_scale, weight_scale, splits, scratch, stream);
 }
 
 int32_t fp8lin_gemm_w8a16_splitk_choice(int64_t M, int64_t N, int64_t K) {

@@ -23,8 +23,11 @@
 //   * Tiles of all groups form one index space, remapped so that the
 //     workgroups dispatched to one XCD (ids congruent mod 8) take a
 //     contiguous run of tiles, rasterized in bands of 4 M-tiles for L2 reuse.
+#include <mutex>
 #include <type_traits>
 #include <utility>
+
+#include "fp8lin.h"
 
 #include "device.h"
 #include "internal.h"
@@ -1240,6 +1243,37 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
 }
 
 int device_cu_count() { return cu_count(); }
+
+// Scratch of the calls that allocate nothing (fp8lin_gemm_w8a8_splitk_noalloc:
+// the float32 split-K partials). Every GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not a device address: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+static __device__ __attribute__((used)) __align__(256) uint8_t scratch[FP8LIN_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t device_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm_w8a8_splitk(const GemmArgs& a, hipStream_t s) {
   static const int cus = cu_count();

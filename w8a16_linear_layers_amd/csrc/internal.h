@@ -67,6 +67,9 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_w8a8_splitk(const GemmArgs& a, hipStream_t s);
 // Compute units of the current device.
 int device_cu_count();
+// The current device's copy of the library's static scratch array
+// (FP8LIN_SCRATCH_BYTES bytes), looked up once per device and kept.
+hipError_t device_scratch(void** ptr);
 hipError_t launch_splitk_reduce(const float* partials, int splits, void* y, int64_t m, int64_t n, int64_t ldy,
                                 float alpha, hipStream_t s);
 // The same grouped launch with the QK RMSNorm + RoPE epilogue on groups 0, 1.
