@@ -155,15 +155,20 @@ __device__ __forceinline__ void wait_vmem_and_barrier() {
 // row64(P) for 64-byte rows). Rows 0-127 and 128-255 come from two buffer
 // resources (the two halves of one matrix, or two matrices such as the gate
 // and up weights), and chunk j lies in the upper half iff j >= kChunks / 2.
-// voff[j] is the chunk's byte offset inside its resource at K = 0; a stage's
+// off(j) is the chunk's byte offset inside its resource at K = 0; a stage's
 // K offset travels in the scalar offset. The swizzles depend only on row
 // bits below 5, which j does not change, so a thread copies the same
-// logical chunk of every row it serves (kbyte).
+// logical chunk of every row it serves (kbyte), and the rows of chunks j and
+// j' of one half differ by a wave-uniform multiple of 256 / kChunks rows.
 // kSwz16: 128-byte rows in the W8A8 layout (swz16 instead of swz8).
-template <int kChunks, bool kSwz16 = false>
+// kCompact: keep one offset register (off(0)) and form off(j) at issue time
+// from it and a scalar row step, instead of one register per chunk.
+template <int kChunks, bool kSwz16 = false, bool kCompact = false>
 struct CopyPlan {
+  static constexpr int kRowsPerChunk = kThreads / kChunks;  // rows between chunks j and j + 1
   i32x4 lo, hi;
-  uint32_t voff[kChunks];
+  uint32_t voff[kCompact ? 1 : kChunks];
+  uint32_t row_step;  // kRowsPerChunk rows in bytes (kCompact)
   int kbyte;  // first K byte of the thread's chunk within a stage row
 
   // Rows [0, 128) from src_lo (rows_lo of them valid), rows [128, 256) from
@@ -176,13 +181,28 @@ struct CopyPlan {
     const int n_hi = __builtin_amdgcn_readfirstlane(max(0, min(rows_hi, 128)));
     lo = make_rsrc(src_lo, (uint32_t)(n_lo * ld_bytes));
     hi = make_rsrc(src_hi, (uint32_t)(n_hi * ld_bytes));
+    row_step = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kRowsPerChunk * ld_bytes));
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
+    for (int j = 0; j < (kCompact ? 1 : kChunks); ++j) {
       const int p = j * kThreads + tid;
       const int r = kChunks == 4 ? row64(p / kChunks) : p / kChunks;
       const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : kSwz16 ? swz16(r) : swz8(r));
       voff[j] = (uint32_t)((r & 127) * ld_bytes) + (uint32_t)c * 16u;
       if (j == 0) kbyte = c * 16;
+    }
+  }
+
+  // Offset of chunk j (a compile-time constant in the unrolled callers). The
+  // compact form adds (j mod kChunks / 2) row steps to an opaque copy of
+  // off(0), so that the sums are formed where they are used rather than kept
+  // in registers across the stage loop.
+  __device__ __forceinline__ uint32_t off(int j) const {
+    if constexpr (kCompact) {
+      uint32_t v = voff[0], st = row_step;
+      asm volatile("" : "+v"(v), "+s"(st));
+      return v + (uint32_t)(j % (kChunks / 2)) * st;
+    } else {
+      return voff[j];
     }
   }
 
@@ -203,14 +223,15 @@ struct CopyPlan {
 
   // Chunk j of the full stage starting at byte `k0b` of each row.
   __device__ __forceinline__ void copy_one(const uint8_t* lds_tile, uint32_t k0b, int j, uint32_t wave_off) const {
-    dma(j, voff[j], k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+    dma(j, off(j), k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
   }
 
   // Chunk j of the stage starting at byte `k0b`, zero at or beyond byte `kb`
   // of a row (the K tail).
   __device__ __forceinline__ void copy_masked(const uint8_t* lds_tile, int k0b, int kb, int j,
                                               uint32_t wave_off) const {
-    dma(j, k0b + kbyte >= kb ? kOutOfRange : voff[j], (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+    const uint32_t o = off(j);  // formed first: the compact form's opaque copy cannot sit under the select
+    dma(j, k0b + kbyte >= kb ? kOutOfRange : o, (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
   }
 
   // All chunks of the stage starting at byte `k0b`; chunks at or beyond
@@ -218,8 +239,10 @@ struct CopyPlan {
   __device__ __forceinline__ void copy(const uint8_t* lds_tile, int k0b, int kb, uint32_t wave_off) const {
     const bool beyond = k0b + kbyte >= kb;
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j)
-      dma(j, beyond ? kOutOfRange : voff[j], (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+    for (int j = 0; j < kChunks; ++j) {
+      const uint32_t o = off(j);
+      dma(j, beyond ? kOutOfRange : o, (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+    }
   }
 
   // Every later copy reads zeros.
@@ -338,26 +361,56 @@ __device__ __forceinline__ void stage_rows_f32(const f32x4 (&acc)[8][8], int j, 
   }
 }
 
+// Buffer stores a thread issues per output tile, derived from the epilogue
+// loops below (the waits that skip a tile's stores count them):
+//   store_rows: 16 lanes per 256-byte staged row, so a 32-row pass is
+//     32 / (64 / 16) = 8 stores per lane; 4 passes per 128-row wave tile,
+//     twice for float32 output (two 64-column halves);
+//   epilogue_swiglu: 8 lanes per h row, 16 rows per wave and pass, so 2 rows
+//     per lane, each one 16-byte store of E4M3 codes or two of 16-bit values.
+constexpr int kEpiPassRows = 32;
+constexpr int kEpiPasses = 128 / kEpiPassRows;
+constexpr int kStoreRowsStores = kEpiPassRows / (64 / 16);
+constexpr int kSwiGLURowsPerLane = (kEpiPassRows / 2) / (64 / 8);
+template <bool kFp8Out>
+constexpr int kSwiGLUPassStores = kSwiGLURowsPerLane * (kFp8Out ? 1 : 2);
+// per tile: kind 0 = 16-bit rows, 1 = float32 rows, 2 = SwiGLU E4M3 h, 3 = SwiGLU 16-bit h
+constexpr int tile_stores(int kind) {
+  return kind == 0   ? kEpiPasses * kStoreRowsStores
+         : kind == 1 ? kEpiPasses * 2 * kStoreRowsStores
+         : kind == 2 ? kEpiPasses * kSwiGLUPassStores<true>
+                     : kEpiPasses * kSwiGLUPassStores<false>;
+}
+static_assert(tile_stores(0) == 32 && tile_stores(1) == 64 && tile_stores(2) == 8 && tile_stores(3) == 16,
+              "stores per tile");
+// The largest count an s_waitcnt vmcnt can encode. A wait that should skip
+// more younger operations than this waits for some of them too: correct,
+// only more conservative.
+constexpr int kMaxVmcnt = 63;
+constexpr int clamp_vmcnt(int n) { return n < kMaxVmcnt ? n : kMaxVmcnt; }
+
 // Store the staged rows [32 j, 32 j + 32) of kElem-byte elements, 16 bytes
 // per lane, the row's first column being n0. Columns at or beyond N get an
-// out-of-range offset, so every lane issues the same eight stores. The
-// staging writes come from the same wave, whose LDS operations complete in
-// order.
+// out-of-range offset, so every lane issues the same kStoreRowsStores
+// stores. The staging writes come from the same wave, whose LDS operations
+// complete in order.
 template <int kElem, int kPolicy>
 __device__ __forceinline__ void store_rows(const uint8_t* stage, int j, const GemmGroup& grp,
                                            __amdgpu_buffer_rsrc_t out, int n0, int lane) {
   const int c = lane & 15;
   const int n = n0 + c * (16 / kElem);
-  u32x4 v[8];
+  // the group's sizes, loaded once (scalar) rather than beside every store
+  const int gn = __builtin_amdgcn_readfirstlane(grp.n), gld = __builtin_amdgcn_readfirstlane(grp.ldy);
+  u32x4 v[kStoreRowsStores];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < kStoreRowsStores; ++q) {
     const int ml = q * 4 + (lane >> 4);
     v[q] = *reinterpret_cast<const u32x4*>(stage + ml * 256 + ((c ^ (ml & 15)) * 16));
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ml = 32 * j + q * 4 + (lane >> 4);
-    const uint32_t off = n < grp.n ? (uint32_t)(ml * grp.ldy + n) * (uint32_t)kElem : kOutOfRange;
+  for (int q = 0; q < kStoreRowsStores; ++q) {
+    const int ml = kEpiPassRows * j + q * 4 + (lane >> 4);
+    const uint32_t off = n < gn ? (uint32_t)(ml * gld + n) * (uint32_t)kElem : kOutOfRange;
     __builtin_amdgcn_raw_buffer_store_b128(v[q], out, (int)off, 0, kPolicy);
   }
 }
@@ -535,6 +588,166 @@ constexpr int kSlotFree = 12;   // barrier that frees this stage's buffer
 constexpr int kCopyStride = 3;  // slots between the copies of stage s + 2
 constexpr int kSlotMid = 32;    // barrier after which stage s + 1 is readable
 
+// A tile's last stage issues the next tile's stages 0 and 1, one copy per
+// slot from kSlotFree: stage 0's 16 copies, then stage 1's.
+constexpr int kLastCopy0 = kSlotFree;       // slot of the first copy of the next tile's stage 0
+constexpr int kLastCopy1 = kSlotFree + 16;  // ... of its stage 1
+constexpr int kLastCopyEnd = kSlotFree + 32;
+
+// ------------------------------------------------------------------ overlapped epilogue
+// Half of the plain bf16 epilogue runs under the matrix cores' work instead
+// of after it. A wave's 128 x 128 output block leaves in two parts of 64
+// columns:
+//   part A, acc[0..3][*] (weight blocks 0-3), is final once the first half
+//     of the tile's last stage has run (acc[i][b] takes its last MFMA at
+//     slot 4 b + i) and is written during that stage, from slot kEpiA0 on,
+//     while the second half multiplies into acc[4..7];
+//   part B, acc[4..7][*], is final only after the last MFMA and is written
+//     right after the stage, before the next tile starts.
+// Each part is 4 passes of 32 rows (pass j: m-blocks 2 j, 2 j + 1). A pass is
+// 8 units -- unit u scales acc[4 P + (u & 3)][2 j + (u >> 2)] by alpha,
+// rounds to bf16 and writes it to the wave's staging area (one ds_write_b64
+// per lane) -- then 4 reads of 8 staged rows (ds_read_b128) and 4 stores of
+// those rows (buffer_store_dwordx4, 8 lanes per 128-byte row segment).
+// Passes alternate between the two 4 KiB halves of the wave's 8 KiB area.
+// Within a slot the order is: MFMA, own fragment read, free barrier, copy,
+// epilogue unit, epilogue read, epilogue store.
+//
+// Measured on one box (16384 x 4096 x 4096, one launch): 2941 -> 2993 and
+// 2956 -> 3022 TFLOP/s against the whole epilogue after the stage; with no
+// epilogue at all (a diagnostic build) 3234-3283, i.e. the epilogue costs
+// about 4 us per tile. Interleaving a unit (4 accumulator reads, 4
+// multiplies, 2 packs, 1 LDS write) per slot already outlasts the 16 x 16 x
+// 128 MFMA beside it, so part A's cost is only partly hidden. Part B in the
+// first half of the next tile's stage 0 (whose MFMAs start from zero and
+// write only acc[0..3] there) ran out of registers beside stage 0's
+// fragments and spilled; stores straight from the accumulators (no staging)
+// were 15-30% slower overall; a software-pipelined part B measured the same.
+constexpr int kEpiHalf = 4096;  // bytes of one pass: 32 rows x 128 bytes
+static_assert(2 * kEpiHalf == kW8A8EpiWave, "two pass areas per wave");
+
+struct EpiSlot {
+  int unit, rd, st;  // -1, or pass * 8 + unit / pass * 4 + read / pass * 4 + store
+};
+struct EpiPlan {
+  EpiSlot op[64];
+  bool ok;
+};
+
+// Units of pass j at slots a0 + 8 j + u, its reads at a0 + 8 + 8 j + 2 k,
+// each store kStoreLag slots after its read.
+constexpr int kStoreLag = 3;
+constexpr EpiPlan make_epi_plan(int a0) {
+  EpiPlan p{};
+  p.ok = true;
+  for (int t = 0; t < 64; ++t) p.op[t] = EpiSlot{-1, -1, -1};
+  for (int j = 0; j < 4; ++j) {
+    for (int u = 0; u < 8; ++u) {
+      const int t = a0 + 8 * j + u;
+      if (t >= 64 || p.op[t].unit >= 0) p.ok = false;
+      else p.op[t].unit = 8 * j + u;
+    }
+    for (int k = 0; k < 4; ++k) {
+      const int tr = a0 + 8 + 8 * j + 2 * k, ts = tr + kStoreLag;
+      if (ts >= 64 || p.op[tr].rd >= 0 || p.op[ts].st >= 0) p.ok = false;
+      else {
+        p.op[tr].rd = 4 * j + k;
+        p.op[ts].st = 4 * j + k;
+      }
+    }
+  }
+  return p;
+}
+constexpr int epi_slot_of(const EpiPlan& p, int kind, int id) {  // kind 0 unit, 1 read, 2 store
+  for (int t = 0; t < 64; ++t)
+    if ((kind == 0 ? p.op[t].unit : kind == 1 ? p.op[t].rd : p.op[t].st) == id) return t;
+  return -1;
+}
+constexpr int epi_stores_from(const EpiPlan& p, int t0) {  // stores at slots >= t0
+  int n = 0;
+  for (int t = t0; t < 64; ++t) n += p.op[t].st >= 0;
+  return n;
+}
+constexpr int kEpiA0 = 8;
+constexpr EpiPlan kEpiA = make_epi_plan(kEpiA0);
+constexpr int kMfmaLatencySlots = 4;  // slots between an accumulator's last MFMA and its first read
+constexpr bool epi_plan_ok(const EpiPlan& q) {
+  if (!q.ok) return false;
+  for (int j = 0; j < 4; ++j) {
+    for (int u = 0; u < 8; ++u)  // acc[u & 3][2 j + (u >> 2)] takes its last MFMA at slot 4 b + i
+      if (epi_slot_of(q, 0, 8 * j + u) < 4 * (2 * j + (u >> 2)) + (u & 3) + kMfmaLatencySlots) return false;
+    for (int k = 0; k < 4; ++k) {
+      const int tr = epi_slot_of(q, 1, 4 * j + k), ts = epi_slot_of(q, 2, 4 * j + k);
+      for (int u = 0; u < 8; ++u)  // a pass's reads follow all of its units
+        if (tr <= epi_slot_of(q, 0, 8 * j + u)) return false;
+      if (ts <= tr) return false;
+      // the next pass's read k reuses the same registers: after this store
+      if (j < 3 && epi_slot_of(q, 1, 4 * (j + 1) + k) <= ts) return false;
+      // pass j + 2 writes the same area: after all of pass j's reads
+      if (j < 2 && epi_slot_of(q, 0, 8 * (j + 2)) <= tr) return false;
+    }
+  }
+  return true;
+}
+static_assert(epi_plan_ok(kEpiA), "the overlapped epilogue's windows, order and staging reuse");
+
+// Where a wave's output rows go, and how they are scaled.
+struct EpiCtx {
+  uint8_t* area;               // the wave's 8 KiB staging area
+  __amdgpu_buffer_rsrc_t out;  // rows m_base .. m_base + 128 of the group's output
+  float alpha;
+  int col0;                    // first output column of the wave's 128-column block
+  int gn, gld;                 // the group's N and ldy
+};
+
+// Unit u of pass j of part P: bf16(acc[4 P + (u & 3)][2 j + (u >> 2)] * alpha)
+// into staged row m = 16 (u >> 2) + r of the pass, 16-byte chunk
+// c = 2 (u & 3) + q / 2 at physical chunk c ^ (m % 8).
+template <int P>
+__device__ __forceinline__ void epi_unit(const f32x4 (&acc)[8][8], int j, int u, const EpiCtx& e, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  const int m = 16 * (u >> 2) + r;
+  const int c = 2 * (u & 3) + (q >> 1);
+  const f32x4 x = acc[4 * P + (u & 3)][2 * j + (u >> 2)];
+  u32x2 v;
+  v[0] = bf16x2(x[0] * e.alpha, x[1] * e.alpha);
+  v[1] = bf16x2(x[2] * e.alpha, x[3] * e.alpha);
+  *reinterpret_cast<u32x2*>(e.area + (j & 1) * kEpiHalf + m * 128 + ((c ^ (m & 7)) * 16) + (q & 1) * 8) = v;
+}
+
+// Read k of pass j: staged rows 8 k .. 8 k + 7, lane l holding chunk l % 8 of
+// row 8 k + l / 8.
+__device__ __forceinline__ u32x4 epi_read(int j, int k, const EpiCtx& e, int lane) {
+  const int row = 8 * k + (lane >> 3), c = lane & 7;
+  return *reinterpret_cast<const u32x4*>(e.area + (j & 1) * kEpiHalf + row * 128 + ((c ^ (row & 7)) * 16));
+}
+
+// Store k of pass j of part P: those 16 bytes to row 32 j + 8 k + l / 8 of the
+// wave's block, columns col0 + 64 P + 8 (l % 8) ..; columns at or past N get
+// an out-of-range offset, rows past M fall outside the resource.
+template <int P>
+__device__ __forceinline__ void epi_store(const u32x4& v, int j, int k, const EpiCtx& e, int lane) {
+  const int row = 32 * j + 8 * k + (lane >> 3);
+  const int col = e.col0 + 64 * P + 8 * (lane & 7);
+  const uint32_t off = col < e.gn ? (uint32_t)(row * e.gld + col) * 2u : kOutOfRange;
+  __builtin_amdgcn_raw_buffer_store_b128(v, e.out, (int)off, 0, kStreamStore);
+}
+
+// Part P on its own (no matrix-core work to hide behind).
+template <int P>
+__device__ __forceinline__ void epi_part_alone(const f32x4 (&acc)[8][8], const EpiCtx& e, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) epi_unit<P>(acc, j, u, e, lane);
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = epi_read(j, k, e, lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) epi_store<P>(v[k], j, k, e, lane);
+  }
+}
+
 // What one stage needs besides the fragments and accumulators.
 struct StageCtx {
   const CopyPlan<8, true>& pw;
@@ -546,6 +759,8 @@ struct StageCtx {
   const int (&ow)[2];
   const int (&ox)[2];
   uint32_t wave_off;
+  const EpiCtx& epi;  // kEpi: whose rows the epilogue part writes
+  int lane;
 };
 
 // The memory operation after MFMA t of a steady stage (at most one each).
@@ -556,6 +771,7 @@ struct SlotOp {
 struct SlotPlan {
   SlotOp op[64];
   int copies_before_mid;  // copies of stage s + 2 issued before the mid-stage barrier
+  int last_copy;          // slot of the last copy of stage s + 2
   bool ok;
 };
 
@@ -582,6 +798,7 @@ constexpr SlotPlan make_slot_plan(int kFree, int kStride, int kMid) {
     }
     p.op[want] = SlotOp{kSlotCopy, u, 0};
     if (want < kMid) ++p.copies_before_mid;
+    p.last_copy = want;
     t = want + 1;
   }
   auto place = [&](int kind, int blk, int e, int earliest) {
@@ -603,15 +820,40 @@ constexpr SlotPlan make_slot_plan(int kFree, int kStride, int kMid) {
 constexpr SlotPlan kSlotPlan = make_slot_plan(kSlotFree, kCopyStride, kSlotMid);
 static_assert(kSlotPlan.ok, "the W8A8 stage's memory operations must fit its 64 slots");
 
-// MFMA t of the stage and the memory operation that follows it. kExtraVm:
+// VMEM operations (copies and stores) between a stage's copies and the wait
+// for them, with the overlapped epilogue (part B's kPartStores stores follow
+// the last stage):
+//   a tile's start waits for stage 0, whose last copy is the last stage's
+//   slot kLastCopy1 - 1: younger are stage 1's 16 copies (KT > 1), part A's
+//   stores from that slot on (a store follows the copy of its slot) and
+//   part B's;
+//   stage 0's mid-stage wait is for stage 1, whose last copy is the last
+//   stage's slot kLastCopyEnd - 1: younger are part A's stores from that
+//   slot on, part B's and stage 0's own copies before the wait.
+constexpr int kPartStores = 16;  // per part: 4 passes x 4 stores
+constexpr int kEpiStoresAfterStage0 = epi_stores_from(kEpiA, kLastCopy1 - 1) + kPartStores;
+constexpr int kEpiStoresAfterStage1 = epi_stores_from(kEpiA, kLastCopyEnd - 1) + kPartStores;
+static_assert(epi_stores_from(kEpiA, 0) == kPartStores, "part A's stores");
+static_assert(16 + kEpiStoresAfterStage0 <= kMaxVmcnt &&
+                  kEpiStoresAfterStage1 + kSlotPlan.copies_before_mid <= kMaxVmcnt,
+              "vmcnt range");
+
+// kEpi: the stage carries part A of the overlapped epilogue (a tile's last stage).
+constexpr bool kEpiNone = false, kEpiPartA = true;
+
+// MFMA t of the stage and the memory operations that follow it. kExtraVm:
 // VMEM operations issued after stage s + 1's copies besides this stage's
-// (the previous tile's output stores, in a tile's stage 0).
-template <int t, int kCopy, int kExtraVm, bool kLast>
-__device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8], const StageCtx& c) {
+// own copies and epilogue stores (the previous tile's output stores, in a
+// tile's stage 0). kFirst: the tile's stage 0, whose MFMAs start from zero.
+template <int t, int kCopy, int kExtraVm, bool kLast, bool kFirst, bool kEpi>
+__device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8], u32x4 (&eb)[4],
+                                          const StageCtx& c) {
   constexpr int kFree = kSlotFree, kMid = kSlotMid;
   constexpr SlotOp op = kSlotPlan.op[t];
   constexpr int i = (t < 32 ? 0 : 4) + (t & 3), b = (t & 31) >> 2;
-  acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf[b], acc[i][b], 0, 0, 0, 0, 0, 0);
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf[b], kFirst ? zero : acc[i][b], 0, 0, 0, 0,
+                                                               0, 0);
   if constexpr (op.kind == kSlotOwn) {
     constexpr int r = op.a;
     if constexpr (r < 2)
@@ -622,8 +864,8 @@ __device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i 
   if constexpr (t == kFree) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // this stage's buffer is free
   if constexpr (kLast) {
     // no stage s + 1: the next tile's stages 0 and 1, one copy per slot
-    if constexpr (t >= kFree && t < kFree + 32) {
-      constexpr int u = t - kFree, st = u >> 4, j = u & 7;
+    if constexpr (t >= kLastCopy0 && t < kLastCopyEnd) {
+      constexpr int u = t - kLastCopy0, st = u >> 4, j = u & 7;
       if (c.has_next && (st == 0 || c.KT > 1)) {
         if constexpr ((u & 15) < 8)
           c.pw.copy_masked(lds8_w(st), st * 128, c.K, j, c.wave_off);
@@ -648,28 +890,36 @@ __device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i 
     }
     if constexpr (t == kMid) {
       constexpr int kVm = (kCopy != 0 ? kSlotPlan.copies_before_mid : 0) + kExtraVm;
-      static_assert(kVm < 64, "vmcnt range");
+      static_assert(kVm <= kMaxVmcnt, "vmcnt range");
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVm) : "memory");
     }
     if constexpr (op.kind == kSlotW) set_half(wf[op.a], op.e, frag16_half(lds8_w(c.nxt), c.ow[op.e], op.a));
     if constexpr (op.kind == kSlotX) set_half(xf[op.a], op.e, frag16_half(lds8_x(c.nxt), c.ox[op.e], op.a));
   }
+  if constexpr (kEpi) {
+    constexpr EpiSlot eo = kEpiA.op[t];
+    if constexpr (eo.unit >= 0) epi_unit<0>(acc, eo.unit >> 3, eo.unit & 7, c.epi, c.lane);
+    if constexpr (eo.rd >= 0) eb[eo.rd & 3] = epi_read(eo.rd >> 2, eo.rd & 3, c.epi, c.lane);
+    if constexpr (eo.st >= 0) epi_store<0>(eb[eo.st & 3], eo.st >> 2, eo.st & 3, c.epi, c.lane);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int kCopy, int kExtraVm, bool kLast, int... ts>
+template <int kCopy, int kExtraVm, bool kLast, bool kFirst, bool kEpi, int... ts>
 __device__ __forceinline__ void w8a8_slots(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8], const StageCtx& c,
                                            std::integer_sequence<int, ts...>) {
-  (w8a8_slot<ts, kCopy, kExtraVm, kLast>(acc, wf, xf, c), ...);
+  u32x4 eb[4];  // epilogue reads in flight to their stores
+  (w8a8_slot<ts, kCopy, kExtraVm, kLast, kFirst, kEpi>(acc, wf, xf, eb, c), ...);
 }
 
-template <int kCopy, int kExtraVm, bool kLast>
+template <int kCopy, int kExtraVm, bool kLast, bool kFirst = false, bool kEpi = kEpiNone>
 __device__ __forceinline__ void w8a8_stage(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8],
                                            const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int s, int K,
                                            int KT, bool has_next, const int (&ow)[2], const int (&ox)[2],
-                                           uint32_t wave_off) {
-  const StageCtx c{pw, px, s & 1, (s & 1) ^ 1, (uint32_t)(s + 2) * 128u, K, KT, has_next, ow, ox, wave_off};
-  w8a8_slots<kCopy, kExtraVm, kLast>(acc, wf, xf, c, std::make_integer_sequence<int, 64>{});
+                                           uint32_t wave_off, const EpiCtx& epi, int lane) {
+  const StageCtx c{pw, px, s & 1, (s & 1) ^ 1, (uint32_t)(s + 2) * 128u, K, KT, has_next, ow, ox, wave_off, epi,
+                   lane};
+  w8a8_slots<kCopy, kExtraVm, kLast, kFirst, kEpi>(acc, wf, xf, c, std::make_integer_sequence<int, 64>{});
 }
 
 // Issue the copies of stages 0 and 1 of a tile into buffers 0 and 1.
@@ -707,7 +957,7 @@ __device__ __forceinline__ void epilogue_swiglu(const Acc& acc, int j, uint8_t* 
   const int col = n_base + 16 * cp;
   constexpr int kBytes = kFp8Out ? 1 : 2;  // per h element
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kSwiGLURowsPerLane; ++q) {
     const int r = 16 * wn + 8 * q + (lane >> 3);  // row within the pass
     u32x4 gv[2], uv[2];
 #pragma unroll
@@ -801,10 +1051,17 @@ gemm_w8a8_kernel(const GemmArgs a) {
     px.init(static_cast<const uint8_t*>(a.x) + (kSplit ? a.g[t.group].koff : 0), t.m0, a.m - t.m0, LD, tid);
   };
   constexpr int kTN = kSwiGLU ? kTileN / 2 : kTileN;
-  // buffer stores per thread of one tile's epilogue: 8 per 32-row block, 16
-  // for float32 partials, or 2 for the fused SwiGLU's E4M3 h; a vmcnt wait
-  // encodes at most 63 (a larger count waits for some stores too)
-  constexpr int kStores = kSwiGLU ? 8 : (kSplit ? 47 : 32);
+  // The previous tile's epilogue stores are younger than this tile's stage 0
+  // and 1 copies; the waits below skip them, as many as a wait can encode
+  // beside the kStageCopies copies of stage 1.
+  constexpr int kStageCopies = 2 * 8;  // pw and px, 8 chunks each
+  constexpr int kStores = clamp_vmcnt(tile_stores(kSwiGLU ? 2 : kSplit ? 1 : 0) + kStageCopies) - kStageCopies;
+  static_assert(kStores > 0 && kStageCopies + kStores <= kMaxVmcnt, "vmcnt range");
+
+  // The plain bf16 output leaves through the overlapped epilogue; the fused
+  // forms (SwiGLU, QK norm, split-K partials) keep a separate epilogue after
+  // the tile's last stage.
+  constexpr bool kOverlap = !kSwiGLU && !kNormRope && !kSplit;
 
   int slot = blockIdx.x;
   TileCoord tc = tile_at<kTN>(a, slot);
@@ -812,6 +1069,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
   w8a8_first_stages(pw, px, K, KT, wave_off);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  f32x4 acc[8][8];
   for (;;) {
     const TileCoord cur = tc;
     const GemmGroup& grp = a.g[cur.group];
@@ -819,42 +1077,57 @@ gemm_w8a8_kernel(const GemmArgs a) {
     const bool has_next = next < a.total_tiles;
     // stage 0 has landed for every wave: after the first tile, only stage
     // 1's copies (when KT > 1) and the previous tile's stores are younger
+    constexpr int kTileStores = kOverlap ? kEpiStoresAfterStage0 : kStores;
     if (KT > 1)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(16 + kStores) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStageCopies + kTileStores) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStores) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kTileStores) : "memory");
     // stage 0's fragments but xf[7] and wf[4..7], which the stage reads itself
     v8i wf[8], xf[8];
 #pragma unroll
     for (int f = 0; f < 4; ++f) read_frag16(wf[f], lds8_w(0), ow, f);
 #pragma unroll
     for (int f = 0; f < 7; ++f) read_frag16(xf[f], lds8_x(0), ox, f);
-    f32x4 acc[8][8];
+    if constexpr (!kOverlap) {
+      // the fused epilogues' register allocation comes out better with
+      // accumulators cleared at the tile start than with stage 0 from zero
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[i][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int b = 0; b < 8; ++b) acc[i][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    EpiCtx ctx{};
+    if constexpr (kOverlap) {
+      ctx.area = epi;
+      ctx.out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
+      ctx.alpha = grp.alpha * alpha_mul;
+      ctx.col0 = cur.n0 + wn * 128;
+      ctx.gn = __builtin_amdgcn_readfirstlane(grp.n);
+      ctx.gld = __builtin_amdgcn_readfirstlane(grp.ldy);
+    }
 
     // Stage kinds: s <= KT - 4 copies stage s + 2 (never the last, so no K
     // tail); s = KT - 3 copies the last stage with its tail masked; s = KT - 2
-    // copies nothing; s = KT - 1 is the last. The mid-stage wait of stage 0
-    // also skips the previous tile's stores.
+    // copies nothing; s = KT - 1 is the last. Stage 0's mid-stage wait also
+    // skips the previous tile's stores; with the overlapped epilogue stage 0
+    // starts from zero accumulators instead of cleared ones.
+    constexpr int kExtra0 = kOverlap ? kEpiStoresAfterStage1 : kStores;
     int s = 0;
     if (KT >= 2) {
       if (KT >= 4)
-        w8a8_stage<1, kStores, false>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off);
+        w8a8_stage<1, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off, ctx, lane);
       else if (KT == 3)
-        w8a8_stage<2, kStores, false>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off);
+        w8a8_stage<2, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off, ctx, lane);
       else
-        w8a8_stage<0, kStores, false>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off);
+        w8a8_stage<0, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off, ctx, lane);
       for (s = 1; s + 3 < KT; ++s)
-        w8a8_stage<1, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+        w8a8_stage<1, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
       if (s == KT - 3) {
-        w8a8_stage<2, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+        w8a8_stage<2, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
         ++s;
       }
       if (s == KT - 2) {
-        w8a8_stage<0, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+        w8a8_stage<0, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
         ++s;
       }
     }
@@ -863,7 +1136,12 @@ gemm_w8a8_kernel(const GemmArgs a) {
       tc = tile_at<kTN>(a, next);
       plan_tile(tc);
     }
-    w8a8_stage<0, 0, true>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off);
+    constexpr bool kEpiLast = kOverlap;  // part A of the overlapped epilogue
+    if (kOverlap && KT == 1)
+      w8a8_stage<0, 0, true, kOverlap, kEpiLast>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx,
+                                                 lane);
+    else
+      w8a8_stage<0, 0, true, false, kEpiLast>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
 
     if constexpr (kSwiGLU) {
       const int I = grp.n;
@@ -872,27 +1150,23 @@ gemm_w8a8_kernel(const GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         epilogue_swiglu<true>(acc, j, lds_mem + kW8A8EpiOffset, wm, wn, alpha, a.out_rs, out, cur.n0, I, lane);
-    } else {
+    } else if constexpr (kSplit) {
+      const __amdgpu_buffer_rsrc_t out4 = out_rsrc<4>(grp, a.m, cur.m0 + wm * 128);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          epilogue_rows_f32<kSplitPartialStore>(acc, j, hf, epi, grp, 1.0f, out4, cur.n0 + wn * 128, lane);
+    } else if constexpr (kNormRope) {
       const __amdgpu_buffer_rsrc_t out = out_rsrc(grp, a.m, cur.m0 + wm * 128);
-      if constexpr (kSplit) {
-        const __amdgpu_buffer_rsrc_t out4 = out_rsrc<4>(grp, a.m, cur.m0 + wm * 128);
+      const bool active = cur.group < 2;
+      const uint16_t* nw = cur.group == 0 ? a.nr_w[0] : a.nr_w[1];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            epilogue_rows_f32<kSplitPartialStore>(acc, j, hf, epi, grp, 1.0f, out4, cur.n0 + wn * 128, lane);
-      } else if constexpr (kNormRope) {
-        const bool active = cur.group < 2;
-        const uint16_t* nw = cur.group == 0 ? a.nr_w[0] : a.nr_w[1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          epilogue_rows_norm_rope(acc, j, epi, grp, grp.alpha, out, cur.n0 + wn * 128, lane, cur.m0 + wm * 128, a.m,
-                                  active, nw, a.nr_cos, a.nr_sin, a.nr_eps);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          epilogue_rows(acc, j, epi, grp, grp.alpha * alpha_mul, out, cur.n0 + wn * 128, lane);
-      }
+      for (int j = 0; j < 4; ++j)
+        epilogue_rows_norm_rope(acc, j, epi, grp, grp.alpha, out, cur.n0 + wn * 128, lane, cur.m0 + wm * 128, a.m,
+                                active, nw, a.nr_cos, a.nr_sin, a.nr_eps);
+    } else {
+      epi_part_alone<1>(acc, ctx, lane);  // part A went out during the last stage
     }
     if (!has_next) break;
     slot = next;
@@ -947,11 +1221,10 @@ __device__ __forceinline__ f32x4 w16_mfma(W16Op<kForm> w, u32x4 x, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, __builtin_bit_cast(v8bf, x), acc, 0, 0, 0);
 }
 
-constexpr int kW16Copies = 12;  // copies per thread per stage
-// Buffer stores per thread per tile: per 32-row block 8 (16-bit output),
-// 16 (float32) or 4 (the fused SwiGLU's 16-bit h).
+constexpr int kW16Copies = 4 + 8;  // copies per thread per stage: 4 weight and 8 activation chunks
+// Buffer stores per thread per tile of the epilogue forms.
 template <bool kSwiGLU, int kForm, bool kSplit = false>
-constexpr int kW16EpilogueStores = kSwiGLU ? 16 : (kForm == kFormF32 || kSplit ? 64 : 32);
+constexpr int kW16EpilogueStores = tile_stores(kSwiGLU ? 3 : (kForm == kFormF32 || kSplit) ? 1 : 0);
 
 // Persistent W8A16 pipeline: K stages of 64 elements; one workgroup per CU
 // walks the tiles of dispatch slots blockIdx.x, blockIdx.x + gridDim.x, ...
@@ -969,8 +1242,10 @@ constexpr int kW16EpilogueStores = kSwiGLU ? 16 : (kForm == kFormF32 || kSplit ?
 // a.k), so its copies start koff elements into the weight and activation rows.
 template <bool kSwiGLU, int kForm, bool kSplit = false>
 struct W16Copier {
-  CopyPlan<4> pw;  // E4M3 weight, 64-byte stage rows
-  CopyPlan<8> px;  // bf16 activation, 128-byte stage rows
+  // The plain forms keep one weight-copy offset register (the fused SwiGLU
+  // form, whose epilogue needs more registers, allocates better with four).
+  CopyPlan<4, false, !kSwiGLU> pw;  // E4M3 weight, 64-byte stage rows
+  CopyPlan<8> px;                   // bf16 activation, 128-byte stage rows
   int tile_slot;   // dispatch slot of the tile being copied
   int k;           // next stage of that tile
 
@@ -995,11 +1270,12 @@ struct W16Copier {
   __device__ __forceinline__ void issue(int c, int buf, int K, int XK, uint32_t wave_off) const {
     if (c < 4) {
       const int k0b = (kForm == kFormF32 ? k / 3 : k) * 64;
-      pw.dma(c, k0b + pw.kbyte >= K ? kOutOfRange : pw.voff[c], (uint32_t)k0b,
+      const uint32_t o = pw.off(c);
+      pw.dma(c, k0b + pw.kbyte >= K ? kOutOfRange : o, (uint32_t)k0b,
             lds_addr(lds16_w(buf)) + c * kThreads * 16 + wave_off);
     } else {
       const int k0b = k * 128;
-      px.dma(c - 4, k0b + px.kbyte >= 2 * XK ? kOutOfRange : px.voff[c - 4], (uint32_t)k0b,
+      px.dma(c - 4, k0b + px.kbyte >= 2 * XK ? kOutOfRange : px.off(c - 4), (uint32_t)k0b,
             lds_addr(lds16_x(buf)) + (c - 4) * kThreads * 16 + wave_off);
     }
   }
@@ -1014,13 +1290,6 @@ struct W16Copier {
         pw.exhaust();
         px.exhaust();
       }
-      // Use the copy offsets here: if the register allocator reloads them
-      // from scratch on this (once per tile) path, the load is waited for
-      // here rather than at their uses inside the stage loop.
-#pragma unroll
-      for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(pw.voff[j]));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(px.voff[j]));
     }
   }
 };
@@ -1067,29 +1336,115 @@ __device__ __forceinline__ void w16_read(W16Half& f, int r, const uint8_t* lds_w
 // Half stage on set f: 64 MFMAs, weight-block-major (MFMA t: weight block
 // t / 8, activation block t % 8); weight block i + 1 is dequantized four
 // MFMAs before its first use. Each MFMA is followed by at most one memory
-// operation:
+// operation, placed by the slot plan below:
 //   first half : the 16 reads of the second half's fragments (set nf) at
 //                odd slots 1-31, and copies 0-5 of stage g + 2 five slots
 //                apart from slot 34. Their buffer held stage g - 1, which
 //                every wave finished reading before the previous stage's
 //                barrier (lgkmcnt(0) precedes it).
 //   second half: after MFMA 3, vmcnt + lgkmcnt(0) + barrier: stage g + 1 has
-//                landed for every wave (only the 6 copies of the first half,
-//                and after a tile change the previous tile's output stores,
-//                are younger than its copies); then the 16 reads of the next
+//                landed for every wave (only the first half's copies, and
+//                after a tile change the previous tile's output stores, are
+//                younger than its copies); then the 16 reads of the next
 //                stage's first-half fragments at even slots 4-34, and copies
 //                6-11 five slots apart from slot 37.
-// vmcnt encodes at most 63: a larger count waits for some of the younger
-// stores too, which is still correct.
-template <bool kSwiGLU, int kForm, bool kSplit = false>
-constexpr int kW16AfterStoresWait = kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm, kSplit> < 63
-                                        ? kW16Copies / 2 + kW16EpilogueStores<kSwiGLU, kForm, kSplit>
-                                        : 63;
+enum W16SlotKind : int { kW16None, kW16Read, kW16Copy };
+struct W16Slot {
+  int kind, a;  // read: fragment block a (0-15); copy: chunk a (0-11)
+};
+struct W16Plan {
+  W16Slot op[2][64];       // [half][MFMA]
+  int wait_slot;           // second half: stage g + 1 is waited for after this MFMA
+  int copies_before_wait;  // copies of stage g + 2 issued before that wait
+  bool ok;
+};
 
-template <bool kSwiGLU, int kForm, bool kSplit, class Copier>
+constexpr W16Plan make_w16_plan() {
+  W16Plan p{};
+  p.ok = true;
+  p.wait_slot = 3;
+  auto put = [&](int h, int t, int kind, int a) {
+    if (t < 0 || t >= 64 || p.op[h][t].kind != kW16None) p.ok = false;
+    else p.op[h][t] = W16Slot{kind, a};
+  };
+  for (int r = 0; r < 16; ++r) put(0, 1 + 2 * r, kW16Read, r);
+  for (int c = 0; c < kW16Copies / 2; ++c) put(0, 34 + 5 * c, kW16Copy, c);
+  for (int r = 0; r < 16; ++r) put(1, 4 + 2 * r, kW16Read, r);
+  for (int c = 0; c < kW16Copies / 2; ++c) put(1, 37 + 5 * c, kW16Copy, kW16Copies / 2 + c);
+  // every chunk copied exactly once per stage, every fragment block read once per half
+  int copies = 0, reads[2] = {0, 0};
+  for (int h = 0; h < 2; ++h)
+    for (int t = 0; t < 64; ++t) {
+      if (p.op[h][t].kind == kW16Copy) {
+        if (p.op[h][t].a != copies) p.ok = false;  // chunks in order
+        ++copies;
+        if (h == 0 || t <= p.wait_slot) ++p.copies_before_wait;
+      }
+      if (p.op[h][t].kind == kW16Read) {
+        if (p.op[h][t].a != reads[h]) p.ok = false;
+        ++reads[h];
+        // the second half reads stage g + 1: only after its wait and barrier
+        if (h == 1 && t <= p.wait_slot) p.ok = false;
+      }
+    }
+  if (copies != kW16Copies || reads[0] != 16 || reads[1] != 16) p.ok = false;
+  return p;
+}
+
+constexpr W16Plan kW16Plan = make_w16_plan();
+static_assert(kW16Plan.ok, "the W8A16 half stages' memory operations must fit their slots");
+// vmcnt of the wait for stage g + 1: the copies issued after its last copy
+constexpr int kW16StageWait = kW16Plan.copies_before_wait;
+static_assert(kW16StageWait == kW16Copies / 2 && kW16StageWait <= kMaxVmcnt, "vmcnt of the stage wait");
+// ... and in a tile's first stage, where the previous tile's epilogue stores
+// are younger too (clamped: a larger count would wait for some stores too)
+template <bool kSwiGLU, int kForm, bool kSplit = false>
+constexpr int kW16AfterStoresWait = clamp_vmcnt(kW16StageWait + kW16EpilogueStores<kSwiGLU, kForm, kSplit>);
+static_assert(kW16AfterStoresWait<false, kFormBf16> == 38 && kW16AfterStoresWait<true, kFormBf16> == 22 &&
+                  kW16AfterStoresWait<false, kFormF32> == kMaxVmcnt,
+              "after-stores waits");
+
+// MFMA t of a half stage and the memory operation that follows it.
+template <int t, bool kSecond, bool kReadNext, bool kSwiGLU, int kForm, bool kSplit, class Copier>
+__device__ __forceinline__ void w16_slot(f32x4 (&acc)[8][8], const W16Half& f, W16Half& nf, W16Op<kForm>& wcur,
+                                         W16Op<kForm>& wnext, const uint8_t* nw, const uint8_t* nx, int nh,
+                                         const W16Addr& ad, Copier& cp, int cbuf, int K, int XK, uint32_t wave_off,
+                                         bool after_stores) {
+  constexpr int i = t >> 3, b = t & 7;
+  constexpr W16Slot op = kW16Plan.op[kSecond ? 1 : 0][t];
+  if constexpr (b == 4 && i < 7) wnext = dequant8<kForm>(f.w[i + 1][0], f.w[i + 1][1]);
+  acc[i][b] = w16_mfma<kForm>(wcur, f.x[b], acc[i][b]);
+  if constexpr (b == 7) wcur = wnext;
+  if constexpr (kSecond && t == kW16Plan.wait_slot) {
+    if (after_stores)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16AfterStoresWait<kSwiGLU, kForm, kSplit>) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16StageWait) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  if constexpr (op.kind == kW16Read && (!kSecond || kReadNext)) w16_read(nf, op.a, nw, nx, nh, ad);
+  if constexpr (op.kind == kW16Copy) cp.issue(op.a, cbuf, K, XK, wave_off);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool kSecond, bool kReadNext, bool kSwiGLU, int kForm, bool kSplit, class Copier, int... ts>
+__device__ __forceinline__ void w16_slots(f32x4 (&acc)[8][8], const W16Half& f, W16Half& nf, W16Op<kForm>& wcur,
+                                          W16Op<kForm>& wnext, const uint8_t* nw, const uint8_t* nx, int nh,
+                                          const W16Addr& ad, Copier& cp, int cbuf, int K, int XK, uint32_t wave_off,
+                                          bool after_stores, std::integer_sequence<int, ts...>) {
+  (w16_slot<ts, kSecond, kReadNext, kSwiGLU, kForm, kSplit>(acc, f, nf, wcur, wnext, nw, nx, nh, ad, cp, cbuf, K, XK,
+                                                            wave_off, after_stores),
+   ...);
+}
+
+// A half stage on set f, reading into nf from buffer nb (half nh of it).
+// kSecond: the stage's second half (waits for stage g + 1, reads its first
+// half unless kReadNext is false); after_stores: the tile's first stage
+// after an epilogue (the wait skips that tile's stores).
+template <bool kSecond, bool kReadNext, bool kSwiGLU, int kForm, bool kSplit, class Copier>
 __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W16Half& nf, int nb, int nh,
                                          const W16Addr& ad, Copier& cp, int cbuf, int K, int XK, uint32_t wave_off,
-                                         bool second, bool after_stores) {
+                                         bool after_stores) {
   // the next set's buffer base, kept opaque so that per-block addresses are
   // not precomputed for every buffer
   uint32_t bw = lds_addr(lds16_w(nb)), bx = lds_addr(lds16_x(nb));
@@ -1097,30 +1452,22 @@ __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W
   const uint8_t* nw = lds_mem + (bw - lds_addr(lds_mem));
   const uint8_t* nx = lds_mem + (bx - lds_addr(lds_mem));
   W16Op<kForm> wcur = dequant8<kForm>(f.w[0][0], f.w[0][1]), wnext;
-#pragma unroll
-  for (int t = 0; t < 64; ++t) {
-    const int i = t >> 3, b = t & 7;
-    if (b == 4 && i < 7) wnext = dequant8<kForm>(f.w[i + 1][0], f.w[i + 1][1]);
-    acc[i][b] = w16_mfma<kForm>(wcur, f.x[b], acc[i][b]);
-    if (b == 7) wcur = wnext;
-    if (!second) {
-      if ((t & 1) && t < 32) w16_read(nf, t >> 1, nw, nx, nh, ad);
-      if (t >= 34 && (t - 34) % 5 == 0 && t <= 59) cp.issue((t - 34) / 5, cbuf, K, XK, wave_off);
-    } else {
-      if (t == 3) {
-        if (after_stores)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16AfterStoresWait<kSwiGLU, kForm, kSplit>) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW16Copies / 2) : "memory");
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
-      if (t >= 4 && t <= 34 && (t & 1) == 0) w16_read(nf, (t - 4) >> 1, nw, nx, nh, ad);
-      if (t >= 37 && (t - 37) % 5 == 0 && t <= 62) cp.issue(6 + (t - 37) / 5, cbuf, K, XK, wave_off);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  w16_slots<kSecond, kReadNext, kSwiGLU, kForm, kSplit>(acc, f, nf, wcur, wnext, nw, nx, nh, ad, cp, cbuf, K, XK,
+                                                        wave_off, after_stores, std::make_integer_sequence<int, 64>{});
 }
 
+// One stage: its first half on set fa (reading the second half's fragments
+// into fb), its second half on fb (reading the next stage's first half into
+// fa unless kReadNext is false). after_stores: the tile's first stage after
+// another tile's epilogue.
+template <bool kReadNext, bool kSwiGLU, int kForm, bool kSplit, class Copier>
+__device__ __forceinline__ void w16_stage(f32x4 (&acc)[8][8], W16Half& fa, W16Half& fb, int b, const W16Addr& ad,
+                                          Copier& cp, int K, int XK, uint32_t wave_off, bool after_stores) {
+  const int nb = b == 2 ? 0 : b + 1;  // next stage's buffer
+  const int cb = b == 0 ? 2 : b - 1;  // buffer of stage + 2
+  w16_half<false, true, kSwiGLU, kForm, kSplit>(acc, fa, fb, b, 1, ad, cp, cb, K, XK, wave_off, false);
+  w16_half<true, kReadNext, kSwiGLU, kForm, kSplit>(acc, fb, fa, nb, 0, ad, cp, cb, K, XK, wave_off, after_stores);
+}
 
 // kSwiGLU: the fused gate/up + SwiGLU form with a 16-bit h (the 16-bit
 // step's split MLP), tiles and weight rows as in the fused W8A8 kernel;
@@ -1156,25 +1503,45 @@ gemm_w8a16_kernel(const GemmArgs a) {
   wait_vmem_and_barrier<kW16Copies>();  // stage 0 has landed
 
   W16Half fa, fb;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) w16_read(fa, r, lds16_w(0), lds16_x(0), 0, ad);
   int b = 0;  // buffer of the current stage
+  if constexpr (kSwiGLU) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w16_read(fa, r, lds16_w(0), lds16_x(0), 0, ad);
+  }
 
   for (int tile_slot = blockIdx.x; tile_slot < a.total_tiles; tile_slot += (int)gridDim.x) {
     const bool first = tile_slot == (int)blockIdx.x;
+    // The plain forms read the tile's first half-stage fragments here, not
+    // during the previous tile's last stage, so that they are not live across
+    // the epilogue (which spilled them). Stage 0 has landed for every wave:
+    // before the first tile by the wait above, for later tiles by the wait in
+    // the previous tile's last stage, and every wave has passed the barrier
+    // that ends the epilogue. The fused SwiGLU form, whose register
+    // allocation comes out better the other way, reads them in the last
+    // stage of the previous tile.
+    if constexpr (!kSwiGLU) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w16_read(fa, r, lds16_w(b), lds16_x(b), 0, ad);
+    }
     f32x4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int s = 0; s < KT; ++s) {
-      const int nb = b == 2 ? 0 : b + 1;      // next stage's buffer
-      const int cb = b == 0 ? 2 : b - 1;      // buffer of stage + 2
-      w16_half<kSwiGLU, kForm, kSplit>(acc, fa, fb, b, 1, ad, cp, cb, K, XK, wave_off, false, false);
-      w16_half<kSwiGLU, kForm, kSplit>(acc, fb, fa, nb, 0, ad, cp, cb, K, XK, wave_off, true, s == 0 && !first);
+    // Stage s: its first half on set fa (reading the second half's
+    // fragments into fb), its second half on fb (reading the next stage's
+    // first half into fa, except in a plain form's last stage).
+    const int full_stages = kSwiGLU ? KT : KT - 1;
+    for (int s = 0; s < full_stages; ++s) {
+      w16_stage<true, kSwiGLU, kForm, kSplit>(acc, fa, fb, b, ad, cp, K, XK, wave_off, s == 0 && !first);
       cp.advance(a, KT, tid);
-      b = nb;
+      b = b == 2 ? 0 : b + 1;
+    }
+    if constexpr (!kSwiGLU) {
+      w16_stage<false, kSwiGLU, kForm, kSplit>(acc, fa, fb, b, ad, cp, K, XK, wave_off, KT == 1 && !first);
+      cp.advance(a, KT, tid);
+      b = b == 2 ? 0 : b + 1;
     }
 
     // Epilogue: rows staged in the activation tile of the last stage's
