@@ -540,31 +540,32 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
     }
     del x4, qg4, qu4, qx4, g4, u4, h4, h4f, h16s, h16f, c4
 
-    # 4096 -> 4096 projection at 1024 and 8192 rows
+    # 4096 -> 4096 projection at 1024, 2048 and 8192 rows. Where 256 x 256 tiles would keep at most 60% of
+    # the CUs busy the library runs 128 x 128 tiles; at 1024 rows the split-K calls on 256 x 256 tiles are
+    # timed beside them for comparison.
     c2 = config2()
     x2 = c2.x.to(dev)
     qw2 = fp8lin.fp8lin_quantize_static(c2.w.to(dev), c2.weight_scale)
     q2 = fp8lin.fp8lin_quantize_static(x2, c2.input_scale)
-    for m in (1024, 8192):
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for m in (1024, 2048, 8192):
         y2 = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
         f = 2.0 * m * N * K
         a = timed(lambda: fp8lin.fp8lin_gemm_w8a8(q2[:m], qw2, c2.input_scale, c2.weight_scale, out=y2), reps)
         b = timed(lambda: fp8lin.fp8lin_gemm_w8a16(x2[:m], qw2, c2.weight_scale, out=y2), reps)
-        row = {"w8a8_tflops": round(f / a / 1e9, 1), "w8a16_tflops": round(f / b / 1e9, 1)}
-        sk = fp8lin.fp8lin_gemm_w8a8_splitk_choice(m, K, K)
-        if sk > 1:  # too few output tiles to fill the device: K split into float32 partials
-            ws_sk = torch.empty(sk * m * K * 4, dtype=torch.uint8, device=dev)
+        big_tiles = ((m + 255) // 256) * (N // 256)
+        row = {"tiles": "128x128" if 5 * big_tiles <= 3 * cus else "256x256",
+               "w8a8_tflops": round(f / a / 1e9, 1), "w8a8_pct_fp8_peak": round(100 * f / a / 1e9 / PEAK_FP8_TFLOPS, 2),
+               "w8a16_tflops": round(f / b / 1e9, 1),
+               "w8a16_pct_bf16_peak": round(100 * f / b / 1e9 / PEAK_BF16_TFLOPS, 2)}
+        if m == 1024:
+            ws_sk = torch.empty(4 * m * K * 4, dtype=torch.uint8, device=dev)
             c = timed(lambda: fp8lin.fp8lin_gemm_w8a8_splitk(q2[:m], qw2, c2.input_scale, c2.weight_scale,
-                                                             splits=sk, out=y2, workspace=ws_sk), reps)
-            row["w8a8_splitk"] = {"splits": sk, "tflops": round(f / c / 1e9, 1)}
-        sk16 = fp8lin.fp8lin_gemm_w8a16_splitk_choice(m, K, K)
-        if sk16 > 1:
-            ws16 = torch.empty(4 * m * K * 4, dtype=torch.uint8, device=dev)
-            row["w8a16_splitk"] = {"splits": sk16}
-            for sp in (2, 4):
-                c = timed(lambda: fp8lin.fp8lin_gemm_w8a16_splitk(x2[:m], qw2, c2.weight_scale, splits=sp, out=y2,
-                                                                  workspace=ws16), reps)
-                row["w8a16_splitk"]["tflops_%d_splits" % sp] = round(f / c / 1e9, 1)
+                                                             splits=2, out=y2, workspace=ws_sk), reps)
+            d = timed(lambda: fp8lin.fp8lin_gemm_w8a16_splitk(x2[:m], qw2, c2.weight_scale, splits=4, out=y2,
+                                                              workspace=ws_sk), reps)
+            row["splitk_256x256"] = {"w8a8_2_splits_tflops": round(f / c / 1e9, 1),
+                                     "w8a16_4_splits_tflops": round(f / d / 1e9, 1)}
         rows["proj_%dx4096x4096" % m] = row
 
     # step policy: host call per transformer forward

@@ -209,11 +209,12 @@ int32_t fp8lin_gemm_w8a8_splitk(const void* qx, const void* qw, void* y_bf16, in
                                 int64_t workspace_bytes, hipStream_t stream);
 
 /* The split count fp8lin_gemm_w8a8_splitk does best with on the current
- * device: doubled from 1 (up to 4) while the tiles of all slices still fill
- * at most half the compute units and every slice keeps at least 512 K bytes
- * (the reduction re-reads splits * M * N * 4 bytes, so more, shorter slices
- * lose: at 1024 x 4096 x 4096 this gives 2).
- * Host only (it reads the device's compute-unit count once). */
+ * device: 1. A split of the 256 x 256 kernel helps only where its tiles fill
+ * at most half the compute units, and there the unsplit call runs on
+ * 128 x 128 tiles (when 256 x 256 ones would keep at most 60% of the compute
+ * units busy), which beats every split (1024 x 4096 x 4096: 1.75-1.79 against
+ * 0.96-1.02 PFLOP/s with 2 slices). Kept so that callers need not change;
+ * explicit split counts stay available. Host only. */
 int32_t fp8lin_gemm_w8a8_splitk_choice(int64_t M, int64_t N, int64_t K);
 
 /* Size of the library's static device scratch array (32 MiB), which each GPU
@@ -269,10 +270,9 @@ int32_t fp8lin_gemm_w8a16_splitk(const void* x, int32_t x_dtype, const void* qw,
                                  int64_t workspace_bytes, hipStream_t stream);
 
 /* The split count fp8lin_gemm_w8a16_splitk does best with on the current
- * device: doubled from 1 (up to 4) while the tiles of all slices still fit
- * the compute units and every slice keeps at least 512 K elements (at
- * 1024 x 4096 x 4096 this gives 4). Host only (it reads the device's
- * compute-unit count once). */
+ * device: 1, for the reason given at fp8lin_gemm_w8a8_splitk_choice
+ * (1024 x 4096 x 4096: 1.0 PFLOP/s unsplit on 128 x 128 tiles against
+ * 0.68-0.72 with 4 slices). Host only. */
 int32_t fp8lin_gemm_w8a16_splitk_choice(int64_t M, int64_t N, int64_t K);
 
 /*

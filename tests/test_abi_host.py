@@ -448,15 +448,13 @@ def test_gemm_w8a16_splitk_validation(lib):
     assert [fp8lin.fp8lin_launch_count(k) for k in (fp8lin.KERNEL_GEMM_W8A16, fp8lin.KERNEL_SPLITK_REDUCE)] == before
 
 
-def test_gemm_w8a16_splitk_choice(lib):
-    """Without a GPU the compute-unit count falls back to 256 (MI355X)."""
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(16384, 4096, 4096) == 1  # 1024 tiles fill the device
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(8192, 4096, 4096) == 1
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 4096) == 4  # 64 tiles x 4 slices of 1024
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 1024) == 2  # two slices of 512; four would be 256
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(1024, 4096, 512) == 1
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(128, 512, 512) == 1
-    assert lib.fp8lin_gemm_w8a16_splitk_choice(0, 4096, 4096) == 1
+def test_gemm_splitk_choice_is_one(lib):
+    """No split beats the unsplit call: where 256 x 256 tiles would leave the device underfilled it runs
+    128 x 128 tiles."""
+    for choice in (lib.fp8lin_gemm_w8a8_splitk_choice, lib.fp8lin_gemm_w8a16_splitk_choice):
+        for m, n, k in ((16384, 4096, 4096), (8192, 4096, 4096), (1024, 4096, 4096), (1024, 4096, 1024),
+                        (128, 512, 512), (0, 4096, 4096)):
+            assert choice(m, n, k) == 1
 
 
 def skna(lib, qx=FAKE, qw=FAKE, y=FAKE, M=1024, N=4096, K=4096, ldy=4096, si=0.01, sw=0.001, splits=2):

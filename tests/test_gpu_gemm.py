@@ -36,7 +36,10 @@ def both_weights(w, s_w, gpu):
      # more tiles than compute units at 1 and 2 K stages: workgroups change tiles inside the last stage
      (4100, 4104, 128), (2100, 8200, 256),
      # the down projection's K = 16384 (128 stages), and with a K tail
-     (300, 264, 16384), (513, 136, 16384 + 16)],
+     (300, 264, 16384), (513, 136, 16384 + 16),
+     # 128 x 128 tiles (256 x 256 tiles would keep at most 60% of the CUs busy): 5 and 6 stages (the
+     # stage loop runs in pairs), ragged M and N
+     (77, 520, 640), (130, 136, 768)],
 )
 def test_w8a8_random_codes(gpu, m, n, k):
     announce("w8a8 random codes m=%d n=%d k=%d" % (m, n, k))
@@ -50,7 +53,9 @@ def test_w8a8_random_codes(gpu, m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(1, 8, 16), (33, 40, 80), (300, 520, 1040), (257, 264, 4096 + 16), (65, 136, 64),
                                    (129, 264, 128), (40, 256, 192), (4100, 4104, 64), (2100, 8200, 128),
-                                   (300, 264, 16384), (129, 520, 16384 + 16)])
+                                   (300, 264, 16384), (129, 520, 16384 + 16),
+                                   # 128 x 128 tiles: 4 and 5 stages of 64 K values
+                                   (77, 520, 256), (130, 136, 320)])
 def test_w8a16_random_codes(gpu, m, n, k):
     announce("w8a16 random codes m=%d n=%d k=%d" % (m, n, k))
     x = normal_bf16((m, k), 0.35, 3000 + m)
@@ -119,6 +124,51 @@ def test_headline_shape_sampled(gpu):
     assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(xr, qw_ref, case.weight_scales[0]), "w8a16")
 
 
+@pytest.mark.parametrize(
+    "m,n,k",
+    # 256 x 256 tiles (enough of them to fill the device), ragged M and N, 1-4 stages and a K tail
+    [(4100, 4104, 4096 + 16), (3100, 3080, 384), (3100, 3080, 512)],
+)
+def test_big_tiles_ragged_sampled(gpu, m, n, k):
+    """The 256 x 256 kernels on shapes with ragged edges and every K-stage kind, on sampled rows (the last
+    M-tile's rows included)."""
+    announce("big tiles m=%d n=%d k=%d" % (m, n, k))
+    q = random_e4m3_codes((m, k), 5000 + m)
+    qw = random_e4m3_codes((n, k), 6000 + n)
+    x = normal_bf16((m, k), 0.35, 7000 + m)
+    y8 = fp8lin.fp8lin_gemm_w8a8(q.to(gpu), qw.to(gpu), 1.7e-3, 3.1e-5)
+    y16 = fp8lin.fp8lin_gemm_w8a16(x.to(gpu), qw.to(gpu), 2.3e-4)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(m, 48, m), np.arange(m - 8, m)]))
+    assert_gemm_close(f32(y8)[rows], linear.gemm_w8a8(q.numpy()[rows], qw.numpy(), 1.7e-3, 3.1e-5), "w8a8")
+    assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(f32(x)[rows], qw.numpy(), 2.3e-4), "w8a16")
+
+
+@pytest.mark.parametrize("m", [1024, 2048])
+def test_small_tiles_full_rows_sampled(gpu, m):
+    """128 x 128 tiles at the small-batch sizes: one tile per CU (1024 rows), several per CU (2048), and the
+    shared-QKV group at 1024 rows (three projections in one launch), on sampled rows."""
+    announce("small tiles m=%d" % m)
+    case = config2(8192)
+    x = case.x[:m].contiguous()
+    qw_gpu, qw_ref = both_weights(case.w, case.weight_scale, gpu)
+    xg = x.to(gpu)
+    q = fp8lin.fp8lin_quantize_static(xg, case.input_scale)
+    y8 = fp8lin.fp8lin_gemm_w8a8(q, qw_gpu, case.input_scale, case.weight_scale)
+    y16 = fp8lin.fp8lin_gemm_w8a16(xg, qw_gpu, case.weight_scale)
+    outs, _ = fp8lin.fp8lin_qkv_shared(xg, [qw_gpu] * 3, [case.weight_scale] * 3, [case.input_scale] * 3,
+                                       fp8lin.MODE_W8A8)
+    torch.cuda.synchronize()
+    rows = sample_rows(m, 96, m + 1)
+    xr = f32(x[rows])
+    qr = linear.quantize_static(xr, case.input_scale)
+    ref8 = linear.gemm_w8a8(qr, qw_ref, case.input_scale, case.weight_scale)
+    assert_gemm_close(f32(y8)[rows], ref8, "w8a8")
+    assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(xr, qw_ref, case.weight_scale), "w8a16")
+    for o in outs:
+        assert torch.equal(o, y8)  # the same projection three times in one grouped launch
+
+
 def test_w8a16_identity_weight_is_exact(gpu):
     announce("w8a16 identity weight")
     k = 512
@@ -176,13 +226,14 @@ def test_w8a16_refuses_fp8_activation(gpu):
     assert e.value.status == fp8lin.EDTYPE
 
 
-@pytest.mark.parametrize("kind", ["w8a8", "w8a16", "gate_up_w8a8", "gate_up_w8a16"])
+@pytest.mark.parametrize("kind", ["w8a8", "w8a16", "gate_up_w8a8", "gate_up_w8a16", "w8a8_small", "w8a16_small"])
 def test_repeated_launches_are_bit_identical(gpu, kind):
     """Several tiles per workgroup (persistent kernels): every launch gives the same bits. A wave that
     reuses LDS another wave still reads (tile changes, staging areas) would show up as run-to-run
-    differences."""
+    differences. The small kinds run 2048 rows: 128 x 128 tiles, two per workgroup."""
     announce("repeatability %s" % kind)
-    m, k, n = 8192, 4096, 4096
+    m, k, n = (2048 if kind.endswith("small") else 8192), 4096, 4096
+    kind = kind.replace("_small", "")
     x = normal_bf16((m, k), 0.35, 61).to(gpu)
     qw = random_e4m3_codes((n, k), 62).to(gpu)
     qw2 = random_e4m3_codes((n, k), 63).to(gpu)
@@ -269,7 +320,8 @@ def test_gemm_w8a16_splitk(gpu, m, n, k, splits):
 
 
 def test_gemm_splitk_choice():
-    """More slices only while the split grid fills at most half the device and slices keep >= 512 K bytes."""
-    assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(16384, 4096, 4096) == 1
-    assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(1024, 4096, 4096) == 2
-    assert fp8lin.fp8lin_gemm_w8a8_splitk_choice(128, 512, 512) == 1
+    """No split where the unsplit call runs on 128 x 128 tiles (which beat the splits) or fills the device."""
+    for choice in (fp8lin.fp8lin_gemm_w8a8_splitk_choice, fp8lin.fp8lin_gemm_w8a16_splitk_choice):
+        assert choice(16384, 4096, 4096) == 1
+        assert choice(1024, 4096, 4096) == 1
+        assert choice(128, 512, 512) == 1

@@ -299,16 +299,13 @@ int32_t fp8lin_gemm_w8a8_group(const void* qx, int64_t M, int64_t K, int32_t npr
 }
 
 int32_t fp8lin_gemm_w8a8_splitk_choice(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 1;
-  const int64_t tiles = ((M + fp8lin::kTileM - 1) / fp8lin::kTileM) * ((N + fp8lin::kTileN - 1) / fp8lin::kTileN);
-  const int64_t cus = fp8lin::device_cu_count();
-  int32_t splits = 1;
-  // Double while the split grid still fills at most half the device and each slice keeps >= 512 K
-  // bytes: the reduction re-reads splits * M * N * 4 bytes, so a full device of short slices loses
-  // (1024 x 4096 x 4096: 2 splits ~1.1x the unsplit launch, 4 splits slower than unsplit).
-  while (splits < 4 && tiles * splits * 2 <= cus / 2 && K % (16 * 2 * splits) == 0 && K / (2 * splits) >= 512)
-    splits *= 2;
-  return splits;
+  // A split helped only where the 256 x 256 tiles fill at most half the device (1024 x 4096 x 4096 with
+  // 2 slices: 0.96-1.02 PFLOP/s against 0.86-0.94 unsplit). There the unsplit call now runs 128 x 128
+  // tiles instead (1.75-1.79 PFLOP/s), which beat every split; elsewhere no split helps.
+  (void)M;
+  (void)N;
+  (void)K;
+  return 1;
 }
 
 }  // extern "C"
@@ -395,16 +392,12 @@ int32_t fp8lin_gemm_w8a8_splitk_noalloc(const void* qx, const void* qw, void* y_
 }
 
 int32_t fp8lin_gemm_w8a16_splitk_choice(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 1;
-  const int64_t tiles = ((M + fp8lin::kTileM - 1) / fp8lin::kTileM) * ((N + fp8lin::kTileN - 1) / fp8lin::kTileN);
-  const int64_t cus = fp8lin::device_cu_count();
-  int32_t splits = 1;
-  // Double while the split grid still fits the device and each slice keeps >= 512 K elements. The
-  // 16-bit product takes twice the matrix-core time of the FP8 one for the same partials, so the
-  // reduction weighs less than in the W8A8 rule (1024 x 4096 x 4096: 2 splits 1.44x, 4 splits 1.72x).
-  while (splits < 4 && tiles * splits * 2 <= cus && K % (16 * 2 * splits) == 0 && K / (2 * splits) >= 512)
-    splits *= 2;
-  return splits;
+  // As for W8A8: where slices helped (1024 x 4096 x 4096: 0.68-0.72 PFLOP/s with 4 slices against 0.40
+  // unsplit) the unsplit call now runs 128 x 128 tiles (1.0 PFLOP/s).
+  (void)M;
+  (void)N;
+  (void)K;
+  return 1;
 }
 
 int32_t fp8lin_gemm_w8a16_splitk(const void* x, int32_t x_dtype, const void* qw, void* y_bf16, int64_t M, int64_t N,

@@ -266,8 +266,8 @@ struct TileCoord {
 
 // Logical tile of dispatch slot `slot`: slot b runs on XCD b % 8, and each
 // XCD gets a contiguous run of tiles, rasterized in bands of kBandM M-tiles.
-// Tiles are 256 rows of M by kTN columns of N.
-template <int kTN = kTileN>
+// Tiles are kTM rows of M by kTN columns of N.
+template <int kTN = kTileN, int kTM = kTileM>
 __device__ __forceinline__ TileCoord tile_at(const GemmArgs& a, int slot) {
   const int T = a.total_tiles;
   const int xcd = slot % kXcds, idx = slot / kXcds;
@@ -287,7 +287,7 @@ __device__ __forceinline__ TileCoord tile_at(const GemmArgs& a, int slot) {
   // the arithmetic above is uniform; say so, so that the values stay scalar
   TileCoord c;
   c.group = __builtin_amdgcn_readfirstlane(gi);
-  c.m0 = __builtin_amdgcn_readfirstlane((first_m + in_band % band_m) * kTileM);
+  c.m0 = __builtin_amdgcn_readfirstlane((first_m + in_band % band_m) * kTM);
   c.n0 = __builtin_amdgcn_readfirstlane((in_band / band_m) * kTN);
   return c;
 }
@@ -1588,6 +1588,303 @@ gemm_w8a16_kernel(const GemmArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ------------------------------------------------------------------ small tiles
+// Shapes whose 256 x 256 tiles cannot fill the device (M = 1024 rows of a
+// 4096 -> 4096 projection: 64 tiles for 256 compute units) run on 128 x 128
+// tiles instead: 4 waves of 64 x 64 (4 x 4 blocks of 16 x 16, the same MFMA
+// forms, fragment layouts and LDS swizzles as the 256 x 256 kernels). K runs
+// in stages held in kSmallBufs LDS buffers; the copies of stage s + 4 are
+// issued during stage s, into the buffer stage s used, and every stage's
+// fragments are read into registers during the previous stage (two
+// register sets, so the stage loop is unrolled by two). One barrier per
+// stage: after it, every wave's copies of stage s + 1 have landed and every
+// wave has read stage s's buffer (lgkmcnt(0) precedes it). Copies of stages
+// past K read zeros, so every stage issues the same copies and the waits
+// count them uniformly.
+constexpr int kSmallTile = 128;
+constexpr int kSmallBufs = 4;
+constexpr int kSmall8Half = kSmallTile * 128;             // one operand of a W8A8 stage: 128 rows x 128 bytes
+constexpr int kSmall8Stage = 2 * kSmall8Half;             // weight, then activation
+constexpr int kSmall16W = kSmallTile * 64;                // W8A16: E4M3 weight, 128 rows x 64 bytes
+constexpr int kSmall16Stage = kSmall16W + kSmallTile * 128;  // then the 16-bit activation, 128 x 64 values
+constexpr int kSmallEpiOffset = kSmallBufs * kSmall8Stage;   // 8 KiB of staging per wave after the buffers
+constexpr int kSmallEpiWave = 64 * 128;                      // 64 output rows of 128 bytes
+static_assert(kSmallEpiOffset + 4 * kSmallEpiWave <= kLdsBytes, "small-tile LDS");
+static_assert(kSmallBufs * kSmall16Stage <= kSmallEpiOffset, "small-tile W8A16 buffers");
+constexpr int kSmall8Copies = 2 * (kSmallTile * 8 / kThreads);   // per thread per stage: 4 + 4
+constexpr int kSmall16Copies = kSmallTile * 4 / kThreads + kSmallTile * 8 / kThreads;  // 2 + 4
+// The wait before stage s's MFMAs is for stage s + 1; younger are the copies
+// of stages s + 2 .. s + kSmallBufs - 1.
+constexpr int kSmall8Wait = (kSmallBufs - 2) * kSmall8Copies;
+constexpr int kSmall16Wait = (kSmallBufs - 2) * kSmall16Copies;
+static_assert(kSmall8Wait <= kMaxVmcnt && kSmall16Wait <= kMaxVmcnt && (kSmallBufs - 1) * kSmall8Copies <= kMaxVmcnt,
+              "vmcnt range");
+
+__device__ __forceinline__ uint8_t* small8_w(int s) { return lds_mem + (s % kSmallBufs) * kSmall8Stage; }
+__device__ __forceinline__ uint8_t* small8_x(int s) { return small8_w(s) + kSmall8Half; }
+__device__ __forceinline__ uint8_t* small16_w(int s) { return lds_mem + (s % kSmallBufs) * kSmall16Stage; }
+__device__ __forceinline__ uint8_t* small16_x(int s) { return small16_w(s) + kSmall16W; }
+
+// Epilogue of a small tile: the wave's 64 x 64 block, bf16(acc * alpha)
+// (binary16 with kF16), staged in the wave's 8 KiB area (row m at m * 128,
+// 16-byte chunk c at c ^ (m % 8)), then 8 stores of 8 rows x 128 bytes.
+template <bool kF16>
+__device__ __forceinline__ void small_epilogue(const f32x4 (&acc)[4][4], uint8_t* area, float alpha,
+                                               __amdgpu_buffer_rsrc_t out, int col0, int gn, int gld, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int q = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * b + r, c = 2 * i + (q >> 1);
+      const f32x4 x = acc[i][b];
+      u32x2 v;
+      v[0] = h16x2<kF16>(x[0] * alpha, x[1] * alpha);
+      v[1] = h16x2<kF16>(x[2] * alpha, x[3] * alpha);
+      *reinterpret_cast<u32x2*>(area + m * 128 + ((c ^ (m & 7)) * 16) + (q & 1) * 8) = v;
+    }
+  const int c = lane & 7, col = col0 + 8 * c;
+  u32x4 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = 8 * k + (lane >> 3);
+    v[k] = *reinterpret_cast<const u32x4*>(area + row * 128 + ((c ^ (row & 7)) * 16));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = 8 * k + (lane >> 3);
+    const uint32_t off = col < gn ? (uint32_t)(row * gld + col) * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(v[k], out, (int)off, 0, kStreamStore);
+  }
+}
+
+// W8A8 small-tile stage s: 16 MFMAs on set f (acc[i][b] += w[i] x[b], MFMA t
+// = (t % 4, t / 4)); after the wait and barrier (MFMA kSmallBarrier) the 16
+// reads of stage s + 1 into nf (r < 8: weight block r / 2 half r % 2, else
+// activation block (r - 8) / 2) and the 8 copies of stage s + kSmallBufs
+// (u < 4 weight chunk, else activation chunk) into the buffer of stage s,
+// spread over the remaining slots.
+struct Small8Frags {
+  v8i w[4], x[4];
+};
+// The wait and barrier come after MFMA kSmallBarrier: the stage's own
+// fragments are already in registers, so the first MFMAs hide the barrier.
+constexpr int kSmallBarrier = 3;
+template <bool kFirst>
+__device__ __forceinline__ void small8_stage(f32x4 (&acc)[4][4], const Small8Frags& f, Small8Frags& nf, int s,
+                                             const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int K,
+                                             const int (&ow)[2], const int (&ox)[2], uint32_t wave_off) {
+  const uint8_t* nw = small8_w(s + 1);
+  const uint8_t* nx = small8_x(s + 1);
+  const int kc = (s + kSmallBufs) * 128;  // K byte of the stage being copied
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int i = t & 3, b = t >> 2;
+    acc[i][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.w[i], f.x[b], kFirst ? zero : acc[i][b], 0, 0, 0,
+                                                                 0, 0, 0);
+    if (t == kSmallBarrier)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kSmall8Wait) : "memory");
+    // reads r = 0..15 of stage s + 1 in slots kSmallBarrier + 1 .. 15 (two in the last ones)
+    if (t > kSmallBarrier) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r * (15 - kSmallBarrier) / 16 + kSmallBarrier + 1 == t) {
+          if (r < 8)
+            set_half(nf.w[r >> 1], r & 1, frag16_half(nw, ow[r & 1], r >> 1));
+          else
+            set_half(nf.x[(r - 8) >> 1], r & 1, frag16_half(nx, ox[r & 1], (r - 8) >> 1));
+        }
+    }
+    // copies u = 0..7 of stage s + kSmallBufs at slots kSmallBarrier + 1 + 1.5 u
+    if (t > kSmallBarrier) {
+#pragma unroll
+      for (int u = 0; u < kSmall8Copies; ++u)
+        if ((3 * u) / 2 + kSmallBarrier + 1 == t) {
+          if (u < 4)
+            pw.copy_masked(small8_w(s), kc, K, u, wave_off);
+          else
+            px.copy_masked(small8_x(s), kc, K, u - 4, wave_off);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Persistent W8A8 small-tile kernel over 128 x 128 tiles of all groups.
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
+gemm_w8a8_small_kernel(const GemmArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = a.k;
+  const int KT = (K + 127) / 128;
+  const uint32_t wave_off = (uint32_t)wave * 64 * 16;
+  const int ow[2] = {frag16_offset(wn * 64 + (lane & 15), lane >> 4, 0),
+                     frag16_offset(wn * 64 + (lane & 15), lane >> 4, 1)};
+  const int ox[2] = {frag16_offset(wm * 64 + (lane & 15), lane >> 4, 0),
+                     frag16_offset(wm * 64 + (lane & 15), lane >> 4, 1)};
+  uint8_t* area = lds_mem + kSmallEpiOffset + wave * kSmallEpiWave;
+  const float alpha_mul = a.in_scale_dev != nullptr ? *a.in_scale_dev : 1.0f;
+
+  for (int slot = blockIdx.x; slot < a.total_tiles; slot += (int)gridDim.x) {
+    const TileCoord tc = tile_at<kSmallTile, kSmallTile>(a, slot);
+    const GemmGroup& grp = a.g[tc.group];
+    CopyPlan<8, true> pw, px;
+    {
+      const uint8_t* w = grp.w + (int64_t)tc.n0 * K;
+      const uint8_t* x = static_cast<const uint8_t*>(a.x) + (int64_t)tc.m0 * K;
+      pw.init2(w, grp.n - tc.n0, w, 0, K, tid);
+      px.init2(x, a.m - tc.m0, x, 0, K, tid);
+    }
+    // stages 0 .. kSmallBufs - 1
+#pragma unroll
+    for (int st = 0; st < kSmallBufs; ++st) {
+#pragma unroll
+      for (int u = 0; u < kSmall8Copies / 2; ++u) pw.copy_masked(small8_w(st), st * 128, K, u, wave_off);
+#pragma unroll
+      for (int u = 0; u < kSmall8Copies / 2; ++u) px.copy_masked(small8_x(st), st * 128, K, u, wave_off);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kSmallBufs - 1) * kSmall8Copies) : "memory");
+    Small8Frags fa, fb;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      read_frag16(fa.w[f], small8_w(0), ow, f);
+      read_frag16(fa.x[f], small8_x(0), ox, f);
+    }
+    f32x4 acc[4][4];
+    small8_stage<true>(acc, fa, fb, 0, pw, px, K, ow, ox, wave_off);
+    int s = 1;
+    for (; s + 1 < KT; s += 2) {
+      small8_stage<false>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
+      small8_stage<false>(acc, fa, fb, s + 1, pw, px, K, ow, ox, wave_off);
+    }
+    if (s < KT) small8_stage<false>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
+
+    const int gn = __builtin_amdgcn_readfirstlane(grp.n), gld = __builtin_amdgcn_readfirstlane(grp.ldy);
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - (tc.m0 + wm * 64), 64)));
+    uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(tc.m0 + wm * 64, a.m) * gld * 2;
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * gld * 2, 0x00020000);
+    small_epilogue<false>(acc, area, grp.alpha * alpha_mul, out, tc.n0 + wn * 64, gn, gld, lane);
+    // the copies of stages past K are still landing in the buffers the next
+    // tile's first copies refill, and every wave must be done with them
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// W8A16 small-tile stage s (64 K values, two halves of 32): 32 MFMAs on set
+// f, weight-block-major within a half (MFMA t of half h: weight block t / 4,
+// activation block t % 4), weight block i + 1 dequantized two MFMAs before
+// its first use; after the wait and barrier (MFMA kSmallBarrier), read
+// r = 0..15 of stage s + 1 one per slot (r = 8 h + j: j < 4 weight block j of
+// half h, else activation block j - 4), and at t = 21, 23, .. 31 copy
+// (t - 21) / 2 of stage s + kSmallBufs (< 2 weight chunk, else activation
+// chunk).
+struct Small16Frags {
+  u32x2 w[2][4];
+  u32x4 x[2][4];
+};
+template <int kForm, bool kFirst>
+__device__ __forceinline__ void small16_stage(f32x4 (&acc)[4][4], const Small16Frags& f, Small16Frags& nf, int s,
+                                              const CopyPlan<4>& pw, const CopyPlan<8>& px, int K,
+                                              const W16Addr& ad, uint32_t wave_off) {
+  const uint8_t* nw = small16_w(s + 1);
+  const uint8_t* nx = small16_x(s + 1);
+  const int kw = (s + kSmallBufs) * 64;   // weight K byte of the stage being copied
+  const int kx = (s + kSmallBufs) * 128;  // activation K byte
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  W16Op<kForm> wcur = dequant8<kForm>(f.w[0][0][0], f.w[0][0][1]), wnext;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int h = t >> 4, i = (t >> 2) & 3, b = t & 3;
+    if (b == 2) {
+      const int hn = i == 3 ? h + 1 : h, in = (i + 1) & 3;
+      if (hn < 2) wnext = dequant8<kForm>(f.w[hn][in][0], f.w[hn][in][1]);
+    }
+    acc[i][b] = w16_mfma<kForm>(wcur, f.x[h][b], (kFirst && h == 0) ? zero : acc[i][b]);
+    if (b == 3) wcur = wnext;
+    if (t == kSmallBarrier)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kSmall16Wait) : "memory");
+    if (t > kSmallBarrier && t <= kSmallBarrier + 16) {
+      const int hh = (t - kSmallBarrier - 1) >> 3, j = (t - kSmallBarrier - 1) & 7;
+      if (j < 4)
+        nf.w[hh][j] = *reinterpret_cast<const u32x2*>(nw + ad.w[hh] + j * 1024);
+      else
+        nf.x[hh][j - 4] = lds_chunk(nx, ad.x[hh] + (j - 4) * 2048);
+    }
+    if (t >= 21 && (t & 1)) {
+      const int u = (t - 21) >> 1;
+      if (u < 2)
+        pw.copy_masked(small16_w(s), kw, K, u, wave_off);
+      else
+        px.copy_masked(small16_x(s), kx, 2 * K, u - 2, wave_off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Persistent W8A16 small-tile kernel (bf16 or binary16 activations and
+// output) over 128 x 128 tiles of all groups.
+template <int kForm>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
+gemm_w8a16_small_kernel(const GemmArgs a) {
+  static_assert(kForm != kFormF32, "16-bit activations");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = a.k;
+  const int KT = (K + 63) / 64;
+  const uint32_t wave_off = (uint32_t)wave * 64 * 16;
+  W16Addr ad;
+  ad.init(wn * 64 + (lane & 15), wm * 64 + (lane & 15), lane >> 4);
+  uint8_t* area = lds_mem + kSmallEpiOffset + wave * kSmallEpiWave;
+
+  for (int slot = blockIdx.x; slot < a.total_tiles; slot += (int)gridDim.x) {
+    const TileCoord tc = tile_at<kSmallTile, kSmallTile>(a, slot);
+    const GemmGroup& grp = a.g[tc.group];
+    CopyPlan<4> pw;
+    CopyPlan<8> px;
+    {
+      const uint8_t* w = grp.w + (int64_t)tc.n0 * K;
+      const uint8_t* x = static_cast<const uint8_t*>(a.x) + (int64_t)tc.m0 * K * 2;
+      pw.init2(w, grp.n - tc.n0, w, 0, K, tid);
+      px.init2(x, a.m - tc.m0, x, 0, (int64_t)K * 2, tid);
+    }
+#pragma unroll
+    for (int st = 0; st < kSmallBufs; ++st) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pw.copy_masked(small16_w(st), st * 64, K, u, wave_off);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) px.copy_masked(small16_x(st), st * 128, 2 * K, u, wave_off);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kSmallBufs - 1) * kSmall16Copies) : "memory");
+    Small16Frags fa, fb;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fa.w[hh][j] = *reinterpret_cast<const u32x2*>(small16_w(0) + ad.w[hh] + j * 1024);
+        fa.x[hh][j] = lds_chunk(small16_x(0), ad.x[hh] + j * 2048);
+      }
+    f32x4 acc[4][4];
+    small16_stage<kForm, true>(acc, fa, fb, 0, pw, px, K, ad, wave_off);
+    int s = 1;
+    for (; s + 1 < KT; s += 2) {
+      small16_stage<kForm, false>(acc, fb, fa, s, pw, px, K, ad, wave_off);
+      small16_stage<kForm, false>(acc, fa, fb, s + 1, pw, px, K, ad, wave_off);
+    }
+    if (s < KT) small16_stage<kForm, false>(acc, fb, fa, s, pw, px, K, ad, wave_off);
+
+    const int gn = __builtin_amdgcn_readfirstlane(grp.n), gld = __builtin_amdgcn_readfirstlane(grp.ldy);
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - (tc.m0 + wm * 64), 64)));
+    uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(tc.m0 + wm * 64, a.m) * gld * 2;
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * gld * 2, 0x00020000);
+    small_epilogue<kForm == kFormF16>(acc, area, grp.alpha, out, tc.n0 + wn * 64, gn, gld, lane);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
 // Compute units of the current device (256 on MI355X).
 int cu_count() {
   int dev = 0, n = 0;
@@ -1599,13 +1896,47 @@ int cu_count() {
 
 }  // namespace
 
-hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
-  // One workgroup per CU (160 KiB of LDS each), a multiple of the 8 XCDs.
+// One workgroup per CU (160 KiB of LDS each), a multiple of the 8 XCDs, at
+// most one per tile.
+int persistent_grid(int tiles) {
   static const int cus = cu_count();
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
-  if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL(gemm_w8a8_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return grid > tiles ? tiles : grid;
+}
+
+// The 128 x 128 plan of a (already planned for 256 x 256 tiles) when its
+// 256 x 256 tiles would keep at most 60% of the compute units busy; false (a
+// unchanged) otherwise. Measured on one MI355X at N = K = 4096: M = 2048
+// (256 x 256 tiles for half the CUs) runs faster on small tiles (W8A8 1953
+// against 1775 TFLOP/s, W8A16 1055 against 810), M = 3072 (three quarters)
+// on the big ones (2480 against 2022, 1209 against 1080).
+bool small_tiles_for(int64_t big_tiles) {
+  static const int cus = cu_count();
+  return 5 * big_tiles <= 3 * (int64_t)cus;
+}
+
+bool small_tiles(GemmArgs& a) {
+  if (!small_tiles_for(a.total_tiles)) return false;
+  a.tiles_m = (a.m + kSmallTile - 1) / kSmallTile;
+  int32_t t = 0;
+  for (int i = 0; i < a.ngroups; ++i) {
+    a.g[i].tiles_n = (a.g[i].n + kSmallTile - 1) / kSmallTile;
+    a.g[i].tile_begin = t;
+    t += a.tiles_m * a.g[i].tiles_n;
+  }
+  a.total_tiles = t;
+  return true;
+}
+
+hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s) {
+  GemmArgs b = a;
+  if (small_tiles(b))
+    hipLaunchKernelGGL(gemm_w8a8_small_kernel, dim3((unsigned)persistent_grid(b.total_tiles)), dim3(kThreads), 0, s,
+                       b);
+  else
+    hipLaunchKernelGGL(gemm_w8a8_kernel<false>, dim3((unsigned)persistent_grid(a.total_tiles)), dim3(kThreads), 0,
+                       s, a);
   return hipGetLastError();
 }
 
@@ -1728,14 +2059,16 @@ hipError_t launch_gemm_w8a16_splitk(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s) {
-  static const int cus = cu_count();
-  int grid = cus - cus % kXcds;
-  if (grid <= 0) grid = kXcds;
-  if (grid > a.total_tiles) grid = a.total_tiles;
+  GemmArgs b = a;
+  if (form != kW16F32 && small_tiles(b)) {
+    auto kernel = form == kW16F16 ? gemm_w8a16_small_kernel<kFormF16> : gemm_w8a16_small_kernel<kFormBf16>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(b.total_tiles)), dim3(kThreads), 0, s, b);
+    return hipGetLastError();
+  }
   auto kernel = form == kW16F16   ? gemm_w8a16_kernel<false, kFormF16>
                 : form == kW16F32 ? gemm_w8a16_kernel<false, kFormF32>
                                   : gemm_w8a16_kernel<false, kFormBf16>;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(a.total_tiles)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -67,6 +67,10 @@ hipError_t launch_gemm_w8a8(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_w8a8_splitk(const GemmArgs& a, hipStream_t s);
 // Compute units of the current device.
 int device_cu_count();
+// True when a W8A8 or 16-bit W8A16 GEMM launch whose 256 x 256 tiles number
+// big_tiles runs on the 128 x 128 tile kernels instead (those tiles would
+// keep at most 60% of the compute units busy).
+bool small_tiles_for(int64_t big_tiles);
 // The current device's copy of the library's static scratch array
 // (FP8LIN_SCRATCH_BYTES bytes), looked up once per device and kept.
 hipError_t device_scratch(void** ptr);
