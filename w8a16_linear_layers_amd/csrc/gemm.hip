@@ -87,31 +87,30 @@ __device__ __forceinline__ uint8_t* lds16_w(int s) { return lds_mem + s * kStage
 __device__ __forceinline__ uint8_t* lds16_x(int s) { return lds_mem + kStages16 * kStageE4M3 + s * kStageBf16; }
 
 // LDS tile layouts (fragment reads take 16-row blocks, lane (r, q) =
-// (l % 16, l / 16) reading row r). The swizzles were chosen against the lane
-// groupings a 64-bank LDS may serve together for a 16-byte read (16
-// consecutive lanes, lanes {8k..8k+7} with {8k+32..8k+39}, or lanes sharing
-// lane-index bits 1 and 4); the hardware's conflict counter does not follow
-// that model closely (it reads the same for several W8A8 layouts), so the
-// choices are measured rather than proven.
-//   128-byte rows of the W8A8 E4M3 tiles (lane quarters 32 bytes apart):
-//     chunk c of row r in physical chunk c ^ swz16(r). swz16 is linear in
-//     row bits 1-3; the one nonzero combination of those bits it maps to
-//     chunk bit 2 alone is bits 1 + 3, which no grouping above varies on its
-//     own.
+// (l % 16, l / 16) reading row r). The swizzles come from measurement: every
+// linear XOR swizzle of a 16-row block (a 3-bit chunk XOR from the 4 low row
+// bits, 4096 candidates) was read on one MI355X in the kernels' own lane
+// pattern, and SQ_LDS_BANK_CONFLICT per ds_read_b128 is either 0 (1344
+// swizzles; a conflict-free 16-byte read takes 4 LDS cycles), 3.56, 10.67 or
+// 24.89 cycles. Bijective swizzles can still conflict (for instance chunk
+// bits from row bits 1 + 3, 2, 1 for the W8A8 tiles read at 3.56, nearly
+// doubling the LDS time of every fragment read); the ones below read at 0.
+//   128-byte rows of the W8A8 E4M3 tiles (lane quarters 32 bytes apart,
+//     halves e = 0, 1): chunk c of row r in physical chunk c ^ swz16(r),
+//     swz16(r) = 2 (r & 3) + bit 2 of r.
 //   128-byte rows of the W8A16 bf16 activation tiles (lane quarters 16
-//     bytes apart): chunk c of row r in physical chunk c ^ swz8(r).
-//   64-byte rows of the W8A16 E4M3 weight tile (lane quarters 8 bytes
-//     apart): logical row r in physical row row64(r) = r ^ (bit3(r) << 1) (a
-//     swap inside groups of 4 rows), chunk c in physical chunk c ^ swz4(r).
-// All are XORs / involutions, hence bijections on the tile.
+//     bytes apart): chunk c of row r in physical chunk c ^ swz8(r),
+//     swz8(r) = r & 7.
+//   64-byte rows of the W8A16 E4M3 weight tile (ds_read_b64, lane quarters 8
+//     bytes apart): logical row r in physical row row64(r) = r ^ (bit3(r) << 1)
+//     (a swap inside groups of 4 rows), chunk c in physical chunk c ^ swz4(r);
+//     measured at 0 as well (1.78 without the row swap).
+// All are XORs / involutions, hence bijections on the tile, and depend only on
+// row bits below 5 (the copy plans rely on it).
 __device__ __forceinline__ int row64(int r) { return r ^ (((r >> 3) & 1) << 1); }
 __device__ __forceinline__ int swz4(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
-__device__ __forceinline__ int swz8(int r) {
-  return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
-}
-__device__ __forceinline__ int swz16(int r) {
-  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1) | (((r >> 1) & 1) << 2);
-}
+__device__ __forceinline__ int swz8(int r) { return r & 7; }
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 // ------------------------------------------------------------------ copies
 
