@@ -167,6 +167,16 @@ def test_small_tiles_full_rows_sampled(gpu, m):
     assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(xr, qw_ref, case.weight_scale), "w8a16")
     for o in outs:
         assert torch.equal(o, y8)  # the same projection three times in one grouped launch
+    # Rows are independent: the first m rows of the 8192-row product (256 x 256 tiles) are the same
+    # numbers, K summed in the same order per element.
+    xb = case.x.to(gpu)
+    qb = fp8lin.fp8lin_quantize_static(xb, case.input_scale)
+    assert torch.equal(qb[:m], q)
+    big8 = fp8lin.fp8lin_gemm_w8a8(qb, qw_gpu, case.input_scale, case.weight_scale)
+    big16 = fp8lin.fp8lin_gemm_w8a16(xb, qw_gpu, case.weight_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(big8[:m], y8), "128x128 and 256x256 W8A8 tiles differ"
+    assert torch.equal(big16[:m].view(torch.int16), y16.view(torch.int16)), "128x128 and 256x256 W8A16 tiles differ"
 
 
 def test_w8a16_identity_weight_is_exact(gpu):
