@@ -1239,7 +1239,12 @@ constexpr int kW16EpilogueStores = tile_stores(kSwiGLU ? 3 : (kForm == kFormF32 
 // per 64-element weight block (stage k reads weight block k / 3).
 // kSplit: group g multiplies K elements [g.koff, g.koff + a.ks) (row pitch
 // a.k), so its copies start koff elements into the weight and activation rows.
-template <bool kSwiGLU, int kForm, bool kSplit = false>
+// kKTail: K (or the slice) is not a whole number of 64-element stages, so the
+// last stage's chunks beyond it must read zero. Otherwise every copy lies
+// inside K (the cursor moves to the next tile after a tile's last stage) and
+// needs no per-lane test: each vector instruction in the stage loop costs
+// matrix-core time.
+template <bool kSwiGLU, int kForm, bool kSplit = false, bool kKTail = true>
 struct W16Copier {
   // The plain forms keep one weight-copy offset register (the fused SwiGLU
   // form, whose epilogue needs more registers, allocates better with four).
@@ -1270,11 +1275,12 @@ struct W16Copier {
     if (c < 4) {
       const int k0b = (kForm == kFormF32 ? k / 3 : k) * 64;
       const uint32_t o = pw.off(c);
-      pw.dma(c, k0b + pw.kbyte >= K ? kOutOfRange : o, (uint32_t)k0b,
+      pw.dma(c, kKTail && k0b + pw.kbyte >= K ? kOutOfRange : o, (uint32_t)k0b,
             lds_addr(lds16_w(buf)) + c * kThreads * 16 + wave_off);
     } else {
       const int k0b = k * 128;
-      px.dma(c - 4, k0b + px.kbyte >= 2 * XK ? kOutOfRange : px.off(c - 4), (uint32_t)k0b,
+      const uint32_t o = px.off(c - 4);
+      px.dma(c - 4, kKTail && k0b + px.kbyte >= 2 * XK ? kOutOfRange : o, (uint32_t)k0b,
             lds_addr(lds16_x(buf)) + (c - 4) * kThreads * 16 + wave_off);
     }
   }
@@ -1476,7 +1482,9 @@ __device__ __forceinline__ void w16_stage(f32x4 (&acc)[8][8], W16Half& fa, W16Ha
 // kSplit (bf16 only): split-K; every group is one K slice (a.ks elements
 // from g.koff, row pitch a.k) of the same product and stores its unscaled
 // float32 partial to its y.
-template <bool kSwiGLU, int kForm, bool kSplit = false>
+// kKTail: as for W16Copier (false only when K, or the slice, is a multiple
+// of 64).
+template <bool kSwiGLU, int kForm, bool kSplit = false, bool kKTail = true>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1))) void
 gemm_w8a16_kernel(const GemmArgs a) {
   static_assert(!(kSwiGLU && kForm == kFormF32), "the fused SwiGLU form has a 16-bit h");
@@ -1491,7 +1499,7 @@ gemm_w8a16_kernel(const GemmArgs a) {
   W16Addr ad;
   ad.init(wn * 128 + (lane & 15), wm * 128 + (lane & 15), lane >> 4);
 
-  W16Copier<kSwiGLU, kForm, kSplit> cp;
+  W16Copier<kSwiGLU, kForm, kSplit, kKTail> cp;
   cp.start_tile(a, blockIdx.x, tid);
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
@@ -1670,7 +1678,11 @@ struct Small8Frags {
 // The wait and barrier come after MFMA kSmallBarrier: the stage's own
 // fragments are already in registers, so the first MFMAs hide the barrier.
 constexpr int kSmallBarrier = 3;
-template <bool kFirst>
+// kMasked: the stage being copied may reach past K (the K tail, or the
+// stages past the tile's last one, which read zeros into buffers no one
+// reads); each lane then tests its chunk. Stages wholly inside K copy
+// without the test.
+template <bool kFirst, bool kMasked>
 __device__ __forceinline__ void small8_stage(f32x4 (&acc)[4][4], const Small8Frags& f, Small8Frags& nf, int s,
                                              const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int K,
                                              const int (&ow)[2], const int (&ox)[2], uint32_t wave_off) {
@@ -1701,10 +1713,17 @@ __device__ __forceinline__ void small8_stage(f32x4 (&acc)[4][4], const Small8Fra
 #pragma unroll
       for (int u = 0; u < kSmall8Copies; ++u)
         if ((3 * u) / 2 + kSmallBarrier + 1 == t) {
-          if (u < 4)
-            pw.copy_masked(small8_w(s), kc, K, u, wave_off);
-          else
-            px.copy_masked(small8_x(s), kc, K, u - 4, wave_off);
+          if constexpr (kMasked) {
+            if (u < 4)
+              pw.copy_masked(small8_w(s), kc, K, u, wave_off);
+            else
+              px.copy_masked(small8_x(s), kc, K, u - 4, wave_off);
+          } else {
+            if (u < 4)
+              pw.copy_one(small8_w(s), (uint32_t)kc, u, wave_off);
+            else
+              px.copy_one(small8_x(s), (uint32_t)kc, u - 4, wave_off);
+          }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1753,13 +1772,20 @@ gemm_w8a8_small_kernel(const GemmArgs a) {
       read_frag16(fa.x[f], small8_x(0), ox, f);
     }
     f32x4 acc[4][4];
-    small8_stage<true>(acc, fa, fb, 0, pw, px, K, ow, ox, wave_off);
+    small8_stage<true, true>(acc, fa, fb, 0, pw, px, K, ow, ox, wave_off);
+    // stage s copies stage s + kSmallBufs, wholly inside K while that is
+    // below K / 128
+    const int full_end = K / 128 - kSmallBufs;
     int s = 1;
-    for (; s + 1 < KT; s += 2) {
-      small8_stage<false>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
-      small8_stage<false>(acc, fa, fb, s + 1, pw, px, K, ow, ox, wave_off);
+    for (; s + 1 < KT && s + 1 < full_end; s += 2) {
+      small8_stage<false, false>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
+      small8_stage<false, false>(acc, fa, fb, s + 1, pw, px, K, ow, ox, wave_off);
     }
-    if (s < KT) small8_stage<false>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
+    for (; s + 1 < KT; s += 2) {
+      small8_stage<false, true>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
+      small8_stage<false, true>(acc, fa, fb, s + 1, pw, px, K, ow, ox, wave_off);
+    }
+    if (s < KT) small8_stage<false, true>(acc, fb, fa, s, pw, px, K, ow, ox, wave_off);
 
     const int gn = __builtin_amdgcn_readfirstlane(grp.n), gld = __builtin_amdgcn_readfirstlane(grp.ldy);
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - (tc.m0 + wm * 64), 64)));
@@ -1784,7 +1810,8 @@ struct Small16Frags {
   u32x2 w[2][4];
   u32x4 x[2][4];
 };
-template <int kForm, bool kFirst>
+// kMasked: as for small8_stage.
+template <int kForm, bool kFirst, bool kMasked>
 __device__ __forceinline__ void small16_stage(f32x4 (&acc)[4][4], const Small16Frags& f, Small16Frags& nf, int s,
                                               const CopyPlan<4>& pw, const CopyPlan<8>& px, int K,
                                               const W16Addr& ad, uint32_t wave_off) {
@@ -1814,10 +1841,17 @@ __device__ __forceinline__ void small16_stage(f32x4 (&acc)[4][4], const Small16F
     }
     if (t >= 21 && (t & 1)) {
       const int u = (t - 21) >> 1;
-      if (u < 2)
-        pw.copy_masked(small16_w(s), kw, K, u, wave_off);
-      else
-        px.copy_masked(small16_x(s), kx, 2 * K, u - 2, wave_off);
+      if constexpr (kMasked) {
+        if (u < 2)
+          pw.copy_masked(small16_w(s), kw, K, u, wave_off);
+        else
+          px.copy_masked(small16_x(s), kx, 2 * K, u - 2, wave_off);
+      } else {
+        if (u < 2)
+          pw.copy_one(small16_w(s), (uint32_t)kw, u, wave_off);
+        else
+          px.copy_one(small16_x(s), (uint32_t)kx, u - 2, wave_off);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1867,13 +1901,20 @@ gemm_w8a16_small_kernel(const GemmArgs a) {
         fa.x[hh][j] = lds_chunk(small16_x(0), ad.x[hh] + j * 2048);
       }
     f32x4 acc[4][4];
-    small16_stage<kForm, true>(acc, fa, fb, 0, pw, px, K, ad, wave_off);
+    small16_stage<kForm, true, true>(acc, fa, fb, 0, pw, px, K, ad, wave_off);
+    // stage s copies stage s + kSmallBufs, wholly inside K while that is
+    // below K / 64
+    const int full_end = K / 64 - kSmallBufs;
     int s = 1;
-    for (; s + 1 < KT; s += 2) {
-      small16_stage<kForm, false>(acc, fb, fa, s, pw, px, K, ad, wave_off);
-      small16_stage<kForm, false>(acc, fa, fb, s + 1, pw, px, K, ad, wave_off);
+    for (; s + 1 < KT && s + 1 < full_end; s += 2) {
+      small16_stage<kForm, false, false>(acc, fb, fa, s, pw, px, K, ad, wave_off);
+      small16_stage<kForm, false, false>(acc, fa, fb, s + 1, pw, px, K, ad, wave_off);
     }
-    if (s < KT) small16_stage<kForm, false>(acc, fb, fa, s, pw, px, K, ad, wave_off);
+    for (; s + 1 < KT; s += 2) {
+      small16_stage<kForm, false, true>(acc, fb, fa, s, pw, px, K, ad, wave_off);
+      small16_stage<kForm, false, true>(acc, fa, fb, s + 1, pw, px, K, ad, wave_off);
+    }
+    if (s < KT) small16_stage<kForm, false, true>(acc, fb, fa, s, pw, px, K, ad, wave_off);
 
     const int gn = __builtin_amdgcn_readfirstlane(grp.n), gld = __builtin_amdgcn_readfirstlane(grp.ldy);
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - (tc.m0 + wm * 64), 64)));
@@ -2041,9 +2082,10 @@ hipError_t launch_gate_up_swiglu(const GemmArgs& a, bool w8a16, bool f16, hipStr
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
+  const bool tail = a.k % 64 != 0;
   auto kernel = !w8a16 ? gemm_w8a8_kernel<true>
-                : f16  ? gemm_w8a16_kernel<true, kFormF16>
-                       : gemm_w8a16_kernel<true, kFormBf16>;
+                : f16  ? (tail ? gemm_w8a16_kernel<true, kFormF16> : gemm_w8a16_kernel<true, kFormF16, false, false>)
+                       : (tail ? gemm_w8a16_kernel<true, kFormBf16> : gemm_w8a16_kernel<true, kFormBf16, false, false>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -2053,7 +2095,8 @@ hipError_t launch_gemm_w8a16_splitk(const GemmArgs& a, hipStream_t s) {
   int grid = cus - cus % kXcds;
   if (grid <= 0) grid = kXcds;
   if (grid > a.total_tiles) grid = a.total_tiles;
-  hipLaunchKernelGGL((gemm_w8a16_kernel<false, kFormBf16, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  auto kernel = a.ks % 64 != 0 ? gemm_w8a16_kernel<false, kFormBf16, true> : gemm_w8a16_kernel<false, kFormBf16, true, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -2064,9 +2107,12 @@ hipError_t launch_gemm_w8a16(const GemmArgs& a, int form, hipStream_t s) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(b.total_tiles)), dim3(kThreads), 0, s, b);
     return hipGetLastError();
   }
-  auto kernel = form == kW16F16   ? gemm_w8a16_kernel<false, kFormF16>
-                : form == kW16F32 ? gemm_w8a16_kernel<false, kFormF32>
-                                  : gemm_w8a16_kernel<false, kFormBf16>;
+  const bool tail = a.k % 64 != 0;
+  auto kernel = form == kW16F16
+                    ? (tail ? gemm_w8a16_kernel<false, kFormF16> : gemm_w8a16_kernel<false, kFormF16, false, false>)
+                : form == kW16F32
+                    ? (tail ? gemm_w8a16_kernel<false, kFormF32> : gemm_w8a16_kernel<false, kFormF32, false, false>)
+                    : (tail ? gemm_w8a16_kernel<false, kFormBf16> : gemm_w8a16_kernel<false, kFormBf16, false, false>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(a.total_tiles)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
