@@ -159,15 +159,14 @@ __device__ __forceinline__ void wait_vmem_and_barrier() {
 // bits below 5, which j does not change, so a thread copies the same
 // logical chunk of every row it serves (kbyte), and the rows of chunks j and
 // j' of one half differ by a wave-uniform multiple of 256 / kChunks rows.
-// kSwz16: 128-byte rows in the W8A8 layout (swz16 instead of swz8).
-// kCompact: keep one offset register (off(0)) and form off(j) at issue time
-// from it and a scalar row step, instead of one register per chunk.
-template <int kChunks, bool kSwz16 = false, bool kCompact = false>
+// kSwz16: 128-byte rows in the W8A8 layout (swz16 instead of swz8). The
+// offsets are kept one register per chunk: forming them at issue time from
+// one register and a scalar step saves registers but costs vector
+// instructions in the stage loops, each of which costs matrix-core time.
+template <int kChunks, bool kSwz16 = false>
 struct CopyPlan {
-  static constexpr int kRowsPerChunk = kThreads / kChunks;  // rows between chunks j and j + 1
   i32x4 lo, hi;
-  uint32_t voff[kCompact ? 1 : kChunks];
-  uint32_t row_step;  // kRowsPerChunk rows in bytes (kCompact)
+  uint32_t voff[kChunks];
   int kbyte;  // first K byte of the thread's chunk within a stage row
 
   // Rows [0, 128) from src_lo (rows_lo of them valid), rows [128, 256) from
@@ -180,9 +179,8 @@ struct CopyPlan {
     const int n_hi = __builtin_amdgcn_readfirstlane(max(0, min(rows_hi, 128)));
     lo = make_rsrc(src_lo, (uint32_t)(n_lo * ld_bytes));
     hi = make_rsrc(src_hi, (uint32_t)(n_hi * ld_bytes));
-    row_step = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kRowsPerChunk * ld_bytes));
 #pragma unroll
-    for (int j = 0; j < (kCompact ? 1 : kChunks); ++j) {
+    for (int j = 0; j < kChunks; ++j) {
       const int p = j * kThreads + tid;
       const int r = kChunks == 4 ? row64(p / kChunks) : p / kChunks;
       const int c = (p % kChunks) ^ (kChunks == 4 ? swz4(r) : kSwz16 ? swz16(r) : swz8(r));
@@ -191,19 +189,8 @@ struct CopyPlan {
     }
   }
 
-  // Offset of chunk j (a compile-time constant in the unrolled callers). The
-  // compact form adds (j mod kChunks / 2) row steps to an opaque copy of
-  // off(0), so that the sums are formed where they are used rather than kept
-  // in registers across the stage loop.
-  __device__ __forceinline__ uint32_t off(int j) const {
-    if constexpr (kCompact) {
-      uint32_t v = voff[0], st = row_step;
-      asm volatile("" : "+v"(v), "+s"(st));
-      return v + (uint32_t)(j % (kChunks / 2)) * st;
-    } else {
-      return voff[j];
-    }
-  }
+  // Offset of chunk j (a compile-time constant in the unrolled callers).
+  __device__ __forceinline__ uint32_t off(int j) const { return voff[j]; }
 
   // Rows [row0, row0 + 256) of one matrix with `rows` valid rows from row0.
   __device__ __forceinline__ void init(const uint8_t* src, int row0, int rows, int64_t ld_bytes, int tid) {
@@ -229,8 +216,7 @@ struct CopyPlan {
   // of a row (the K tail).
   __device__ __forceinline__ void copy_masked(const uint8_t* lds_tile, int k0b, int kb, int j,
                                               uint32_t wave_off) const {
-    const uint32_t o = off(j);  // formed first: the compact form's opaque copy cannot sit under the select
-    dma(j, k0b + kbyte >= kb ? kOutOfRange : o, (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
+    dma(j, k0b + kbyte >= kb ? kOutOfRange : off(j), (uint32_t)k0b, lds_addr(lds_tile) + j * kThreads * 16 + wave_off);
   }
 
   // All chunks of the stage starting at byte `k0b`; chunks at or beyond
@@ -1246,9 +1232,7 @@ constexpr int kW16EpilogueStores = tile_stores(kSwiGLU ? 3 : (kForm == kFormF32 
 // matrix-core time.
 template <bool kSwiGLU, int kForm, bool kSplit = false, bool kKTail = true>
 struct W16Copier {
-  // The plain forms keep one weight-copy offset register (the fused SwiGLU
-  // form, whose epilogue needs more registers, allocates better with four).
-  CopyPlan<4, false, !kSwiGLU> pw;  // E4M3 weight, 64-byte stage rows
+  CopyPlan<4> pw;  // E4M3 weight, 64-byte stage rows
   CopyPlan<8> px;                   // bf16 activation, 128-byte stage rows
   int tile_slot;   // dispatch slot of the tile being copied
   int k;           // next stage of that tile
@@ -1453,7 +1437,7 @@ __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W
   // the next set's buffer base, kept opaque so that per-block addresses are
   // not precomputed for every buffer
   uint32_t bw = lds_addr(lds16_w(nb)), bx = lds_addr(lds16_x(nb));
-  asm volatile("" : "+v"(bw), "+v"(bx));
+  asm volatile("" : "+s"(bw), "+s"(bx));
   const uint8_t* nw = lds_mem + (bw - lds_addr(lds_mem));
   const uint8_t* nx = lds_mem + (bx - lds_addr(lds_mem));
   W16Op<kForm> wcur = dequant8<kForm>(f.w[0][0], f.w[0][1]), wnext;
@@ -1468,8 +1452,8 @@ __device__ __forceinline__ void w16_half(f32x4 (&acc)[8][8], const W16Half& f, W
 template <bool kReadNext, bool kSwiGLU, int kForm, bool kSplit, class Copier>
 __device__ __forceinline__ void w16_stage(f32x4 (&acc)[8][8], W16Half& fa, W16Half& fb, int b, const W16Addr& ad,
                                           Copier& cp, int K, int XK, uint32_t wave_off, bool after_stores) {
-  const int nb = b == 2 ? 0 : b + 1;  // next stage's buffer
-  const int cb = b == 0 ? 2 : b - 1;  // buffer of stage + 2
+  const int nb = b == 2 ? 0 : b + 1;   // next stage's buffer
+  const int cb = nb == 2 ? 0 : nb + 1;  // buffer of stage + 2 (so written, it stays scalar)
   w16_half<false, true, kSwiGLU, kForm, kSplit>(acc, fa, fb, b, 1, ad, cp, cb, K, XK, wave_off, false);
   w16_half<true, kReadNext, kSwiGLU, kForm, kSplit>(acc, fb, fa, nb, 0, ad, cp, cb, K, XK, wave_off, after_stores);
 }
