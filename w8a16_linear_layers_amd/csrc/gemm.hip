@@ -1782,21 +1782,31 @@ gemm_w8a8_small_kernel(const GemmArgs a) {
   }
 }
 
-// W8A16 small-tile stage s (64 K values, two halves of 32): 32 MFMAs on set
-// f, weight-block-major within a half (MFMA t of half h: weight block t / 4,
-// activation block t % 4), weight block i + 1 dequantized two MFMAs before
-// its first use; after the wait and barrier (MFMA kSmallBarrier), read
-// r = 0..15 of stage s + 1 one per slot (r = 8 h + j: j < 4 weight block j of
-// half h, else activation block j - 4), and at t = 21, 23, .. 31 copy
-// (t - 21) / 2 of stage s + kSmallBufs (< 2 weight chunk, else activation
-// chunk).
+// W8A16 small tiles use a different wave split from W8A8: wave w takes the
+// 32 output columns [32 w, 32 w + 32) of all 128 rows (2 weight blocks x 8
+// activation blocks of 16), so each weight block it converts to bf16 (four
+// v_cvt_scalef32_pk_bf16_fp8 per lane) feeds 8 MFMAs instead of 4; vector
+// instructions in the stage loop are not hidden behind the 16-cycle MFMAs,
+// and with 64 x 64 wave tiles the conversions (one per MFMA) were the
+// kernel's largest cost. Reads per stage: 20 instead of 16.
+//
+// Stage s (64 K values, two halves of 32): 32 MFMAs on set f, weight-block
+// major within a half (MFMA t of half h: weight block (t % 16) / 8,
+// activation block t % 8), the next weight block converted two MFMAs before
+// its first use; after the wait and barrier (MFMA kSmallBarrier) the 20
+// reads of stage s + 1 into nf, one per slot (r = 10 h + j: j < 2 weight
+// block j of half h, else activation block j - 2), and at t = 21, 23, .. 31
+// copy (t - 21) / 2 of stage s + kSmallBufs (< 2 weight chunk, else
+// activation chunk).
 struct Small16Frags {
-  u32x2 w[2][4];
-  u32x4 x[2][4];
+  u32x2 w[2][2];
+  u32x4 x[2][8];
 };
+constexpr int kSmall16Reads = 2 * (2 + 8);
+static_assert(kSmallBarrier + kSmall16Reads < 32, "the reads of the next stage fit the stage's slots");
 // kMasked: as for small8_stage.
 template <int kForm, bool kFirst, bool kMasked>
-__device__ __forceinline__ void small16_stage(f32x4 (&acc)[4][4], const Small16Frags& f, Small16Frags& nf, int s,
+__device__ __forceinline__ void small16_stage(f32x4 (&acc)[2][8], const Small16Frags& f, Small16Frags& nf, int s,
                                               const CopyPlan<4>& pw, const CopyPlan<8>& px, int K,
                                               const W16Addr& ad, uint32_t wave_off) {
   const uint8_t* nw = small16_w(s + 1);
@@ -1807,21 +1817,21 @@ __device__ __forceinline__ void small16_stage(f32x4 (&acc)[4][4], const Small16F
   W16Op<kForm> wcur = dequant8<kForm>(f.w[0][0][0], f.w[0][0][1]), wnext;
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
-    const int h = t >> 4, i = (t >> 2) & 3, b = t & 3;
-    if (b == 2) {
-      const int hn = i == 3 ? h + 1 : h, in = (i + 1) & 3;
+    const int h = t >> 4, i = (t >> 3) & 1, b = t & 7;
+    if (b == 6) {
+      const int hn = i == 1 ? h + 1 : h, in = i ^ 1;
       if (hn < 2) wnext = dequant8<kForm>(f.w[hn][in][0], f.w[hn][in][1]);
     }
     acc[i][b] = w16_mfma<kForm>(wcur, f.x[h][b], (kFirst && h == 0) ? zero : acc[i][b]);
-    if (b == 3) wcur = wnext;
+    if (b == 7) wcur = wnext;
     if (t == kSmallBarrier)
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kSmall16Wait) : "memory");
-    if (t > kSmallBarrier && t <= kSmallBarrier + 16) {
-      const int hh = (t - kSmallBarrier - 1) >> 3, j = (t - kSmallBarrier - 1) & 7;
-      if (j < 4)
+    if (t > kSmallBarrier && t <= kSmallBarrier + kSmall16Reads) {
+      const int r = t - kSmallBarrier - 1, hh = r / 10, j = r % 10;
+      if (j < 2)
         nf.w[hh][j] = *reinterpret_cast<const u32x2*>(nw + ad.w[hh] + j * 1024);
       else
-        nf.x[hh][j - 4] = lds_chunk(nx, ad.x[hh] + (j - 4) * 2048);
+        nf.x[hh][j - 2] = lds_chunk(nx, ad.x[hh] + (j - 2) * 2048);
     }
     if (t >= 21 && (t & 1)) {
       const int u = (t - 21) >> 1;
@@ -1841,6 +1851,41 @@ __device__ __forceinline__ void small16_stage(f32x4 (&acc)[4][4], const Small16F
   }
 }
 
+// Epilogue of a W8A16 small tile: the wave's 128 x 32 block, bf16(acc *
+// alpha) (binary16 with kF16), staged in the wave's 8 KiB area (row m at
+// m * 64, 16-byte chunk c at c ^ (m % 4)), then 8 stores of 16 rows x 64
+// bytes.
+template <bool kF16>
+__device__ __forceinline__ void small16_epilogue(const f32x4 (&acc)[2][8], uint8_t* area, float alpha,
+                                                 __amdgpu_buffer_rsrc_t out, int col0, int gn, int gld, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int q = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = 16 * b + r, c = 2 * i + (q >> 1);
+      const f32x4 x = acc[i][b];
+      u32x2 v;
+      v[0] = h16x2<kF16>(x[0] * alpha, x[1] * alpha);
+      v[1] = h16x2<kF16>(x[2] * alpha, x[3] * alpha);
+      *reinterpret_cast<u32x2*>(area + m * 64 + ((c ^ (m & 3)) * 16) + (q & 1) * 8) = v;
+    }
+  const int c = lane & 3, col = col0 + 8 * c;
+  u32x4 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = 16 * k + (lane >> 2);
+    v[k] = *reinterpret_cast<const u32x4*>(area + row * 64 + ((c ^ (row & 3)) * 16));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = 16 * k + (lane >> 2);
+    const uint32_t off = col < gn ? (uint32_t)(row * gld + col) * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_buffer_store_b128(v[k], out, (int)off, 0, kStreamStore);
+  }
+}
+
 // Persistent W8A16 small-tile kernel (bf16 or binary16 activations and
 // output) over 128 x 128 tiles of all groups.
 template <int kForm>
@@ -1849,12 +1894,11 @@ gemm_w8a16_small_kernel(const GemmArgs a) {
   static_assert(kForm != kFormF32, "16-bit activations");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
   const int K = a.k;
   const int KT = (K + 63) / 64;
   const uint32_t wave_off = (uint32_t)wave * 64 * 16;
   W16Addr ad;
-  ad.init(wn * 64 + (lane & 15), wm * 64 + (lane & 15), lane >> 4);
+  ad.init(wave * 32 + (lane & 15), lane & 15, lane >> 4);
   uint8_t* area = lds_mem + kSmallEpiOffset + wave * kSmallEpiWave;
 
   for (int slot = blockIdx.x; slot < a.total_tiles; slot += (int)gridDim.x) {
@@ -1878,13 +1922,13 @@ gemm_w8a16_small_kernel(const GemmArgs a) {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((kSmallBufs - 1) * kSmall16Copies) : "memory");
     Small16Frags fa, fb;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        fa.w[hh][j] = *reinterpret_cast<const u32x2*>(small16_w(0) + ad.w[hh] + j * 1024);
-        fa.x[hh][j] = lds_chunk(small16_x(0), ad.x[hh] + j * 2048);
-      }
-    f32x4 acc[4][4];
+      for (int j = 0; j < 2; ++j) fa.w[hh][j] = *reinterpret_cast<const u32x2*>(small16_w(0) + ad.w[hh] + j * 1024);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fa.x[hh][j] = lds_chunk(small16_x(0), ad.x[hh] + j * 2048);
+    }
+    f32x4 acc[2][8];
     small16_stage<kForm, true, true>(acc, fa, fb, 0, pw, px, K, ad, wave_off);
     // stage s copies stage s + kSmallBufs, wholly inside K while that is
     // below K / 64
@@ -1901,10 +1945,10 @@ gemm_w8a16_small_kernel(const GemmArgs a) {
     if (s < KT) small16_stage<kForm, false, true>(acc, fb, fa, s, pw, px, K, ad, wave_off);
 
     const int gn = __builtin_amdgcn_readfirstlane(grp.n), gld = __builtin_amdgcn_readfirstlane(grp.ldy);
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - (tc.m0 + wm * 64), 64)));
-    uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(tc.m0 + wm * 64, a.m) * gld * 2;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(a.m - tc.m0, 128)));
+    uint8_t* base = static_cast<uint8_t*>(grp.y) + (int64_t)min(tc.m0, a.m) * gld * 2;
     const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, rows * gld * 2, 0x00020000);
-    small_epilogue<kForm == kFormF16>(acc, area, grp.alpha, out, tc.n0 + wn * 64, gn, gld, lane);
+    small16_epilogue<kForm == kFormF16>(acc, area, grp.alpha, out, tc.n0 + wave * 32, gn, gld, lane);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
