@@ -179,6 +179,21 @@ def test_gemm_w8a16_f16_full_size_sampled(gpu):
                   "w8a16 f16 full size")
 
 
+def test_gemm_w8a16_f16_big_tiles_k_tail_sampled(gpu):
+    """256 x 256 tiles (187 of them) with K not a whole number of 64-element stages: the form whose copies test
+    each lane's chunk against K."""
+    announce("gemm_w8a16 f16 2600x4104x528 (256x256 tiles, K tail)")
+    m, n, k = 2600, 4104, 528
+    x = normal_f16((m, k), 0.35, 97)
+    qw, qr, s_w = weight(n, k, 98, gpu)
+    y = fp8lin.fp8lin_gemm_w8a16(x.to(gpu), qw, s_w)
+    torch.cuda.synchronize()
+    rows = sample_rows(m, 96, 7)
+    xr = f64(x[rows])
+    assert_within(f64(y)[rows], linear.gemm_w8a16(xr, qr, s_w), linear.gemm_w8a16_bound(xr, qr, s_w, k, f16.ulp),
+                  "w8a16 f16 K tail")
+
+
 def test_gemm_w8a16_f16_exact_on_scaled_permutations(gpu):
     announce("gemm_w8a16 f16 permutation")
     n = 528

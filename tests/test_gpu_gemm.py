@@ -297,7 +297,7 @@ def test_gemm_w8a8_splitk(gpu, m, n, k, splits):
 
 
 @pytest.mark.parametrize("m,n,k,splits", [(1024, 4096, 4096, 2), (1024, 4096, 4096, 4), (300, 528, 1024, 4),
-                                          (77, 64, 128, 2)])
+                                          (77, 64, 128, 2), (77, 64, 160, 2)])
 def test_gemm_w8a16_splitk(gpu, m, n, k, splits):
     """W8A16 with K split into float32 partials, summed in slice order: the oracle's tolerance, both the split
     and the unsplit GEMM within the float32-summation bound of the exact product (their summation orders
