@@ -1582,16 +1582,21 @@ gemm_w8a16_kernel(const GemmArgs a) {
 // ------------------------------------------------------------------ small tiles
 // Shapes whose 256 x 256 tiles cannot fill the device (M = 1024 rows of a
 // 4096 -> 4096 projection: 64 tiles for 256 compute units) run on 128 x 128
-// tiles instead: 4 waves of 64 x 64 (4 x 4 blocks of 16 x 16, the same MFMA
-// forms, fragment layouts and LDS swizzles as the 256 x 256 kernels). K runs
-// in stages held in kSmallBufs LDS buffers; the copies of stage s + 4 are
-// issued during stage s, into the buffer stage s used, and every stage's
-// fragments are read into registers during the previous stage (two
-// register sets, so the stage loop is unrolled by two). One barrier per
-// stage: after it, every wave's copies of stage s + 1 have landed and every
-// wave has read stage s's buffer (lgkmcnt(0) precedes it). Copies of stages
-// past K read zeros, so every stage issues the same copies and the waits
-// count them uniformly.
+// tiles instead, 4 waves each (W8A8: 64 x 64 per wave, 4 x 4 blocks of
+// 16 x 16; W8A16: 32 output columns of all 128 rows, see its stage below),
+// with the same MFMA forms, fragment layouts and LDS swizzles as the
+// 256 x 256 kernels. K runs in stages held in kSmallBufs LDS buffers; the
+// copies of stage s + 4 are issued during stage s, into the buffer stage s
+// used, and every stage's fragments are read into registers during the
+// previous stage (two register sets, so the stage loop is unrolled by two).
+// One barrier per stage: after it, every wave's copies of stage s + 1 have
+// landed and every wave has read stage s's buffer (lgkmcnt(0) precedes it).
+// Every stage issues the same copies, so the waits count them uniformly;
+// the copies of stages that reach past K (the K tail, and the stages after
+// the tile's last one, into buffers no one reads) test each lane's chunk
+// against K and read zeros there, which also keeps them inside the tensor
+// (the K offset travels in the scalar offset, outside the buffer range
+// check).
 constexpr int kSmallTile = 128;
 constexpr int kSmallBufs = 4;
 constexpr int kSmall8Half = kSmallTile * 128;             // one operand of a W8A8 stage: 128 rows x 128 bytes
@@ -1616,7 +1621,7 @@ __device__ __forceinline__ uint8_t* small8_x(int s) { return small8_w(s) + kSmal
 __device__ __forceinline__ uint8_t* small16_w(int s) { return lds_mem + (s % kSmallBufs) * kSmall16Stage; }
 __device__ __forceinline__ uint8_t* small16_x(int s) { return small16_w(s) + kSmall16W; }
 
-// Epilogue of a small tile: the wave's 64 x 64 block, bf16(acc * alpha)
+// Epilogue of a W8A8 small tile: the wave's 64 x 64 block, bf16(acc * alpha)
 // (binary16 with kF16), staged in the wave's 8 KiB area (row m at m * 128,
 // 16-byte chunk c at c ^ (m % 8)), then 8 stores of 8 rows x 128 bytes.
 template <bool kF16>
