@@ -5,7 +5,7 @@ import sys
 import numpy as np
 import torch
 
-from oracle import linear
+from oracle import linear, swiglu
 
 
 def announce(what):
@@ -44,3 +44,18 @@ def sample_rows(m, count, seed):
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([rng.choice(m, size=min(count, m), replace=False), [0, m - 1]]))
     return rows
+
+
+def check_swiglu_codes(g, u, s_h, got):
+    """SwiGLU E4M3 codes of bf16 g, u against the oracle's: equal, except where the exact value lies within
+    relative 2^-20 of an E4M3 rounding midpoint, where the other neighbour (one code step away) is accepted.
+    Returns the number of such differences."""
+    ref, t = swiglu.swiglu_2in_quant(f32(g).astype(np.float64), f32(u).astype(np.float64), s_h)
+    diff = got != ref
+    if diff.any():
+        near = swiglu.near_midpoint(t)
+        assert not (diff & ~near).any(), "%d codes differ away from a midpoint" % np.count_nonzero(diff & ~near)
+        # where they differ, the GPU chose the other neighbour of the midpoint
+        step = (got[diff] & 0x7F).astype(int) - (ref[diff] & 0x7F).astype(int)
+        assert np.all(np.abs(step) == 1)
+    return int(diff.sum())

@@ -18,7 +18,7 @@ import torch
 import w8a16_linear_layers_amd as fp8lin
 from oracle import bf16 as obf16
 from oracle import linear, swiglu
-from tests.helpers import announce, assert_gemm_close, f32, sample_rows, u8
+from tests.helpers import announce, assert_gemm_close, check_swiglu_codes, f32, sample_rows, u8
 from workloads import config3, config4, normal_bf16
 
 pytestmark = pytest.mark.gpu
@@ -127,18 +127,6 @@ def test_gate_up_group(gpu):
 
 
 # ---------------------------------------------------------------- SwiGLU
-
-
-def check_swiglu_codes(g, u, s_h, got):
-    ref, t = swiglu.swiglu_2in_quant(f32(g).astype(np.float64), f32(u).astype(np.float64), s_h)
-    diff = got != ref
-    if diff.any():
-        near = swiglu.near_midpoint(t)
-        assert not (diff & ~near).any(), "%d codes differ away from a midpoint" % np.count_nonzero(diff & ~near)
-        # where they differ, the GPU chose the other neighbour of the midpoint
-        step = (got[diff] & 0x7F).astype(int) - (ref[diff] & 0x7F).astype(int)
-        assert np.all(np.abs(step) == 1)
-    return int(diff.sum())
 
 
 @pytest.mark.parametrize("shape", [(1, 16), (37, 208), (1000, 1040)])

@@ -2,10 +2,13 @@
 
 The mode trace must be the printed W8A16 x3 / W8A8 x2 / W8A16 x3 bit for
 bit; kernel launch counts show one activation quantization per shared group
-on W8A8 steps and none on W8A16 steps. End-to-end numerics of one block
-stack against the oracle's own chain (each stage rounded to bf16 as the
-layer outputs it) are reported and loosely bounded: the pages print no
-values for this, so beyond the per-op parity tests it is unpinned.
+on W8A8 steps and none on W8A16 steps. Every op of a block is checked
+element by element against the oracle applied to the GPU's own input to
+that op (teacher-forced: rows and ops are independent, so each check is
+exact for its op). End-to-end numerics of one block stack against the
+oracle's own chain (each stage rounded to bf16 as the layer outputs it) are
+reported and loosely bounded: the pages print no values for this, so beyond
+the per-op checks it is unpinned.
 """
 
 import json
@@ -18,7 +21,7 @@ import torch
 import w8a16_linear_layers_amd as fp8lin
 from oracle import bf16 as obf16
 from oracle import linear, swiglu
-from tests.helpers import announce, f32
+from tests.helpers import announce, assert_gemm_close, check_swiglu_codes, f32, u8
 from w8a16_linear_layers_amd import schedule
 from workloads import config5, config5_step_input
 
@@ -86,6 +89,53 @@ def test_eight_step_trace_and_launch_counts(gpu, setup, golden_dir):
     assert c1[fp8lin.KERNEL_GEMM_W8A8] == 4 * passes8
     assert c1[fp8lin.KERNEL_GEMM_W8A16] == 4 * passes16
     assert c1[fp8lin.KERNEL_SWIGLU] == passes8 + passes16
+
+
+@pytest.mark.parametrize("mode", ["W8A8", "W8A16"])
+def test_block_ops_teacher_forced(gpu, setup, mode):
+    """One block pass (split MLP) at step 3's input, each op against the oracle on the GPU's own input to it:
+    Q, K, V from x; the output projection from the GPU's V; gate and up from the GPU's projection output; the
+    SwiGLU (E4M3 codes, or bf16 within one ulp) from the GPU's gate and up; the down projection from the
+    GPU's h."""
+    announce("block ops teacher-forced %s" % mode)
+    cases, blocks, buf = setup
+    c, w = cases[0], blocks[0]
+    x = config5_step_input(3, 0, M, HIDDEN)
+    m = fp8lin.MODE_W8A8 if mode == "W8A8" else fp8lin.MODE_W8A16
+    y = schedule.block_forward(w, x.to(gpu), m, buf, buf.out[0])
+    torch.cuda.synchronize()
+    qw = lambda t, s: linear.quantize_static(f32(t), s)  # noqa: E731
+    # both sides quantize the weights; the codes must agree before the products are compared
+    pairs = list(zip(w.qkv, c.w_qkv, c.s_qkv)) + [(w.out, c.w_out, c.s_out), (w.gate, c.w_gate, c.s_gate),
+                                                   (w.up, c.w_up, c.s_up), (w.down, c.w_down, c.s_down)]
+    for codes, wt, s_w in pairs:
+        assert np.array_equal(u8(codes), qw(wt, s_w))
+    xs = f32(x)
+    if mode == "W8A8":
+        qx = linear.quantize_static(xs, c.s_in_qkv)
+        for got, wt, s_w, name in zip((buf.q, buf.k, buf.v), c.w_qkv, c.s_qkv, "QKV"):
+            assert_gemm_close(got, linear.gemm_w8a8(qx, qw(wt, s_w), c.s_in_qkv, s_w), "W8A8 " + name)
+        v = f32(buf.v)
+        assert_gemm_close(buf.o, linear.gemm_w8a8(linear.quantize_static(v, c.s_in_out), qw(c.w_out, c.s_out),
+                                                   c.s_in_out, c.s_out), "W8A8 output projection")
+        qo = linear.quantize_static(f32(buf.o), c.s_in_mlp)
+        assert_gemm_close(buf.g, linear.gemm_w8a8(qo, qw(c.w_gate, c.s_gate), c.s_in_mlp, c.s_gate), "W8A8 gate")
+        assert_gemm_close(buf.u, linear.gemm_w8a8(qo, qw(c.w_up, c.s_up), c.s_in_mlp, c.s_up), "W8A8 up")
+        n = check_swiglu_codes(buf.g, buf.u, c.s_h, u8(buf.h8))
+        print("SwiGLU codes at a rounding midpoint: %d" % n)
+        assert_gemm_close(y, linear.gemm_w8a8(u8(buf.h8), qw(c.w_down, c.s_down), c.s_h, c.s_down), "W8A8 down")
+    else:
+        for got, wt, s_w, name in zip((buf.q, buf.k, buf.v), c.w_qkv, c.s_qkv, "QKV"):
+            assert_gemm_close(got, linear.gemm_w8a16(xs, qw(wt, s_w), s_w), "W8A16 " + name)
+        assert_gemm_close(buf.o, linear.gemm_w8a16(f32(buf.v), qw(c.w_out, c.s_out), c.s_out),
+                          "W8A16 output projection")
+        o = f32(buf.o)
+        assert_gemm_close(buf.g, linear.gemm_w8a16(o, qw(c.w_gate, c.s_gate), c.s_gate), "W8A16 gate")
+        assert_gemm_close(buf.u, linear.gemm_w8a16(o, qw(c.w_up, c.s_up), c.s_up), "W8A16 up")
+        h = swiglu.swiglu_2in(f32(buf.g), f32(buf.u))
+        got = f32(buf.h16).astype(np.float64)
+        assert np.all(np.abs(got - h) <= obf16.ulp(h)), "W8A16 SwiGLU beyond one bf16 ulp"
+        assert_gemm_close(y, linear.gemm_w8a16(f32(buf.h16), qw(c.w_down, c.s_down), c.s_down), "W8A16 down")
 
 
 @pytest.mark.parametrize("mode", ["W8A8", "W8A16"])
