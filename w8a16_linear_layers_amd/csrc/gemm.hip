@@ -580,101 +580,139 @@ constexpr int kLastCopy1 = kSlotFree + 16;  // ... of its stage 1
 constexpr int kLastCopyEnd = kSlotFree + 32;
 
 // ------------------------------------------------------------------ overlapped epilogue
-// Half of the plain bf16 epilogue runs under the matrix cores' work instead
-// of after it. A wave's 128 x 128 output block leaves in two parts of 64
-// columns:
+// Most of the plain bf16 epilogue runs beside the matrix cores' work of a
+// tile's last stage instead of after it. A wave's 128 x 128 output block
+// leaves in two parts of 64 columns:
 //   part A, acc[0..3][*] (weight blocks 0-3), is final once the first half
-//     of the tile's last stage has run (acc[i][b] takes its last MFMA at
-//     slot 4 b + i) and is written during that stage, from slot kEpiA0 on,
-//     while the second half multiplies into acc[4..7];
-//   part B, acc[4..7][*], is final only after the last MFMA and is written
-//     right after the stage, before the next tile starts.
+//     of the stage has run (acc[i][b] takes its last MFMA at slot 4 b + i);
+//   part B, acc[4..7][*], becomes final through the second half (last MFMA
+//     at slot 32 + 4 b + i).
 // Each part is 4 passes of 32 rows (pass j: m-blocks 2 j, 2 j + 1). A pass is
 // 8 units -- unit u scales acc[4 P + (u & 3)][2 j + (u >> 2)] by alpha,
 // rounds to bf16 and writes it to the wave's staging area (one ds_write_b64
 // per lane) -- then 4 reads of 8 staged rows (ds_read_b128) and 4 stores of
 // those rows (buffer_store_dwordx4, 8 lanes per 128-byte row segment).
 // Passes alternate between the two 4 KiB halves of the wave's 8 KiB area.
-// Within a slot the order is: MFMA, own fragment read, free barrier, copy,
-// epilogue unit, epilogue read, epilogue store.
+// The plan below places the 8 passes one unit per slot from slot kEpi0:
+// all of part A and 3 of part B's passes' units fall inside the stage, the
+// rest runs right after it, before the next tile starts. Within a slot the
+// order is: MFMA, own fragment read, free barrier, copy, epilogue unit,
+// epilogue read, epilogue store.
 //
 // Measured on one box (16384 x 4096 x 4096, one launch): 2941 -> 2993 and
-// 2956 -> 3022 TFLOP/s against the whole epilogue after the stage; with no
-// epilogue at all (a diagnostic build) 3234-3283, i.e. the epilogue costs
-// about 4 us per tile. Interleaving a unit (4 accumulator reads, 4
-// multiplies, 2 packs, 1 LDS write) per slot already outlasts the 16 x 16 x
-// 128 MFMA beside it, so part A's cost is only partly hidden. Part B in the
-// first half of the next tile's stage 0 (whose MFMAs start from zero and
-// write only acc[0..3] there) ran out of registers beside stage 0's
-// fragments and spilled; stores straight from the accumulators (no staging)
-// were 15-30% slower overall; a software-pipelined part B measured the same.
+// 2956 -> 3022 TFLOP/s with part A in the stage against the whole epilogue
+// after it, and 3026 -> 3040 with part B's first passes moved in as well;
+// with no epilogue at all (a diagnostic build) 3234-3283. Interleaving a
+// unit (4 accumulator reads, 4 multiplies, 2 packs, 1 LDS write) per slot
+// already outlasts the 16 x 16 x 128 MFMA beside it, so the work is only
+// partly hidden, and the board is power-limited: the epilogue's
+// instructions cost clock wherever they run. Part B in the first half of
+// the next tile's stage 0 (whose MFMAs start from zero and write only
+// acc[0..3] there) ran out of registers beside stage 0's fragments and
+// spilled; stores straight from the accumulators (no staging) were 15-30%
+// slower overall; a software-pipelined part B measured the same.
 constexpr int kEpiHalf = 4096;  // bytes of one pass: 32 rows x 128 bytes
 static_assert(2 * kEpiHalf == kW8A8EpiWave, "two pass areas per wave");
 
 struct EpiSlot {
   int unit, rd, st;  // -1, or pass * 8 + unit / pass * 4 + read / pass * 4 + store
 };
+// Passes 0-3 are part A, 4-7 part B (pass p: part p / 4, rows 32 (p % 4) ..,
+// staging half p % 2). Slots 0-63 go with the last stage's MFMAs; later
+// slots only order what runs after the stage.
+constexpr int kEpiSlots = 128;
 struct EpiPlan {
-  EpiSlot op[64];
+  EpiSlot op[kEpiSlots];
+  int end;  // one past the last slot in use
   bool ok;
 };
+constexpr int kMfmaLatencySlots = 4;  // slots between an accumulator's last MFMA and its first read
+// First slot at which unit u of pass p reads a final accumulator:
+// acc[4 P + (u & 3)][2 j + (u >> 2)] takes its last MFMA at slot 32 P + 4 b + i.
+constexpr int epi_ready(int p, int u) {
+  return 32 * (p >> 2) + 4 * (2 * (p & 3) + (u >> 2)) + (u & 3) + kMfmaLatencySlots;
+}
 
-// Units of pass j at slots a0 + 8 j + u, its reads at a0 + 8 + 8 j + 2 k,
-// each store kStoreLag slots after its read.
+// Greedy plan, one unit, one read and one store per slot at most: the units
+// of pass p in order, from slot a0, each once its accumulator is final and,
+// for pass p >= 2, after the last read of pass p - 2 (same staging half);
+// read k of pass p after the pass's units, two slots after read k - 1 and
+// after store k of pass p - 1 (same registers); each store kStoreLag slots
+// after its read.
 constexpr int kStoreLag = 3;
 constexpr EpiPlan make_epi_plan(int a0) {
   EpiPlan p{};
   p.ok = true;
-  for (int t = 0; t < 64; ++t) p.op[t] = EpiSlot{-1, -1, -1};
-  for (int j = 0; j < 4; ++j) {
+  p.end = 0;
+  for (int t = 0; t < kEpiSlots; ++t) p.op[t] = EpiSlot{-1, -1, -1};
+  int last_unit = a0 - 1, last_rd[8] = {}, st_of[8][4] = {};
+  for (int q = 0; q < 8; ++q) {
     for (int u = 0; u < 8; ++u) {
-      const int t = a0 + 8 * j + u;
-      if (t >= 64 || p.op[t].unit >= 0) p.ok = false;
-      else p.op[t].unit = 8 * j + u;
-    }
-    for (int k = 0; k < 4; ++k) {
-      const int tr = a0 + 8 + 8 * j + 2 * k, ts = tr + kStoreLag;
-      if (ts >= 64 || p.op[tr].rd >= 0 || p.op[ts].st >= 0) p.ok = false;
-      else {
-        p.op[tr].rd = 4 * j + k;
-        p.op[ts].st = 4 * j + k;
+      int t = last_unit + 1;
+      if (t < epi_ready(q, u)) t = epi_ready(q, u);
+      if (q >= 2 && t <= last_rd[q - 2]) t = last_rd[q - 2] + 1;
+      while (t < kEpiSlots && p.op[t].unit >= 0) ++t;
+      if (t >= kEpiSlots) {
+        p.ok = false;
+        return p;
       }
+      p.op[t].unit = 8 * q + u;
+      last_unit = t;
+    }
+    int t = last_unit + 1;
+    for (int k = 0; k < 4; ++k) {
+      if (q >= 1 && t <= st_of[q - 1][k]) t = st_of[q - 1][k] + 1;
+      while (t < kEpiSlots && p.op[t].rd >= 0) ++t;
+      int ts = t + kStoreLag;
+      while (ts < kEpiSlots && p.op[ts].st >= 0) ++ts;
+      if (ts >= kEpiSlots) {
+        p.ok = false;
+        return p;
+      }
+      p.op[t].rd = 4 * q + k;
+      p.op[ts].st = 4 * q + k;
+      st_of[q][k] = ts;
+      last_rd[q] = t;
+      if (ts + 1 > p.end) p.end = ts + 1;
+      t += 2;
     }
   }
   return p;
 }
 constexpr int epi_slot_of(const EpiPlan& p, int kind, int id) {  // kind 0 unit, 1 read, 2 store
-  for (int t = 0; t < 64; ++t)
+  for (int t = 0; t < kEpiSlots; ++t)
     if ((kind == 0 ? p.op[t].unit : kind == 1 ? p.op[t].rd : p.op[t].st) == id) return t;
   return -1;
 }
 constexpr int epi_stores_from(const EpiPlan& p, int t0) {  // stores at slots >= t0
   int n = 0;
-  for (int t = t0; t < 64; ++t) n += p.op[t].st >= 0;
+  for (int t = t0; t < kEpiSlots; ++t) n += p.op[t].st >= 0;
   return n;
 }
-constexpr int kEpiA0 = 8;
-constexpr EpiPlan kEpiA = make_epi_plan(kEpiA0);
-constexpr int kMfmaLatencySlots = 4;  // slots between an accumulator's last MFMA and its first read
+constexpr int kEpi0 = 8;
+constexpr EpiPlan kEpiPlan = make_epi_plan(kEpi0);
 constexpr bool epi_plan_ok(const EpiPlan& q) {
-  if (!q.ok) return false;
-  for (int j = 0; j < 4; ++j) {
-    for (int u = 0; u < 8; ++u)  // acc[u & 3][2 j + (u >> 2)] takes its last MFMA at slot 4 b + i
-      if (epi_slot_of(q, 0, 8 * j + u) < 4 * (2 * j + (u >> 2)) + (u & 3) + kMfmaLatencySlots) return false;
+  if (!q.ok || q.end > kEpiSlots) return false;
+  for (int p = 0; p < 8; ++p) {
+    for (int u = 0; u < 8; ++u) {
+      const int tu = epi_slot_of(q, 0, 8 * p + u);
+      if (tu < 0 || (tu < 64 && tu < epi_ready(p, u))) return false;
+      if (u > 0 && tu <= epi_slot_of(q, 0, 8 * p + u - 1)) return false;
+    }
     for (int k = 0; k < 4; ++k) {
-      const int tr = epi_slot_of(q, 1, 4 * j + k), ts = epi_slot_of(q, 2, 4 * j + k);
+      const int tr = epi_slot_of(q, 1, 4 * p + k), ts = epi_slot_of(q, 2, 4 * p + k);
+      if (tr < 0 || ts <= tr) return false;
       for (int u = 0; u < 8; ++u)  // a pass's reads follow all of its units
-        if (tr <= epi_slot_of(q, 0, 8 * j + u)) return false;
-      if (ts <= tr) return false;
+        if (tr <= epi_slot_of(q, 0, 8 * p + u)) return false;
       // the next pass's read k reuses the same registers: after this store
-      if (j < 3 && epi_slot_of(q, 1, 4 * (j + 1) + k) <= ts) return false;
-      // pass j + 2 writes the same area: after all of pass j's reads
-      if (j < 2 && epi_slot_of(q, 0, 8 * (j + 2)) <= tr) return false;
+      if (p < 7 && epi_slot_of(q, 1, 4 * (p + 1) + k) <= ts) return false;
+      // pass p + 2 writes the same area: after all of pass p's reads
+      if (p < 6 && epi_slot_of(q, 0, 8 * (p + 2)) <= tr) return false;
     }
   }
   return true;
 }
-static_assert(epi_plan_ok(kEpiA), "the overlapped epilogue's windows, order and staging reuse");
+static_assert(epi_plan_ok(kEpiPlan), "the overlapped epilogue's windows, order and staging reuse");
 
 // Where a wave's output rows go, and how they are scaled.
 struct EpiCtx {
@@ -716,21 +754,6 @@ __device__ __forceinline__ void epi_store(const u32x4& v, int j, int k, const Ep
   const int col = e.col0 + 64 * P + 8 * (lane & 7);
   const uint32_t off = col < e.gn ? (uint32_t)(row * e.gld + col) * 2u : kOutOfRange;
   __builtin_amdgcn_raw_buffer_store_b128(v, e.out, (int)off, 0, kStreamStore);
-}
-
-// Part P on its own (no matrix-core work to hide behind).
-template <int P>
-__device__ __forceinline__ void epi_part_alone(const f32x4 (&acc)[8][8], const EpiCtx& e, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) epi_unit<P>(acc, j, u, e, lane);
-    u32x4 v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = epi_read(j, k, e, lane);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) epi_store<P>(v[k], j, k, e, lane);
-  }
 }
 
 // What one stage needs besides the fragments and accumulators.
@@ -806,25 +829,33 @@ constexpr SlotPlan kSlotPlan = make_slot_plan(kSlotFree, kCopyStride, kSlotMid);
 static_assert(kSlotPlan.ok, "the W8A8 stage's memory operations must fit its 64 slots");
 
 // VMEM operations (copies and stores) between a stage's copies and the wait
-// for them, with the overlapped epilogue (part B's kPartStores stores follow
-// the last stage):
+// for them, with the overlapped epilogue (its stores at slots 64 and later
+// follow the last stage):
 //   a tile's start waits for stage 0, whose last copy is the last stage's
-//   slot kLastCopy1 - 1: younger are stage 1's 16 copies (KT > 1), part A's
-//   stores from that slot on (a store follows the copy of its slot) and
-//   part B's;
+//   slot kLastCopy1 - 1: younger are stage 1's 16 copies (KT > 1) and the
+//   epilogue's stores from that slot on (a store follows the copy of its
+//   slot);
 //   stage 0's mid-stage wait is for stage 1, whose last copy is the last
-//   stage's slot kLastCopyEnd - 1: younger are part A's stores from that
-//   slot on, part B's and stage 0's own copies before the wait.
-constexpr int kPartStores = 16;  // per part: 4 passes x 4 stores
-constexpr int kEpiStoresAfterStage0 = epi_stores_from(kEpiA, kLastCopy1 - 1) + kPartStores;
-constexpr int kEpiStoresAfterStage1 = epi_stores_from(kEpiA, kLastCopyEnd - 1) + kPartStores;
-static_assert(epi_stores_from(kEpiA, 0) == kPartStores, "part A's stores");
+//   stage's slot kLastCopyEnd - 1: younger are the epilogue's stores from
+//   that slot on and stage 0's own copies before the wait.
+constexpr int kEpiStoresAfterStage0 = epi_stores_from(kEpiPlan, kLastCopy1 - 1);
+constexpr int kEpiStoresAfterStage1 = epi_stores_from(kEpiPlan, kLastCopyEnd - 1);
+static_assert(epi_stores_from(kEpiPlan, 0) == 32, "8 passes x 4 stores");
 static_assert(16 + kEpiStoresAfterStage0 <= kMaxVmcnt &&
                   kEpiStoresAfterStage1 + kSlotPlan.copies_before_mid <= kMaxVmcnt,
               "vmcnt range");
 
-// kEpi: the stage carries part A of the overlapped epilogue (a tile's last stage).
-constexpr bool kEpiNone = false, kEpiPartA = true;
+// kEpi: the stage carries the overlapped epilogue (a tile's last stage).
+constexpr bool kEpiNone = false, kEpiOverlap = true;
+
+// The epilogue operations of slot t of the plan.
+template <int t>
+__device__ __forceinline__ void epi_slot_ops(const f32x4 (&acc)[8][8], u32x4 (&eb)[4], const EpiCtx& e, int lane) {
+  constexpr EpiSlot eo = kEpiPlan.op[t];
+  if constexpr (eo.unit >= 0) epi_unit<(eo.unit >> 5)>(acc, (eo.unit >> 3) & 3, eo.unit & 7, e, lane);
+  if constexpr (eo.rd >= 0) eb[eo.rd & 3] = epi_read((eo.rd >> 2) & 3, eo.rd & 3, e, lane);
+  if constexpr (eo.st >= 0) epi_store<(eo.st >> 4)>(eb[eo.st & 3], (eo.st >> 2) & 3, eo.st & 3, e, lane);
+}
 
 // MFMA t of the stage and the memory operations that follow it. kExtraVm:
 // VMEM operations issued after stage s + 1's copies besides this stage's
@@ -881,13 +912,15 @@ __device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i 
     if constexpr (op.kind == kSlotW) set_half(wf[op.a], op.e, frag16_half(lds8_w(c.nxt), c.ow[op.e], op.a));
     if constexpr (op.kind == kSlotX) set_half(xf[op.a], op.e, frag16_half(lds8_x(c.nxt), c.ox[op.e], op.a));
   }
-  if constexpr (kEpi) {
-    constexpr EpiSlot eo = kEpiA.op[t];
-    if constexpr (eo.unit >= 0) epi_unit<0>(acc, eo.unit >> 3, eo.unit & 7, c.epi, c.lane);
-    if constexpr (eo.rd >= 0) eb[eo.rd & 3] = epi_read(eo.rd >> 2, eo.rd & 3, c.epi, c.lane);
-    if constexpr (eo.st >= 0) epi_store<0>(eb[eo.st & 3], eo.st >> 2, eo.st & 3, c.epi, c.lane);
-  }
+  if constexpr (kEpi) epi_slot_ops<t>(acc, eb, c.epi, c.lane);
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// The epilogue's slots past the stage's 64, in order.
+template <int... ts>
+__device__ __forceinline__ void epi_after_stage(const f32x4 (&acc)[8][8], u32x4 (&eb)[4], const StageCtx& c,
+                                                std::integer_sequence<int, ts...>) {
+  (epi_slot_ops<64 + ts>(acc, eb, c.epi, c.lane), ...);
 }
 
 template <int kCopy, int kExtraVm, bool kLast, bool kFirst, bool kEpi, int... ts>
@@ -895,6 +928,7 @@ __device__ __forceinline__ void w8a8_slots(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i
                                            std::integer_sequence<int, ts...>) {
   u32x4 eb[4];  // epilogue reads in flight to their stores
   (w8a8_slot<ts, kCopy, kExtraVm, kLast, kFirst, kEpi>(acc, wf, xf, eb, c), ...);
+  if constexpr (kEpi) epi_after_stage(acc, eb, c, std::make_integer_sequence<int, kEpiPlan.end - 64>{});
 }
 
 template <int kCopy, int kExtraVm, bool kLast, bool kFirst = false, bool kEpi = kEpiNone>
@@ -902,8 +936,11 @@ __device__ __forceinline__ void w8a8_stage(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i
                                            const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int s, int K,
                                            int KT, bool has_next, const int (&ow)[2], const int (&ox)[2],
                                            uint32_t wave_off, const EpiCtx& epi, int lane) {
-  const StageCtx c{pw, px, s & 1, (s & 1) ^ 1, (uint32_t)(s + 2) * 128u, K, KT, has_next, ow, ox, wave_off, epi,
-                   lane};
+  uint32_t k2 = (uint32_t)(s + 2) * 128u;
+  // the masked copies' offsets are loop-invariant where s is known: keep
+  // them from being hoisted out of the tile loop into registers
+  if constexpr (kCopy == 2) asm volatile("" : "+s"(k2));
+  const StageCtx c{pw, px, s & 1, (s & 1) ^ 1, k2, K, KT, has_next, ow, ox, wave_off, epi, lane};
   w8a8_slots<kCopy, kExtraVm, kLast, kFirst, kEpi>(acc, wf, xf, c, std::make_integer_sequence<int, 64>{});
 }
 
@@ -1121,7 +1158,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
       tc = tile_at<kTN>(a, next);
       plan_tile(tc);
     }
-    constexpr bool kEpiLast = kOverlap;  // part A of the overlapped epilogue
+    constexpr bool kEpiLast = kOverlap;  // the overlapped epilogue
     if (kOverlap && KT == 1)
       w8a8_stage<0, 0, true, kOverlap, kEpiLast>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx,
                                                  lane);
@@ -1150,9 +1187,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
       for (int j = 0; j < 4; ++j)
         epilogue_rows_norm_rope(acc, j, epi, grp, grp.alpha, out, cur.n0 + wn * 128, lane, cur.m0 + wm * 128, a.m,
                                 active, nw, a.nr_cos, a.nr_sin, a.nr_eps);
-    } else {
-      epi_part_alone<1>(acc, ctx, lane);  // part A went out during the last stage
-    }
+    }  // else the output went out with the last stage
     if (!has_next) break;
     slot = next;
   }
