@@ -144,6 +144,25 @@ def test_big_tiles_ragged_sampled(gpu, m, n, k):
     assert_gemm_close(f32(y16)[rows], linear.gemm_w8a16(f32(x)[rows], qw.numpy(), 2.3e-4), "w8a16")
 
 
+@pytest.mark.parametrize("k", [384, 640, 4096 + 16])
+def test_w8a8_tile_changes_odd_stage_counts(gpu, k):
+    """Workgroups that walk 2-3 tiles of an odd number of K stages (3, 5, 33; 33 x 17 = 561 tiles of 256 x 256
+    for 256 compute units): a tile starts on the LDS buffer the previous tile's last stage left, so the buffer
+    parity alternates from tile to tile, and stage KT - 2 already copies the next tile's stage 0. Rows from
+    every M-tile (each row crosses all 17 N-tiles) against the oracle, and a second launch bit-identical."""
+    m, n = 8200, 4104
+    announce("w8a8 tile changes m=%d n=%d k=%d" % (m, n, k))
+    q = random_e4m3_codes((m, k), 8000 + k)
+    qw = random_e4m3_codes((n, k), 9000 + k)
+    qg, qwg = q.to(gpu), qw.to(gpu)
+    y = fp8lin.fp8lin_gemm_w8a8(qg, qwg, 1.7e-3, 3.1e-5)
+    y2 = fp8lin.fp8lin_gemm_w8a8(qg, qwg, 1.7e-3, 3.1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    rows = np.unique(np.concatenate([sample_rows(m, 64, k), np.arange(k % 256, m, 256), [m - 1]]))
+    assert_gemm_close(f32(y)[rows], linear.gemm_w8a8(q.numpy()[rows], qw.numpy(), 1.7e-3, 3.1e-5), "w8a8")
+
+
 @pytest.mark.parametrize("m", [1024, 2048])
 def test_small_tiles_full_rows_sampled(gpu, m):
     """128 x 128 tiles at the small-batch sizes: one tile per CU (1024 rows), several per CU (2048), and the

@@ -557,10 +557,11 @@ __device__ __forceinline__ void read_frag16(v8i& v, const uint8_t* tile, const i
 // second half -- each register block is refilled in place as soon as it is
 // done, and the 16 blocks (128 VGPRs) are all the fragments there are.
 // Each MFMA is followed by at most one memory operation (slot plan below);
-// a tile's last stage (kLast) has no stage s + 1: after the barrier that
-// frees its buffer no wave reads either buffer, and the next tile's stages 0
-// and 1 are issued, one copy per slot (plans pw, px of that tile; none when
-// has_next is false). sched_barrier keeps the compiler from regrouping slots.
+// a tile's last stage (kLast) has no stage s + 1 and reads nothing for one;
+// after the barrier that frees its buffer it copies the next tile's stage 1
+// there (stage KT - 2 copied that tile's stage 0; plans pw, px of that tile,
+// none when has_next is false). sched_barrier keeps the compiler from
+// regrouping slots.
 //
 // Why 16 x 16 x 128 and not 32 x 32 x 64 (same 128 x 128 wave tile, same
 // LDS traffic): on one MI355X, back-to-back FP8 MFMAs sustain 4.36-4.47
@@ -573,11 +574,10 @@ constexpr int kSlotFree = 12;   // barrier that frees this stage's buffer
 constexpr int kCopyStride = 3;  // slots between the copies of stage s + 2
 constexpr int kSlotMid = 32;    // barrier after which stage s + 1 is readable
 
-// A tile's last stage issues the next tile's stages 0 and 1, one copy per
-// slot from kSlotFree: stage 0's 16 copies, then stage 1's.
-constexpr int kLastCopy0 = kSlotFree;       // slot of the first copy of the next tile's stage 0
-constexpr int kLastCopy1 = kSlotFree + 16;  // ... of its stage 1
-constexpr int kLastCopyEnd = kSlotFree + 32;
+// Across a tile change the copies keep the steady rhythm: stage KT - 2
+// issues the next tile's stage 0 and the last stage its stage 1 (KT = 1:
+// stage 0), each into the buffer it frees, at the steady stage's copy slots.
+// A tile's stage s uses buffer (s + p) % 2, p the tile's buffer parity.
 
 // ------------------------------------------------------------------ overlapped epilogue
 // Most of the plain bf16 epilogue runs beside the matrix cores' work of a
@@ -828,21 +828,17 @@ constexpr SlotPlan make_slot_plan(int kFree, int kStride, int kMid) {
 constexpr SlotPlan kSlotPlan = make_slot_plan(kSlotFree, kCopyStride, kSlotMid);
 static_assert(kSlotPlan.ok, "the W8A8 stage's memory operations must fit its 64 slots");
 
-// VMEM operations (copies and stores) between a stage's copies and the wait
-// for them, with the overlapped epilogue (its stores at slots 64 and later
-// follow the last stage):
-//   a tile's start waits for stage 0, whose last copy is the last stage's
-//   slot kLastCopy1 - 1: younger are stage 1's 16 copies (KT > 1) and the
-//   epilogue's stores from that slot on (a store follows the copy of its
-//   slot);
-//   stage 0's mid-stage wait is for stage 1, whose last copy is the last
-//   stage's slot kLastCopyEnd - 1: younger are the epilogue's stores from
-//   that slot on and stage 0's own copies before the wait.
-constexpr int kEpiStoresAfterStage0 = epi_stores_from(kEpiPlan, kLastCopy1 - 1);
-constexpr int kEpiStoresAfterStage1 = epi_stores_from(kEpiPlan, kLastCopyEnd - 1);
-static_assert(epi_stores_from(kEpiPlan, 0) == 32, "8 passes x 4 stores");
-static_assert(16 + kEpiStoresAfterStage0 <= kMaxVmcnt &&
-                  kEpiStoresAfterStage1 + kSlotPlan.copies_before_mid <= kMaxVmcnt,
+// VMEM operations (copies and stores) younger than the previous tile's
+// last stage's last copy (its slot kSlotPlan.last_copy; a store follows the
+// copy of its slot, and the epilogue's stores at slots 64 and later follow
+// the stage): the overlapped epilogue's stores from that slot on. They are
+// what a tile's stage 0 skips in its wait for stage 1 (KT > 1), and in its
+// start's wait for stage 0 when KT = 1; with KT > 1 stage 0 came from stage
+// KT - 2, so the start skips stage 1's copies and all of the stores.
+constexpr int kEpiStores = 32;  // 8 passes x 4 stores
+constexpr int kEpiStoresAfterLastCopy = epi_stores_from(kEpiPlan, kSlotPlan.last_copy);
+static_assert(epi_stores_from(kEpiPlan, 0) == kEpiStores, "8 passes x 4 stores");
+static_assert(16 + kEpiStores <= kMaxVmcnt && kEpiStoresAfterLastCopy + kSlotPlan.copies_before_mid <= kMaxVmcnt,
               "vmcnt range");
 
 // kEpi: the stage carries the overlapped epilogue (a tile's last stage).
@@ -879,14 +875,16 @@ __device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i 
   }
   if constexpr (t == kFree) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // this stage's buffer is free
   if constexpr (kLast) {
-    // no stage s + 1: the next tile's stages 0 and 1, one copy per slot
-    if constexpr (t >= kLastCopy0 && t < kLastCopyEnd) {
-      constexpr int u = t - kLastCopy0, st = u >> 4, j = u & 7;
-      if (c.has_next && (st == 0 || c.KT > 1)) {
-        if constexpr ((u & 15) < 8)
-          c.pw.copy_masked(lds8_w(st), st * 128, c.K, j, c.wave_off);
+    // no stage s + 1: the next tile's stage 1 into this buffer (KT = 1: its
+    // stage 0 into the other one)
+    if constexpr (op.kind == kSlotCopy) {
+      constexpr int u = op.a, j = u & 7;
+      if (c.has_next) {
+        const int buf = c.KT > 1 ? c.cur : c.nxt, k0b = c.KT > 1 ? 128 : 0;
+        if constexpr (u < 8)
+          c.pw.copy_masked(lds8_w(buf), k0b, c.K, j, c.wave_off);
         else
-          c.px.copy_masked(lds8_x(st), st * 128, c.K, j, c.wave_off);
+          c.px.copy_masked(lds8_x(buf), k0b, c.K, j, c.wave_off);
       }
     }
   } else {
@@ -902,6 +900,14 @@ __device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i 
           c.pw.copy_masked(lds8_w(c.cur), (int)c.k2, c.K, j, c.wave_off);
         else
           c.px.copy_masked(lds8_x(c.cur), (int)c.k2, c.K, j, c.wave_off);
+      } else if constexpr (kCopy == 3) {
+        // the next tile's stage 0 (pw, px already planned for it; without a
+        // next tile, this tile's stage 0 again, into a buffer no one reads,
+        // so the waits count the same copies)
+        if constexpr (u < 8)
+          c.pw.copy_masked(lds8_w(c.cur), 0, c.K, j, c.wave_off);
+        else
+          c.px.copy_masked(lds8_x(c.cur), 0, c.K, j, c.wave_off);
       }
     }
     if constexpr (t == kMid) {
@@ -933,14 +939,15 @@ __device__ __forceinline__ void w8a8_slots(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i
 
 template <int kCopy, int kExtraVm, bool kLast, bool kFirst = false, bool kEpi = kEpiNone>
 __device__ __forceinline__ void w8a8_stage(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i (&xf)[8],
-                                           const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int s, int K,
-                                           int KT, bool has_next, const int (&ow)[2], const int (&ox)[2],
+                                           const CopyPlan<8, true>& pw, const CopyPlan<8, true>& px, int s, int p,
+                                           int K, int KT, bool has_next, const int (&ow)[2], const int (&ox)[2],
                                            uint32_t wave_off, const EpiCtx& epi, int lane) {
   uint32_t k2 = (uint32_t)(s + 2) * 128u;
   // the masked copies' offsets are loop-invariant where s is known: keep
   // them from being hoisted out of the tile loop into registers
   if constexpr (kCopy == 2) asm volatile("" : "+s"(k2));
-  const StageCtx c{pw, px, s & 1, (s & 1) ^ 1, k2, K, KT, has_next, ow, ox, wave_off, epi, lane};
+  const int b = (s + p) & 1;  // this stage's buffer
+  const StageCtx c{pw, px, b, b ^ 1, k2, K, KT, has_next, ow, ox, wave_off, epi, lane};
   w8a8_slots<kCopy, kExtraVm, kLast, kFirst, kEpi>(acc, wf, xf, c, std::make_integer_sequence<int, 64>{});
 }
 
@@ -1025,11 +1032,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(void* h, int M, int m_b
 }
 
 // Persistent W8A8 kernel: one workgroup per CU walks the tiles of dispatch
-// slots blockIdx.x, blockIdx.x + gridDim.x, ... In a tile's last stage,
-// once no wave reads the pipeline buffers, the first two stages of the next
-// tile are issued, so their latency overlaps the last MFMAs and the tile's
-// output stores (which go through an LDS area of each wave's own). The next
-// tile then waits for its stage 0 with a count that skips those stores
+// slots blockIdx.x, blockIdx.x + gridDim.x, ... The copies run across tile
+// changes at the steady rate of one stage per stage: a tile's stage KT - 2
+// copies the next tile's stage 0 and its last stage the next tile's stage 1,
+// each into the buffer it frees (so a tile starts on the buffer parity the
+// previous one left), and their latency overlaps the last MFMAs and the
+// tile's output stores (which go through an LDS area of each wave's own).
+// The next tile waits for its stage 0 with a count that skips those stores
 // (they were issued later), and for stage 1 inside its stage 0, so it never
 // waits for the stores.
 // kSwiGLU: the fused gate/up + SwiGLU form. A tile is 256 rows of M by 128
@@ -1092,24 +1101,29 @@ gemm_w8a8_kernel(const GemmArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   f32x4 acc[8][8];
+  int p = 0;  // buffer parity: a tile's stage s uses buffer (s + p) % 2
   for (;;) {
     const TileCoord cur = tc;
     const GemmGroup& grp = a.g[cur.group];
     const int next = slot + (int)gridDim.x;
     const bool has_next = next < a.total_tiles;
-    // stage 0 has landed for every wave: after the first tile, only stage
-    // 1's copies (when KT > 1) and the previous tile's stores are younger
-    constexpr int kTileStores = kOverlap ? kEpiStoresAfterStage0 : kStores;
+    // stage 0 has landed for every wave. Younger, after the first tile: with
+    // KT > 1 stage 1's copies and all of the previous tile's stores (stage 0
+    // came from that tile's stage KT - 2); with KT = 1 the stores issued
+    // after the last stage's last copy.
+    constexpr int kStartVm = kStageCopies + (kOverlap ? kEpiStores : kStores);
+    constexpr int kStartVm1 = kOverlap ? kEpiStoresAfterLastCopy : kStores;
+    static_assert(kStartVm <= kMaxVmcnt, "vmcnt range");
     if (KT > 1)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStageCopies + kTileStores) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStartVm) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kTileStores) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStartVm1) : "memory");
     // stage 0's fragments but xf[7] and wf[4..7], which the stage reads itself
     v8i wf[8], xf[8];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) read_frag16(wf[f], lds8_w(0), ow, f);
+    for (int f = 0; f < 4; ++f) read_frag16(wf[f], lds8_w(p), ow, f);
 #pragma unroll
-    for (int f = 0; f < 7; ++f) read_frag16(xf[f], lds8_x(0), ox, f);
+    for (int f = 0; f < 7; ++f) read_frag16(xf[f], lds8_x(p), ox, f);
     if constexpr (!kOverlap) {
       // the fused epilogues' register allocation comes out better with
       // accumulators cleared at the tile start than with stage 0 from zero
@@ -1127,44 +1141,55 @@ gemm_w8a8_kernel(const GemmArgs a) {
       ctx.gn = __builtin_amdgcn_readfirstlane(grp.n);
       ctx.gld = __builtin_amdgcn_readfirstlane(grp.ldy);
     }
+    // the next tile's copies start in stage KT - 2 (KT = 1: the last stage)
+    auto plan_next = [&] {
+      if (has_next) {
+        tc = tile_at<kTN>(a, next);
+        plan_tile(tc);
+      }
+    };
 
     // Stage kinds: s <= KT - 4 copies stage s + 2 (never the last, so no K
     // tail); s = KT - 3 copies the last stage with its tail masked; s = KT - 2
-    // copies nothing; s = KT - 1 is the last. Stage 0's mid-stage wait also
-    // skips the previous tile's stores; with the overlapped epilogue stage 0
-    // starts from zero accumulators instead of cleared ones.
-    constexpr int kExtra0 = kOverlap ? kEpiStoresAfterStage1 : kStores;
+    // copies the next tile's stage 0; s = KT - 1 is the last. Stage 0's
+    // mid-stage wait also skips the previous tile's stores issued after its
+    // last copy; with the overlapped epilogue stage 0 starts from zero
+    // accumulators instead of cleared ones.
+    constexpr int kExtra0 = kOverlap ? kEpiStoresAfterLastCopy : kStores;
     int s = 0;
     if (KT >= 2) {
-      if (KT >= 4)
-        w8a8_stage<1, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off, ctx, lane);
-      else if (KT == 3)
-        w8a8_stage<2, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off, ctx, lane);
-      else
-        w8a8_stage<0, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, K, KT, has_next, ow, ox, wave_off, ctx, lane);
+      if (KT >= 4) {
+        w8a8_stage<1, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, p, K, KT, has_next, ow, ox, wave_off, ctx,
+                                                lane);
+      } else if (KT == 3) {
+        w8a8_stage<2, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, p, K, KT, has_next, ow, ox, wave_off, ctx,
+                                                lane);
+      } else {
+        plan_next();
+        w8a8_stage<3, kExtra0, false, kOverlap>(acc, wf, xf, pw, px, 0, p, K, KT, has_next, ow, ox, wave_off, ctx,
+                                                lane);
+      }
       for (s = 1; s + 3 < KT; ++s)
-        w8a8_stage<1, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
+        w8a8_stage<1, 0, false>(acc, wf, xf, pw, px, s, p, K, KT, has_next, ow, ox, wave_off, ctx, lane);
       if (s == KT - 3) {
-        w8a8_stage<2, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
+        w8a8_stage<2, 0, false>(acc, wf, xf, pw, px, s, p, K, KT, has_next, ow, ox, wave_off, ctx, lane);
         ++s;
       }
       if (s == KT - 2) {
-        w8a8_stage<0, 0, false>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
+        plan_next();
+        w8a8_stage<3, 0, false>(acc, wf, xf, pw, px, s, p, K, KT, has_next, ow, ox, wave_off, ctx, lane);
         ++s;
       }
-    }
-    // the last stage issues the next tile's first stages: plan them now
-    if (has_next) {
-      tc = tile_at<kTN>(a, next);
-      plan_tile(tc);
+    } else {
+      plan_next();
     }
     constexpr bool kEpiLast = kOverlap;  // the overlapped epilogue
     if (kOverlap && KT == 1)
-      w8a8_stage<0, 0, true, kOverlap, kEpiLast>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx,
+      w8a8_stage<0, 0, true, kOverlap, kEpiLast>(acc, wf, xf, pw, px, s, p, K, KT, has_next, ow, ox, wave_off, ctx,
                                                  lane);
     else
-      w8a8_stage<0, 0, true, false, kEpiLast>(acc, wf, xf, pw, px, s, K, KT, has_next, ow, ox, wave_off, ctx, lane);
-
+      w8a8_stage<0, 0, true, false, kEpiLast>(acc, wf, xf, pw, px, s, p, K, KT, has_next, ow, ox, wave_off, ctx,
+                                              lane);
     if constexpr (kSwiGLU) {
       const int I = grp.n;
       const __amdgpu_buffer_rsrc_t out = h_rsrc(grp.y, a.m, cur.m0 + wm * 128, I, 1);
@@ -1190,6 +1215,7 @@ gemm_w8a8_kernel(const GemmArgs a) {
     }  // else the output went out with the last stage
     if (!has_next) break;
     slot = next;
+    p = (p + KT) & 1;
   }
 }
 
