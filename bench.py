@@ -96,6 +96,31 @@ def timed(fn, reps, warmup=3, warm_ms=30.0):
     return e0.elapsed_time(e1) / reps
 
 
+def timed_graph(fn, reps, calls=20, warm_ms=30.0):
+    """Average device time per fn() call, ms, with `calls` calls captured in one HIP graph and the graph
+    replayed `reps` times: the kernels then run back to back, without the host's per-call launch time
+    between them (what a serving loop that replays a captured step sees). fn() must write only buffers
+    allocated before capture."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture stream
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    settle(graph.replay, warm_ms)
+    e0, e1 = events(2)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * calls)
+
+
 def settle(fn, warm_ms=30.0):
     """Run fn() for about `warm_ms` of device time (sized from one timed call), so that the shader clock
     has settled under the load before timing starts; returns the device time spent, ms."""
@@ -558,6 +583,19 @@ def other_rows(dev, case, x, qws, qx, ys, schedule_row=True):
                "w8a8_tflops": round(f / a / 1e9, 1), "w8a8_pct_fp8_peak": round(100 * f / a / 1e9 / PEAK_FP8_TFLOPS, 2),
                "w8a16_tflops": round(f / b / 1e9, 1),
                "w8a16_pct_bf16_peak": round(100 * f / b / 1e9 / PEAK_BF16_TFLOPS, 2)}
+        if m < 8192:
+            # the same calls replayed from a captured graph: at 17-60 us per kernel the host's launch time
+            # between eager calls shows in the rows above
+            q2m, x2m = q2[:m], x2[:m]
+            ag = timed_graph(lambda: fp8lin.fp8lin_gemm_w8a8(q2m, qw2, c2.input_scale, c2.weight_scale, out=y2),
+                             reps)
+            bg = timed_graph(lambda: fp8lin.fp8lin_gemm_w8a16(x2m, qw2, c2.weight_scale, out=y2), reps)
+            row["graph_replay"] = {
+                "calls_per_graph": 20,
+                "w8a8_tflops": round(f / ag / 1e9, 1),
+                "w8a8_pct_fp8_peak": round(100 * f / ag / 1e9 / PEAK_FP8_TFLOPS, 2),
+                "w8a16_tflops": round(f / bg / 1e9, 1),
+                "w8a16_pct_bf16_peak": round(100 * f / bg / 1e9 / PEAK_BF16_TFLOPS, 2)}
         if m == 1024:
             ws_sk = torch.empty(4 * m * K * 4, dtype=torch.uint8, device=dev)
             c = timed(lambda: fp8lin.fp8lin_gemm_w8a8_splitk(q2[:m], qw2, c2.input_scale, c2.weight_scale,
