@@ -602,11 +602,11 @@ constexpr int kSlotMid = 32;    // barrier after which stage s + 1 is readable
 // Measured on one box (16384 x 4096 x 4096, one launch): 2941 -> 2993 and
 // 2956 -> 3022 TFLOP/s with part A in the stage against the whole epilogue
 // after it, and 3026 -> 3040 with part B's first passes moved in as well;
-// with no epilogue at all (a diagnostic build) 3234-3283. Interleaving a
-// unit (4 accumulator reads, 4 multiplies, 2 packs, 1 LDS write) per slot
-// already outlasts the 16 x 16 x 128 MFMA beside it, so the work is only
-// partly hidden, and the board is power-limited: the epilogue's
-// instructions cost clock wherever they run. Part B in the first half of
+// with no epilogue at all (a diagnostic build) 3234-3283. Timing builds
+// that drop one part at a time place the remaining cost in the global
+// stores (+7% without them), not in the units' arithmetic (+0.4% without
+// it): the stores share the CU's vector-memory requests with the copies,
+// whose rate bounds this kernel. Part B in the first half of
 // the next tile's stage 0 (whose MFMAs start from zero and write only
 // acc[0..3] there) ran out of registers beside stage 0's fragments and
 // spilled; stores straight from the accumulators (no staging) were 15-30%
