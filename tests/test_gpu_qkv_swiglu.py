@@ -19,7 +19,7 @@ import w8a16_linear_layers_amd as fp8lin
 from oracle import bf16 as obf16
 from oracle import linear, swiglu
 from tests.helpers import announce, assert_gemm_close, check_swiglu_codes, f32, sample_rows, u8
-from workloads import config3, config4, normal_bf16
+from workloads import config3, config4, normal_bf16, random_e4m3_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,31 @@ def test_gemm_w8a8_group(gpu, m, k, ns):
         assert outs[i].shape == (m, ns[i]) and outs[i].is_contiguous()
         ref = linear.gemm_w8a8(qx_ref, linear.quantize_static(f32(w.contiguous()), s), case.input_scale, s)
         assert_gemm_close(f32(outs[i])[rows], ref, "group proj %d" % i)
+
+
+@pytest.mark.parametrize("k", [384, 640])
+def test_four_ragged_projections_many_tiles(gpu, k):
+    """Four projections of ragged widths in one launch (the W8A8 group and the W8A16 shared call) at 4100 rows:
+    17 x 25 = 425 tiles of 256 x 256 for 256 compute units, so workgroups cross projection boundaries and
+    change tiles after an odd number of 128-byte W8A8 stages (3, 5). Rows from every M-tile against the
+    oracle, per projection."""
+    m, ns = 4100, (264, 4104, 136, 1032)
+    announce("four ragged projections m=%d k=%d" % (m, k))
+    q = random_e4m3_codes((m, k), 100 + k)
+    qws = [random_e4m3_codes((n, k), 200 + n + k) for n in ns]
+    x = normal_bf16((m, k), 0.35, 300 + k)
+    s_in, sw = 1.7e-3, [3.1e-5, 2.2e-5, 4.7e-5, 1.3e-5]
+    qwg = [w.to(gpu) for w in qws]
+    outs8 = fp8lin.fp8lin_gemm_w8a8_group(q.to(gpu), qwg, s_in, sw)
+    outs16, ws = fp8lin.fp8lin_qkv_shared(x.to(gpu), qwg, sw, [s_in] * 4, fp8lin.MODE_W8A16)
+    torch.cuda.synchronize()
+    assert ws is None
+    rows = np.unique(np.concatenate([sample_rows(m, 48, k), np.arange(k % 256, m, 256), [m - 1]]))
+    qr, xr = q.numpy()[rows], f32(x)[rows]
+    for i in range(4):
+        assert outs8[i].shape == (m, ns[i]) and outs16[i].shape == (m, ns[i])
+        assert_gemm_close(f32(outs8[i])[rows], linear.gemm_w8a8(qr, qws[i].numpy(), s_in, sw[i]), "w8a8 proj %d" % i)
+        assert_gemm_close(f32(outs16[i])[rows], linear.gemm_w8a16(xr, qws[i].numpy(), sw[i]), "w8a16 proj %d" % i)
 
 
 def test_qkv_shared_w8a16_stands_down(gpu):
