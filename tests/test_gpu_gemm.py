@@ -286,7 +286,9 @@ def test_repeated_launches_are_bit_identical(gpu, kind):
 
 
 @pytest.mark.parametrize("m,n,k,splits", [(1024, 4096, 4096, 4), (1024, 4096, 4096, 2), (300, 528, 1024, 4),
-                                          (77, 64, 128, 2)])
+                                          (77, 64, 128, 2),
+                                          # 306 tiles of 3-stage slices: workgroups change tiles at an odd K count
+                                          (2100, 4104, 768, 2)])
 def test_gemm_w8a8_splitk(gpu, m, n, k, splits):
     """K split into float32 partials, summed in slice order: the oracle's tolerance, within one bf16 ulp of
     the unsplit GEMM, and nothing written past the partials."""
