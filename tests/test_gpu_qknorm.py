@@ -126,7 +126,9 @@ def test_on_the_qkv_group_outputs(gpu):
 
 
 @pytest.mark.parametrize("m,kdim,n,nproj", [(600, 1024, 1024, 3), (300, 528, 384, 3), (77, 64, 128, 2),
-                                            (16384, 4096, 4096, 3)])
+                                            (16384, 4096, 4096, 3),
+                                            # 816 tiles of 3 K stages: 3-4 tile changes per workgroup
+                                            (4100, 384, 4096, 3)])
 def test_fused_qkv_norm_rope(gpu, m, kdim, n, nproj):
     """Q and K normalized and rotated in the grouped GEMM's epilogue: within the bound of the exact
     norm + RoPE of the plain grouped GEMM's own bf16 outputs; V equal to the plain output bit for bit."""

@@ -214,7 +214,9 @@ def test_swiglu_rejects_non_contiguous(gpu):
 
 @pytest.mark.parametrize(
     "m,k,inter",
-    [(300, 528, 272), (256, 256, 128), (77, 64, 16), (513, 1040, 400), (8192, 4096, 16384)],
+    [(300, 528, 272), (256, 256, 128), (77, 64, 16), (513, 1040, 400), (8192, 4096, 16384),
+     # 17 x 17 tiles of 3 K stages: workgroups change tiles at an odd K-stage count
+     (4100, 384, 2064)],
 )
 def test_gate_up_swiglu_fused(gpu, m, k, inter):
     """One launch equals gemm_w8a8(gate), gemm_w8a8(up), swiglu_2in_quant bit for bit, and the oracle's
