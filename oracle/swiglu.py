@@ -21,7 +21,9 @@ Readings (the pages are silent):
     and FP16 shapes): the same float64 h from the half-precision values;
     FP8 output as above, FP16 output within one binary16 ulp of
     f16_rne(h), which overflows to an infinity from 65520 up.
-Parity beyond these closed forms is unpinned: the pages print no values.
+The pages print no worked SwiGLU values; the pins are scipy's logistic
+function, the reflection identity silu(-g) = silu(g) - g, special values
+and torch's bf16 cast (tests/test_oracle_swiglu_policy.py).
 """
 
 import numpy as np
