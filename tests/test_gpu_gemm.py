@@ -66,6 +66,43 @@ def test_w8a16_random_codes(gpu, m, n, k):
     assert_gemm_close(y, linear.gemm_w8a16(f32(x), qw.numpy(), s_w), "w8a16 %dx%dx%d" % (m, n, k))
 
 
+def _random_shape(seed):
+    """A seeded GEMM shape: M from one of three ranges (up to one 256-row tile, up to ~4 of them, and 2600-5999
+    rows with N of at least 2048, where 256 x 256 tiles fill the device), N a multiple of 8 up to 5592, K a
+    multiple of 16 up to 4784, and an output row pitch up to 16 elements past N."""
+    rng = np.random.default_rng(5000 + seed)
+    lo, hi, nlo = [(1, 300, 1), (300, 1100, 1), (2600, 6000, 256)][seed % 3]
+    m = int(rng.integers(lo, hi))
+    n = 8 * int(rng.integers(nlo, 700))
+    k = 16 * int(rng.integers(1, 300))
+    pad = 8 * int(rng.integers(0, 3))
+    return m, n, k, pad
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(gpu, seed):
+    """Both GEMMs at seeded random shapes (every tile path, K-stage count and ragged edge the draws land
+    on), against the oracle on every row of the smaller products and on sampled rows of the larger ones; the
+    output's padding columns are left untouched."""
+    m, n, k, pad = _random_shape(seed)
+    announce("random shape m=%d n=%d k=%d ldy=%d" % (m, n, k, n + pad))
+    q = random_e4m3_codes((m, k), 7000 + seed)
+    qw = random_e4m3_codes((n, k), 7100 + seed)
+    x = normal_bf16((m, k), 0.35, 7200 + seed)
+    s_in, s_w, s_w16 = 1.7e-3, 3.1e-5, 2.3e-4
+    qwg = qw.to(gpu)
+    buf8 = torch.full((m, n + pad), 7.0, dtype=torch.bfloat16, device=gpu)
+    buf16 = torch.full((m, n + pad), 7.0, dtype=torch.bfloat16, device=gpu)
+    fp8lin.fp8lin_gemm_w8a8(q.to(gpu), qwg, s_in, s_w, out=buf8[:, :n])
+    fp8lin.fp8lin_gemm_w8a16(x.to(gpu), qwg, s_w16, out=buf16[:, :n])
+    torch.cuda.synchronize()
+    if pad:
+        assert torch.all(buf8[:, n:] == 7.0) and torch.all(buf16[:, n:] == 7.0)
+    rows = np.arange(m) if m * n * k <= 4e8 else sample_rows(m, 64, seed)
+    assert_gemm_close(f32(buf8[:, :n])[rows], linear.gemm_w8a8(q.numpy()[rows], qw.numpy(), s_in, s_w), "w8a8")
+    assert_gemm_close(f32(buf16[:, :n])[rows], linear.gemm_w8a16(f32(x)[rows], qw.numpy(), s_w16), "w8a16")
+
+
 def test_config1_both_modes(gpu):
     announce("config1 w8a8 + w8a16")
     case = config1()
