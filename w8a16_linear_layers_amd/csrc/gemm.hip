@@ -901,13 +901,14 @@ __device__ __forceinline__ void w8a8_slot(f32x4 (&acc)[8][8], v8i (&wf)[8], v8i 
         else
           c.px.copy_masked(lds8_x(c.cur), (int)c.k2, c.K, j, c.wave_off);
       } else if constexpr (kCopy == 3) {
-        // the next tile's stage 0 (pw, px already planned for it; without a
-        // next tile, this tile's stage 0 again, into a buffer no one reads,
-        // so the waits count the same copies)
+        // the next tile's stage 0 (pw, px already planned for it); without a
+        // next tile every lane's offset is out of range (zeros into a buffer
+        // no one reads, no memory read), so the waits count the same copies
+        const int kb = c.has_next ? c.K : 0;
         if constexpr (u < 8)
-          c.pw.copy_masked(lds8_w(c.cur), 0, c.K, j, c.wave_off);
+          c.pw.copy_masked(lds8_w(c.cur), 0, kb, j, c.wave_off);
         else
-          c.px.copy_masked(lds8_x(c.cur), 0, c.K, j, c.wave_off);
+          c.px.copy_masked(lds8_x(c.cur), 0, kb, j, c.wave_off);
       }
     }
     if constexpr (t == kMid) {
